@@ -1,0 +1,299 @@
+/*
+ * CPU oracle for the AVQ-Attention forward pass ("AVQ-Attention: Adaptive
+ * Vector-Quantized Attention", Sec. 3-4).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load or call this code.  The GPU library
+ * never links it, includes it or shares any helper with it.
+ *
+ * Plain, slow and written to be checked by eye against the pages: every
+ * quantity is computed in float64 straight from its definition, one (batch,
+ * head) unit at a time, single-threaded.  Inputs are float64 arrays holding
+ * the exact values of the stored bf16/fp32 tensors.
+ *
+ * Readings taken where the pages are silent (each also listed in the design doc):
+ *  - argmin ties go to the lowest index; a child replaces the parent only if
+ *    it is strictly closer;
+ *  - top-P orders parents by importance descending, then index ascending;
+ *  - query tiles are contiguous index ranges of T queries, the last may be
+ *    shorter;
+ *  - the importance uses the final parent-level denominator of each query;
+ *  - the softmax scale is an explicit argument (the pages write exp(q.k)).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* storage rounding                                                    */
+/* ------------------------------------------------------------------ */
+
+/* Nearest bf16 value to x (8 significant bits, exponent range of fp32),
+ * ties to even, returned as a double.  Written from the definition of
+ * round-to-nearest-even on the significand. */
+double avqo_round_bf16(double x)
+{
+    if (x == 0.0 || isnan(x) || isinf(x)) return x;
+    int e;
+    (void)frexp(x, &e);                 /* x = m * 2^e with 0.5 <= |m| < 1 */
+    int q = e - 8;                      /* weight of the last kept bit   */
+    if (q < -133) q = -133;             /* bf16 subnormal quantum 2^-133 */
+    double scaled = ldexp(x, -q);       /* exact */
+    double fl = floor(scaled);
+    double diff = scaled - fl;
+    double r;
+    if (diff > 0.5) r = fl + 1.0;
+    else if (diff < 0.5) r = fl;
+    else r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+    double y = ldexp(r, q);
+    if (fabs(y) >= 0x1p128) return copysign(INFINITY, x);
+    return y;
+}
+
+/* dtype 0 = fp32, 1 = bf16 */
+void avqo_round(const double *x, int64_t n, int dtype, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = dtype == 1 ? avqo_round_bf16(x[i]) : (double)(float)x[i];
+}
+
+/* ------------------------------------------------------------------ */
+/* O1  tree: parent = mean of its children (Sec. 4.1, "Parent-child    */
+/*     constraint"); one head.                                         */
+/* ------------------------------------------------------------------ */
+void avqo_build_tree(const double *children /*[M0][C][d]*/, int M0, int C, int d,
+                     int dtype, double *parents /*[M0][d]*/)
+{
+    for (int p = 0; p < M0; ++p)
+        for (int t = 0; t < d; ++t) {
+            double s = 0.0;
+            for (int c = 0; c < C; ++c) s += children[((int64_t)p * C + c) * d + t];
+            double mean = s / C;
+            parents[(int64_t)p * d + t] = dtype == 1 ? avqo_round_bf16(mean) : (double)(float)mean;
+        }
+}
+
+/* squared norm of every row */
+void avqo_sqnorm(const double *rows, int64_t nrows, int d, double *out)
+{
+    for (int64_t r = 0; r < nrows; ++r) {
+        double s = 0.0;
+        for (int t = 0; t < d; ++t) s += rows[r * d + t] * rows[r * d + t];
+        out[r] = s;
+    }
+}
+
+static double sqdist(const double *a, const double *b, int d)
+{
+    double s = 0.0;
+    for (int t = 0; t < d; ++t) {
+        double u = a[t] - b[t];
+        s += u * u;
+    }
+    return s;
+}
+
+/* relative gap between the two smallest of n values (0 if fewer than 2) */
+static double rel_gap(const double *v, int n)
+{
+    if (n < 2) return INFINITY;
+    double a = INFINITY, b = INFINITY;
+    for (int i = 0; i < n; ++i) {
+        if (v[i] < a) { b = a; a = v[i]; }
+        else if (v[i] < b) b = v[i];
+    }
+    if (b == 0.0) return 0.0;
+    return (b - a) / b;
+}
+
+/* ------------------------------------------------------------------ */
+/* O2  two-stage assignment (Sec. 3.2 assignment rule; Sec. 4.2: nearest */
+/*     parent first, then only that parent's children, reassigned if a  */
+/*     child is closer than the cached parent distance).                */
+/*     leaf = p* (key stays at its parent) or M0 + p*C + c*.            */
+/*     force_child != 0 treats the parent distance as +infinity.        */
+/*     gap_parent: relative top-2 gap over the M0 parents;              */
+/*     gap_leaf:   relative top-2 gap over {p*} U children(p*).         */
+/* ------------------------------------------------------------------ */
+void avqo_assign(const double *K /*[N][d]*/, int64_t N, int d,
+                 const double *parents /*[M0][d]*/, const double *children /*[M0][C][d]*/,
+                 int M0, int C, int force_child,
+                 int32_t *pstar, int32_t *leaf, double *gap_parent, double *gap_leaf)
+{
+    double *Dp = (double *)malloc(sizeof(double) * (size_t)M0);
+    double *Dl = (double *)malloc(sizeof(double) * (size_t)(C + 1));
+    for (int64_t k = 0; k < N; ++k) {
+        const double *key = K + k * d;
+        int best = 0;
+        for (int p = 0; p < M0; ++p) {
+            Dp[p] = sqdist(key, parents + (int64_t)p * d, d);
+            if (Dp[p] < Dp[best]) best = p;
+        }
+        int cbest = 0;
+        for (int c = 0; c < C; ++c) {
+            Dl[c] = sqdist(key, children + ((int64_t)best * C + c) * d, d);
+            if (Dl[c] < Dl[cbest]) cbest = c;
+        }
+        int to_child = force_child || Dl[cbest] < Dp[best];
+        pstar[k] = best;
+        leaf[k] = to_child ? M0 + best * C + cbest : best;
+        if (gap_parent) gap_parent[k] = rel_gap(Dp, M0);
+        if (gap_leaf) {
+            Dl[C] = Dp[best];
+            gap_leaf[k] = rel_gap(Dl, force_child ? C : C + 1);
+        }
+    }
+    free(Dp);
+    free(Dl);
+}
+
+/* ------------------------------------------------------------------ */
+/* O3  aggregation (Sec. 4.2 "at each level"; Sec. 4.3 value sums and   */
+/*     counts).  Slot p holds every key whose nearest parent is p; slot */
+/*     M0 + p*C + c holds only the keys reassigned to that child.       */
+/* ------------------------------------------------------------------ */
+void avqo_aggregate(const double *V /*[N][d]*/, int64_t N, int d, const int32_t *leaf,
+                    int M0, int C, double *vsum /*[M0(1+C)][d]*/, int64_t *count)
+{
+    int64_t S = (int64_t)M0 * (1 + C);
+    memset(vsum, 0, sizeof(double) * (size_t)(S * d));
+    memset(count, 0, sizeof(int64_t) * (size_t)S);
+    for (int64_t k = 0; k < N; ++k) {
+        int32_t l = leaf[k];
+        int32_t p = l < M0 ? l : (l - M0) / C;
+        for (int t = 0; t < d; ++t) vsum[(int64_t)p * d + t] += V[k * d + t];
+        count[p] += 1;
+        if (l >= M0) {
+            for (int t = 0; t < d; ++t) vsum[(int64_t)l * d + t] += V[k * d + t];
+            count[l] += 1;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* O4-O8  attention of every query over the tree, tile by tile          */
+/*   O4 parent pass   (Sec. 4.3 "Tiled VQ-attention")                   */
+/*   O5 importance    (Sec. 4.3 "Codeword importance")                  */
+/*   O6 top-P         (Sec. 4.3 "Child spawning")                       */
+/*   O7 correction    (Sec. 4.3 "Child attention": parent logit as the  */
+/*                     mean of child logits; the parent weight of each  */
+/*                     reassigned subset is replaced by the child       */
+/*                     weight, exp(S_ic) - exp(S_ip), one shared shift) */
+/*   O8 Y = X / Z                                                       */
+/* Tiles [t_begin, t_end) only; Y rows of other tiles are untouched.    */
+/* forced_sel (nullable, [ntiles][P]) replaces O6's choice.             */
+/* Returns 0, or -1 on allocation failure.                              */
+/* ------------------------------------------------------------------ */
+typedef struct { double w; int idx; } wi_pair;
+static int cmp_pair(const void *a, const void *b)
+{
+    const wi_pair *x = (const wi_pair *)a, *y = (const wi_pair *)b;
+    if (x->w > y->w) return -1;
+    if (x->w < y->w) return 1;
+    return x->idx < y->idx ? -1 : (x->idx > y->idx ? 1 : 0);
+}
+
+int avqo_attention(const double *Q /*[N][d]*/, int64_t N, int d,
+                   const double *parents /*[M0][d]*/, const double *children /*[M0][C][d]*/,
+                   int M0, int C, const double *vsum /*[M0(1+C)][d]*/, const int64_t *count,
+                   int P, int T, double scale, const int32_t *forced_sel,
+                   int64_t t_begin, int64_t t_end,
+                   double *Y /*[N][d]*/, double *importance /*[ntiles][M0]*/, int32_t *sel /*[ntiles][P]*/)
+{
+    double *E = (double *)malloc(sizeof(double) * (size_t)T * M0);
+    double *m = (double *)malloc(sizeof(double) * (size_t)T);
+    double *Z = (double *)malloc(sizeof(double) * (size_t)T);
+    double *X = (double *)malloc(sizeof(double) * (size_t)T * d);
+    double *s = (double *)malloc(sizeof(double) * (size_t)(M0 > C ? M0 : C));
+    double *w = (double *)malloc(sizeof(double) * (size_t)M0);
+    wi_pair *order = (wi_pair *)malloc(sizeof(wi_pair) * (size_t)M0);
+    int32_t *chosen = (int32_t *)malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+    if (!E || !m || !Z || !X || !s || !w || !order || !chosen) {
+        free(E); free(m); free(Z); free(X); free(s); free(w); free(order); free(chosen);
+        return -1;
+    }
+
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        int64_t i0 = t * T;
+        int64_t i1 = i0 + T < N ? i0 + T : N;
+        int nI = (int)(i1 - i0);
+
+        /* O4 */
+        for (int ii = 0; ii < nI; ++ii) {
+            const double *q = Q + (i0 + ii) * d;
+            double mx = -INFINITY;
+            for (int j = 0; j < M0; ++j) {
+                double dot = 0.0;
+                for (int u = 0; u < d; ++u) dot += q[u] * parents[(int64_t)j * d + u];
+                s[j] = scale * dot;
+                if (s[j] > mx) mx = s[j];
+            }
+            m[ii] = mx;
+            double z = 0.0;
+            double *x = X + (int64_t)ii * d;
+            for (int u = 0; u < d; ++u) x[u] = 0.0;
+            for (int j = 0; j < M0; ++j) {
+                double e = exp(s[j] - mx);
+                E[(int64_t)ii * M0 + j] = e;
+                z += e * (double)count[j];
+                for (int u = 0; u < d; ++u) x[u] += e * vsum[(int64_t)j * d + u];
+            }
+            Z[ii] = z;
+        }
+
+        /* O5 */
+        for (int j = 0; j < M0; ++j) {
+            double acc = 0.0;
+            for (int ii = 0; ii < nI; ++ii) acc += E[(int64_t)ii * M0 + j] * (double)count[j] / Z[ii];
+            w[j] = acc;
+            if (importance) importance[t * M0 + j] = acc;
+        }
+
+        /* O6 */
+        if (forced_sel) {
+            for (int k = 0; k < P; ++k) chosen[k] = forced_sel[t * P + k];
+        } else {
+            for (int j = 0; j < M0; ++j) { order[j].w = w[j]; order[j].idx = j; }
+            qsort(order, (size_t)M0, sizeof(wi_pair), cmp_pair);
+            for (int k = 0; k < P; ++k) chosen[k] = order[k].idx;
+        }
+        if (sel) for (int k = 0; k < P; ++k) sel[t * P + k] = chosen[k];
+
+        /* O7 */
+        for (int ii = 0; ii < nI; ++ii) {
+            const double *q = Q + (i0 + ii) * d;
+            double *x = X + (int64_t)ii * d;
+            for (int k = 0; k < P; ++k) {
+                int p = chosen[k];
+                double mean = 0.0, smax = -INFINITY;
+                for (int c = 0; c < C; ++c) {
+                    const double *cw = children + ((int64_t)p * C + c) * d;
+                    double dot = 0.0;
+                    for (int u = 0; u < d; ++u) dot += q[u] * cw[u];
+                    s[c] = scale * dot;
+                    mean += s[c];
+                    if (s[c] > smax) smax = s[c];
+                }
+                mean /= C;
+                if (smax > m[ii]) {
+                    double a = exp(m[ii] - smax);
+                    for (int u = 0; u < d; ++u) x[u] *= a;
+                    Z[ii] *= a;
+                    m[ii] = smax;
+                }
+                double ep = exp(mean - m[ii]);
+                for (int c = 0; c < C; ++c) {
+                    int64_t slot = (int64_t)M0 + (int64_t)p * C + c;
+                    double dA = exp(s[c] - m[ii]) - ep;
+                    for (int u = 0; u < d; ++u) x[u] += dA * vsum[slot * d + u];
+                    Z[ii] += dA * (double)count[slot];
+                }
+            }
+            /* O8 */
+            for (int u = 0; u < d; ++u) Y[(i0 + ii) * d + u] = x[u] / Z[ii];
+        }
+    }
+    free(E); free(m); free(Z); free(X); free(s); free(w); free(order); free(chosen);
+    return 0;
+}

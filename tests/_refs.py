@@ -1,0 +1,58 @@
+"""Independent reference formulations used to pin the oracle (tests only).
+
+These are *different* formulations of what the oracle computes, not copies of
+it: the oracle works on aggregated codewords (value sums and counts) with an
+online max and a child-for-parent correction, while the references below work
+key by key on the quantised keys, or are textbook softmax attention.
+"""
+
+import numpy as np
+
+
+def softmax_attention(Q, K, V, scale):
+    """Textbook softmax attention for one head: Q [n][d], K, V [N][d]
+    ("AVQ-Attention", Sec. 3.1)."""
+    S = scale * Q @ K.T
+    S -= S.max(axis=1, keepdims=True)
+    A = np.exp(S)
+    return (A @ V) / A.sum(axis=1, keepdims=True)
+
+
+def key_level_vq_attention(Q, parents, children, V, pstar, leaf, sel, T, scale):
+    """Softmax attention of each query over the *keys*, every key replaced by
+    its representative codeword (Sec. 3.2: attention with K_hat).  In a tile
+    whose selection contains the key's parent the representative is the key's
+    leaf (child or the parent itself); otherwise it is the parent.
+    Q [N][d], parents [M0][d], children [M0][C][d], sel [ntiles][P]."""
+    N, d = Q.shape
+    M0, C = children.shape[0], children.shape[1]
+    flat = children.reshape(M0 * C, d)
+    Y = np.empty((N, d))
+    for t in range(-(-N // T)):
+        i0, i1 = t * T, min(N, (t + 1) * T)
+        refined = np.isin(pstar, np.asarray(sel[t], dtype=np.int64))
+        rep = np.where((leaf >= M0)[:, None] & refined[:, None],
+                       flat[np.maximum(leaf - M0, 0)], parents[pstar])
+        Y[i0:i1] = softmax_attention(Q[i0:i1], rep, V, scale)
+    return Y
+
+
+def brute_force_assign(keys, parents, children, force_child=False):
+    """Pure-Python two-stage assignment for tiny inputs: parents ranked by
+    (distance, index); then the chosen parent's children ranked the same way;
+    a child wins only when strictly closer (or always with force_child)."""
+    M0 = len(parents)
+    C = len(children[0])
+
+    def dist(a, b):
+        return sum((x - y) * (x - y) for x, y in zip(a, b))
+
+    out = []
+    for k in keys:
+        p = sorted(range(M0), key=lambda j: (dist(k, parents[j]), j))[0]
+        c = sorted(range(C), key=lambda j: (dist(k, children[p][j]), j))[0]
+        if force_child or dist(k, children[p][c]) < dist(k, parents[p]):
+            out.append((p, M0 + p * C + c))
+        else:
+            out.append((p, p))
+    return out
