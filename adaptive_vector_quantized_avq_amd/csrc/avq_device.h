@@ -1,0 +1,230 @@
+// Device-side building blocks shared by the gfx950 kernels of this library.
+//
+// MFMA tile convention (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x4_f32,
+// wave64): lane l = 16*g + i (g = l / 16 in 0..3, i = l % 16).
+//   A operand  lane (g, i) supplies row i, 8 contraction values;
+//   B operand  lane (g, i) supplies column i, the same 8 contraction values;
+//   C/D        lane (g, i) holds rows 4g..4g+3 of column i.
+// Which 8 contraction indices a lane group supplies is free as long as the A
+// and B operands agree; every "Frag" below holds 8 consecutive contraction
+// values of one row/column, the lane group g supplying indices 8g..8g+7 of a
+// 32-wide contraction step.  For bf16 one instruction covers the step; for
+// fp32 eight 16x16x4 instructions do (instruction t takes element t of each
+// lane), which sums the same 32 products.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace avq {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> {
+    bf16x8 v;
+};
+template <> struct Frag<float> {
+    f32x4 lo, hi;
+};
+
+__device__ __forceinline__ f32x4 mma(const Frag<bf16> &a, const Frag<bf16> &b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma(const Frag<float> &a, const Frag<float> &b, f32x4 c)
+{
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[t], b.lo[t], c, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[t], b.hi[t], c, 0, 0, 0);
+    return c;
+}
+
+// 8 consecutive elements at p (16-byte aligned for bf16, 16-byte aligned
+// halves for fp32)
+__device__ __forceinline__ Frag<bf16> load_frag(const bf16 *p)
+{
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8 *>(p);
+    return f;
+}
+__device__ __forceinline__ Frag<float> load_frag(const float *p)
+{
+    Frag<float> f;
+    f.lo = *reinterpret_cast<const f32x4 *>(p);
+    f.hi = *reinterpret_cast<const f32x4 *>(p + 4);
+    return f;
+}
+template <typename T> __device__ __forceinline__ Frag<T> zero_frag();
+template <> __device__ __forceinline__ Frag<bf16> zero_frag<bf16>()
+{
+    Frag<bf16> f;
+    f.v = bf16x8{};
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> zero_frag<float>()
+{
+    Frag<float> f;
+    f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+    f.hi = f.lo;
+    return f;
+}
+
+__device__ __forceinline__ void store_frag(bf16 *dst, const Frag<bf16> &f)
+{
+    *reinterpret_cast<bf16x8 *>(dst) = f.v;
+}
+__device__ __forceinline__ void store_frag(float *dst, const Frag<float> &f)
+{
+    *reinterpret_cast<f32x4 *>(dst) = f.lo;
+    *reinterpret_cast<f32x4 *>(dst + 4) = f.hi;
+}
+// store s * f (used with s = -2, exact in both types)
+__device__ __forceinline__ void store_scaled_frag(bf16 *dst, const Frag<bf16> &f, float s)
+{
+    Frag<bf16> o;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o.v[k] = (bf16)((float)f.v[k] * s);
+    store_frag(dst, o);
+}
+__device__ __forceinline__ void store_scaled_frag(float *dst, const Frag<float> &f, float s)
+{
+    Frag<float> o;
+    o.lo = f.lo * s;
+    o.hi = f.hi * s;
+    store_frag(dst, o);
+}
+__device__ __forceinline__ float frag_elem(const Frag<bf16> &f, int k) { return (float)f.v[k]; }
+__device__ __forceinline__ float frag_elem(const Frag<float> &f, int k)
+{
+    return k < 4 ? f.lo[k] : f.hi[k - 4];
+}
+
+__host__ __device__ __forceinline__ int round16(int x) { return (x + 15) & ~15; }
+__host__ __device__ __forceinline__ int round32(int x) { return (x + 31) & ~31; }
+
+// Build a B-operand fragment from two 16x16 accumulator tiles of the same
+// column (rows 4g..4g+3 of each): element k < 4 is row 4g+k of tile a,
+// element k >= 4 is row 4g+k-4 of tile b.  The matching A operand must
+// present its contraction index in the same order (see perm32 below).
+__device__ __forceinline__ Frag<bf16> pack_frag_bf16(f32x4 a, f32x4 b)
+{
+    Frag<bf16> f;
+    f.v[0] = (bf16)a[0];
+    f.v[1] = (bf16)a[1];
+    f.v[2] = (bf16)a[2];
+    f.v[3] = (bf16)a[3];
+    f.v[4] = (bf16)b[0];
+    f.v[5] = (bf16)b[1];
+    f.v[6] = (bf16)b[2];
+    f.v[7] = (bf16)b[3];
+    return f;
+}
+template <typename T> __device__ __forceinline__ Frag<T> pack_frag(f32x4 a, f32x4 b);
+template <> __device__ __forceinline__ Frag<bf16> pack_frag<bf16>(f32x4 a, f32x4 b)
+{
+    return pack_frag_bf16(a, b);
+}
+template <> __device__ __forceinline__ Frag<float> pack_frag<float>(f32x4 a, f32x4 b)
+{
+    Frag<float> f;
+    f.lo = a;
+    f.hi = b;
+    return f;
+}
+
+// Position, inside a 32-wide contraction step, at which row rho (0..31) of
+// the two stacked accumulator tiles sits in the packed fragments above:
+// lane group g supplies positions 8g..8g+7 = rows 4g..4g+3 then 16+4g..16+4g+3.
+__host__ __device__ __forceinline__ int perm32(int rho)
+{
+    return 8 * ((rho & 15) >> 2) + 4 * (rho >> 4) + (rho & 3);
+}
+
+// ---------------------------------------------------------------- conversions
+template <typename T> __device__ __forceinline__ T from_float(float x);
+template <> __device__ __forceinline__ float from_float<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_float<bf16>(float x) { return (bf16)x; }
+__device__ __forceinline__ float to_float(float x) { return x; }
+__device__ __forceinline__ float to_float(bf16 x) { return (float)x; }
+
+// nearest bf16 to a double (ties to even), as its bit pattern; the operand
+// is assumed to lie in bf16's normal range or be zero
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double x)
+{
+    unsigned long long b = (unsigned long long)__double_as_longlong(x);
+    unsigned long long lsb = (b >> 45) & 1ull;
+    b = (b + ((1ull << 44) - 1ull) + lsb) & ~((1ull << 45) - 1ull);
+    float f = (float)__longlong_as_double((long long)b);   // exact
+    return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+// ---------------------------------------------------------------- wave reductions
+// DPP row controls (within rows of 16 lanes)
+#define AVQ_DPP_QUAD_XOR1 0xB1    // quad_perm [1,0,3,2]
+#define AVQ_DPP_QUAD_XOR2 0x4E    // quad_perm [2,3,0,1]
+#define AVQ_DPP_ROW_HALF_MIRROR 0x141
+#define AVQ_DPP_ROW_MIRROR 0x140
+
+template <int CTRL> __device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the 16 lanes of each row (result in every lane of the row)
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp<AVQ_DPP_QUAD_XOR1>(x);
+    x += dpp<AVQ_DPP_QUAD_XOR2>(x);
+    x += dpp<AVQ_DPP_ROW_HALF_MIRROR>(x);
+    x += dpp<AVQ_DPP_ROW_MIRROR>(x);
+    return x;
+}
+
+// across the four lane groups g (lanes i, i+16, i+32, i+48)
+__device__ __forceinline__ float xgroup_sum(float x)
+{
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+__device__ __forceinline__ float xgroup_max(float x)
+{
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+__device__ __forceinline__ float xgroup_min(float x)
+{
+    x = fminf(x, __shfl_xor(x, 16));
+    x = fminf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+// (value, index) minimum across the lane groups; ties -> smaller index
+__device__ __forceinline__ void xgroup_argmin(float &v, int &idx)
+{
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+        float ov = __shfl_xor(v, m);
+        int oi = __shfl_xor(idx, m);
+        bool take = (ov < v) || (ov == v && oi < idx);
+        v = take ? ov : v;
+        idx = take ? oi : idx;
+    }
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+__device__ __forceinline__ int mbcnt(unsigned long long mask)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
+}
+
+}  // namespace avq

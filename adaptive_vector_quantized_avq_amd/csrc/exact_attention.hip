@@ -1,0 +1,135 @@
+// Exact softmax attention ("AVQ-Attention", Sec. 3.1), non-causal, computed
+// flash-attention style (Sec. 3.3: per key block J, X_I(J) = A_IJ V_J and
+// Z_I(J) = sum_j A_Ij, accumulated with an online maximum).  It serves as the
+// timing context next to the AVQ kernels and as the GPU-side check of the
+// one-key-per-leaf limit, where AVQ must reproduce exact attention.
+//
+// Same transposed layout as the AVQ attention kernel: S^T = K_J . Q^T with
+// one query per lane, so P^T feeds X^T += V_J^T . P^T directly.
+#include "avq_kernels.h"
+
+namespace avq {
+
+constexpr float kLog2eExact = 1.4426950408889634f;
+constexpr int kExactKeys = 64;   // keys per LDS block
+constexpr int kExactWaves = 4;   // 16 queries per wave
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kExactWaves) void exact_attention_kernel(
+    const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, int N, float sl2,
+    T *__restrict__ Y)
+{
+    constexpr int KB = kExactKeys;
+    constexpr int NT = 64 * kExactWaves;
+    constexpr int KS = D / 32;
+    constexpr int DB = D / 16;
+    constexpr int LDP = D + 8;
+    constexpr int LDV = KB + 8;
+    __shared__ __align__(16) T Ks[KB * LDP];
+    __shared__ __align__(16) T Vt[D * LDV];
+
+    const int bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, i16 = lane & 15;
+    const int64_t base = (int64_t)bh * N * D;
+    const int q = blockIdx.x * (16 * kExactWaves) + 16 * w + i16;
+    const bool qv = q < N;
+    Frag<T> qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = qv ? load_frag(Q + base + (int64_t)q * D + 32 * ks + 8 * g) : zero_frag<T>();
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x4 X[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) X[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = 0; k0 < N; k0 += KB) {
+        __syncthreads();
+        for (int e = tid * 8; e < KB * D; e += NT * 8) {
+            const int r = e / D, c = e % D;
+            Frag<T> f = (k0 + r) < N ? load_frag(K + base + (int64_t)(k0 + r) * D + c) : zero_frag<T>();
+            store_frag(Ks + r * LDP + c, f);
+        }
+        for (int e = tid; e < KB * (D / 8); e += NT) {
+            const int r = e / (D / 8), c8 = e % (D / 8);
+            Frag<T> f = (k0 + r) < N ? load_frag(V + base + (int64_t)(k0 + r) * D + 8 * c8) : zero_frag<T>();
+            const int pos = (r & ~31) + perm32(r & 31);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) Vt[(8 * c8 + k) * LDV + pos] = from_float<T>(frag_elem(f, k));
+        }
+        __syncthreads();
+        f32x4 Sb[KB / 16];
+        float mb = -INFINITY;
+#pragma unroll
+        for (int rb = 0; rb < KB / 16; ++rb) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                a = mma(load_frag(Ks + (16 * rb + i16) * LDP + 32 * ks + 8 * g), qf[ks], a);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = (k0 + 16 * rb + 4 * g + r) < N ? a[r] * sl2 : -INFINITY;
+                a[r] = x;
+                mb = fmaxf(mb, x);
+            }
+            Sb[rb] = a;
+        }
+        mb = xgroup_max(mb);
+        const float mn = fmaxf(m, mb);
+        const float alpha = exp2f(m - mn);
+        m = mn;
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) X[db] *= alpha;
+#pragma unroll
+        for (int rb = 0; rb < KB / 16; ++rb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float e = exp2f(Sb[rb][r] - m);
+                Sb[rb][r] = e;
+                lsum += e;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < KB / 32; ++s) {
+            const Frag<T> bf = pack_frag<T>(Sb[2 * s], Sb[2 * s + 1]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                X[db] = mma(load_frag(Vt + (16 * db + i16) * LDV + 32 * s + 8 * g), bf, X[db]);
+        }
+    }
+    const float L = xgroup_sum(lsum);
+    if (qv) {
+        const float rl = 1.0f / L;
+        T *yr = Y + base + (int64_t)q * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yr[16 * db + 4 * g + r] = from_float<T>(X[db][r] * rl);
+    }
+}
+
+template <typename T, int D>
+static hipError_t launch_exact_t(const void *Q, const void *K, const void *V, int B, int H, int N,
+                                 float scale, void *Y, hipStream_t stream)
+{
+    const int qpb = 16 * kExactWaves;
+    hipLaunchKernelGGL((exact_attention_kernel<T, D>), dim3((N + qpb - 1) / qpb, B * H),
+                       dim3(64 * kExactWaves), 0, stream, (const T *)Q, (const T *)K, (const T *)V, N,
+                       scale * kLog2eExact, (T *)Y);
+    return hipGetLastError();
+}
+
+hipError_t launch_exact_attention(const void *Q, const void *K, const void *V, int B, int H, int N,
+                                  int d, float scale, int dtype, void *Y, hipStream_t stream)
+{
+    if (dtype == 1) {
+        if (d == 64) return launch_exact_t<bf16, 64>(Q, K, V, B, H, N, scale, Y, stream);
+        return launch_exact_t<bf16, 128>(Q, K, V, B, H, N, scale, Y, stream);
+    }
+    if (d == 64) return launch_exact_t<float, 64>(Q, K, V, B, H, N, scale, Y, stream);
+    return launch_exact_t<float, 128>(Q, K, V, B, H, N, scale, Y, stream);
+}
+
+}  // namespace avq

@@ -85,7 +85,10 @@ def _f64(a):
 
 
 def default_threads() -> int:
-    return max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
+    """Host threads for independent units: the CPUs this process may use,
+    at most 16 (one GPU's share of a GPU host)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, n))
 
 
 def _run(fn, units, threads):

@@ -1,0 +1,207 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Every case prints what it runs before touching the GPU."""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _protocol import Y_TOL, check_selection, check_stage1, tensor_to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    sys.stdout.write(f"\n[case] {msg}\n")
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def avq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import adaptive_vector_quantized_avq_amd as m
+    m.load_library()
+    return m
+
+
+DEV = "cuda:0"
+
+
+def to_dev(arr, dtype):
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(DEV)
+
+
+def run_gpu(avq, inp, P, T, force_child=False):
+    ch = to_dev(inp.children, inp.dtype)
+    K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
+    parents, sq = avq.build_tree(ch)
+    vsum, count, leaf = avq.assign_aggregate(K, V, parents, ch, sq, force_child=force_child,
+                                             want_leaf=True)
+    Y, sel, imp = avq.attention_fwd(Q, parents, ch, vsum, count, P, T, inp.scale,
+                                    want_sel=True, want_importance=True)
+    torch.cuda.synchronize()
+    return dict(parents=tensor_to_f64(parents, inp.dtype), sqnorm=sq.cpu().numpy(),
+                vsum=vsum.cpu().numpy().astype(np.float64), count=count.cpu().numpy(),
+                leaf=leaf.cpu().numpy(), Y=tensor_to_f64(Y, inp.dtype),
+                sel=sel.cpu().numpy(), imp=imp.cpu().numpy().astype(np.float64))
+
+
+def check_all(avq, inp, P=None, T=None, force_child=False, tile_ranges=None):
+    """Run the whole forward on the GPU once, check stage 1 on every key and
+    stage 2 on the given query-tile ranges (default: every tile)."""
+    P = inp.P if P is None else P
+    T = inp.T if T is None else T
+    _say(f"{inp.name} dtype={inp.dtype} B={inp.B} H={inp.H} N={inp.N} d={inp.d} M0={inp.M0} "
+         f"C={inp.C} P={P} T={T} force_child={force_child} seed={inp.seed}")
+    g = run_gpu(avq, inp, P, T, force_child)
+    ch64 = inp.f64("children")
+    par64, sq64 = oracle.build_tree(ch64, inp.dtype)
+    np.testing.assert_array_equal(g["parents"], par64)
+    np.testing.assert_array_equal(g["sqnorm"], sq64.astype(np.float32))
+    a, vsum, count = check_stage1(inp, par64, g["leaf"], g["vsum"], g["count"], force_child)
+    Q64 = inp.f64("Q")
+    nt = -(-inp.N // T)
+    errs, namb = [], 0
+    for (t0, t1) in (tile_ranges or [(0, nt)]):
+        _, w, sel = oracle.attention(Q64, par64, ch64, vsum, count, P, T, inp.scale, tiles=(t0, t1))
+        namb += check_selection(w[:, :, t0:t1], sel[:, :, t0:t1], g["sel"][:, :, t0:t1], P)
+        np.testing.assert_allclose(g["imp"][:, :, t0:t1], w[:, :, t0:t1], rtol=2e-4, atol=1e-7 * T)
+        Yf, _, _ = oracle.attention(Q64, par64, ch64, vsum, count, P, T, inp.scale,
+                                    forced_sel=g["sel"], tiles=(t0, t1))
+        rows = slice(t0 * T, min(inp.N, t1 * T))
+        errs.append(float(np.abs(g["Y"][:, :, rows] - Yf[:, :, rows]).max()))
+    err = max(errs)
+    _say(f"  max|dY|={err:.3e} ambiguous keys={a['n_ambiguous']} tiles={namb} "
+         f"residual keys={int(count[..., :inp.M0].sum() - count[..., inp.M0:].sum())}")
+    assert err <= Y_TOL[inp.dtype], err
+    return dict(err=err, g=g, vsum=vsum, count=count)
+
+
+# ------------------------------------------------------------------ workloads
+
+
+@pytest.mark.parametrize("name,N", [("tiny-f32", 1024), ("vit-b", 3000), ("seg-zipf", 5000),
+                                    ("long-64k", 9000), ("wide-d128", 3000)])
+def test_workload_reduced(avq, name, N):
+    inp = synth.generate(name, B=1, H=2, N=N)
+    check_all(avq, inp)
+
+
+@pytest.mark.parametrize("P", [0, 4, 16, 128])
+def test_seg_zipf_P_sweep(avq, P):
+    inp = synth.generate("seg-zipf", B=2, H=2, N=4100)
+    check_all(avq, inp, P=P)
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_workload_full_size_sampled_tiles(avq, name):
+    """Full size of every workload; stage 1 checked on every key, stage 2
+    on the first, a middle and the last query tile of every (b, h)."""
+    inp = synth.generate(name)
+    nt = inp.ntiles
+    check_all(avq, inp, tile_ranges=[(0, 1), (nt // 2, nt // 2 + 1), (nt - 1, nt)])
+
+
+# ------------------------------------------------------------------ edge shapes
+
+EDGE = [
+    # dtype, d, M0, C, P, T, N, force_child
+    ("bf16", 64, 1, 4, 1, 64, 1, False),
+    ("bf16", 64, 1, 4, 0, 16, 37, False),
+    ("f32", 64, 5, 2, 3, 16, 300, False),
+    ("bf16", 64, 17, 8, 17, 32, 777, False),
+    ("bf16", 64, 33, 16, 5, 128, 2049, False),
+    ("f32", 128, 24, 4, 7, 64, 1500, False),
+    ("bf16", 128, 64, 16, 64, 128, 1025, False),
+    ("bf16", 64, 256, 8, 256, 128, 2100, False),
+    ("bf16", 64, 40, 8, 6, 64, 3000, True),
+    ("f32", 64, 16, 4, 4, 64, 1024, True),
+]
+
+
+@pytest.mark.parametrize("dtype,d,M0,C,P,T,N,force", EDGE)
+def test_edge_shapes(avq, dtype, d, M0, C, P, T, N, force):
+    inp = synth.generate("vit-b", B=1, H=2, N=N, d=d, M0=M0, C=C, P=P, T=T, dtype=dtype,
+                         seed=77 + M0 + N)
+    check_all(avq, inp, force_child=force)
+
+
+def test_scale_one_and_dyadic_tree(avq):
+    inp = synth.generate_dyadic(5, B=2, H=2, N=700, d=64, M0=8, C=4, P=3, T=32)
+    inp.scale = 1.0 / 64.0
+    check_all(avq, inp)
+
+
+# ------------------------------------------------------------------ invariants
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_key_per_leaf_equals_exact_attention(avq, dtype):
+    inp = synth.generate_one_key_per_leaf(21, B=1, H=2, d=64, M0=16, C=8, T=32, dtype=dtype)
+    _say(f"one key per leaf dtype={dtype} N={inp.N}")
+    r = check_all(avq, inp, P=16, T=32)
+    Q, K, V = (to_dev(x, dtype) for x in (inp.Q, inp.K, inp.V))
+    Ye = tensor_to_f64(avq.exact_attention_fwd(Q, K, V, inp.scale), dtype)
+    from _refs import softmax_attention
+    ref = np.stack([softmax_attention(inp.f64("Q")[0, h], inp.f64("K")[0, h], inp.f64("V")[0, h],
+                                      inp.scale) for h in range(2)])[None]
+    assert np.abs(Ye - ref).max() <= Y_TOL[dtype]
+    assert np.abs(r["g"]["Y"] - ref).max() <= Y_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_exact_attention_kernel(avq, dtype, d):
+    _say(f"exact attention dtype={dtype} d={d}")
+    rng = np.random.default_rng(3)
+    B, H, N = 1, 2, 333
+    x = rng.standard_normal((3, B, H, N, d))
+    st = [synth.to_storage(x[i], dtype) for i in range(3)]
+    Q, K, V = (to_dev(s, dtype) for s in st)
+    Y = tensor_to_f64(avq.exact_attention_fwd(Q, K, V, 0.125), dtype)
+    f = [synth.storage_to_f64(s, dtype) for s in st]
+    from _refs import softmax_attention
+    ref = np.stack([softmax_attention(f[0][0, h], f[1][0, h], f[2][0, h], 0.125) for h in range(H)])[None]
+    assert np.abs(Y - ref).max() <= Y_TOL[dtype] / 4
+
+
+def test_constant_values_give_constant_output(avq):
+    inp = synth.generate("long-64k", B=1, H=2, N=4096)
+    inp.V[:] = synth.f64_to_bf16_bits(np.full(1, 0.75))[0]
+    _say("constant values")
+    for P in (0, 16, 256):
+        ch = to_dev(inp.children, "bf16")
+        K, V, Q = (to_dev(x, "bf16") for x in (inp.K, inp.V, inp.Q))
+        parents, sq = avq.build_tree(ch)
+        vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq)
+        Y, _, _ = avq.attention_fwd(Q, parents, ch, vsum, count, P, 128, inp.scale)
+        torch.cuda.synchronize()
+        assert np.abs(tensor_to_f64(Y, "bf16") - 0.75).max() <= 4e-3
+
+
+def test_invalid_arguments_raise(avq):
+    _say("invalid arguments")
+    inp = synth.generate("vit-b", B=1, H=1, N=256, M0=8)
+    ch = to_dev(inp.children, "bf16")
+    K, V, Q = (to_dev(x, "bf16") for x in (inp.K, inp.V, inp.Q))
+    parents, sq = avq.build_tree(ch)
+    vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq)
+    with pytest.raises(avq.AvqError, match="INVALID_ARG"):
+        avq.attention_fwd(Q, parents, ch, vsum, count, 9, 128, inp.scale)   # P > M0
+    with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
+        avq.attention_fwd(Q, parents, ch, vsum, count, 2, 48, inp.scale)   # tile 48
+    with pytest.raises(avq.AvqError, match="INVALID_ARG"):
+        avq.attention_fwd(Q, parents, ch, vsum, count, 2, 128, float("nan"))
+    with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
+        bad = torch.zeros((1, 8, 4, 96), dtype=torch.bfloat16, device=DEV)
+        avq.build_tree(bad)   # d = 96
+    torch.cuda.synchronize()
