@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void refine_aggregate_kernel(
     const T *__restrict__ children, const float *__restrict__ sqnorm, int H, int N, int M0, int C,
     int nchunks, int force_child, const int32_t *__restrict__ sorted,
     const int32_t *__restrict__ chunk_off, float *__restrict__ vsum, int32_t *__restrict__ count,
-    int32_t *__restrict__ leaf)
+    int32_t *__restrict__ leaf, unsigned char *__restrict__ pack)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int G = kRefineGroup;
@@ -332,6 +332,38 @@ __global__ __launch_bounds__(256) void refine_aggregate_kernel(
         for (int c = 0; c < C; ++c) s += cnt[lp * C + c];
         cs[p0 + lp] = s;
     }
+
+    // the same aggregates as stage-2 operands (layout in PackLayout)
+    const PackLayout PL = pack_layout(M0, C, D, (int)sizeof(T));
+    const int M0p = padded_parents(M0);
+    unsigned char *pk = pack + (size_t)bh * PL.bytes;
+    T *pvt = reinterpret_cast<T *>(pk + PL.pvt);
+    float *pnp = reinterpret_cast<float *>(pk + PL.pn);
+    T *cvt = reinterpret_cast<T *>(pk + PL.cvt);
+    float *cnp = reinterpret_cast<float *>(pk + PL.cn);
+    for (int e = tid; e < Gv * D; e += 256) {
+        const int lp = e / D, t = e % D, j = p0 + lp;
+        float s = acc[(G * C + lp) * LDA + t];
+        for (int c = 0; c < C; ++c) s += acc[(lp * C + c) * LDA + t];
+        pvt[(size_t)t * M0p + (j & ~31) + perm32(j & 31)] = from_float<T>(s);
+    }
+    for (int lp = tid; lp < Gv; lp += 256) {
+        int s = cnt[G * C + lp];
+        for (int c = 0; c < C; ++c) s += cnt[lp * C + c];
+        pnp[p0 + lp] = (float)s;
+    }
+    for (int e = tid; e < Gv * D * C; e += 256) {
+        const int lp = e / (D * C), rem = e % (D * C), t = rem / C, c = rem % C;
+        cvt[((size_t)(p0 + lp) * D + t) * C + c] = from_float<T>(acc[(lp * C + c) * LDA + t]);
+    }
+    for (int e = tid; e < Gv * C; e += 256) cnp[(size_t)p0 * C + e] = (float)cnt[e];
+    if (p0 + Gv == M0) {   // padding columns of the parent operands
+        for (int e = tid; e < (M0p - M0) * D; e += 256) {
+            const int j = M0 + e / D, t = e % D;
+            pvt[(size_t)t * M0p + (j & ~31) + perm32(j & 31)] = from_float<T>(0.f);
+        }
+        for (int j = M0 + tid; j < M0p; j += 256) pnp[j] = 0.f;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -339,8 +371,8 @@ __global__ __launch_bounds__(256) void refine_aggregate_kernel(
 template <typename T, int D>
 static hipError_t launch_t(const void *K, const void *V, const void *parents, const void *children,
                            const float *sqnorm, int B, int H, int N, int M0, int C, unsigned flags,
-                           float *vsum, int32_t *count, int32_t *leaf, const AssignWorkspace &ws,
-                           hipStream_t stream)
+                           float *vsum, int32_t *count, int32_t *leaf, void *pack,
+                           const AssignWorkspace &ws, hipStream_t stream)
 {
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     const int M0p = round16(M0);
@@ -371,24 +403,24 @@ static hipError_t launch_t(const void *K, const void *V, const void *parents, co
     hipLaunchKernelGGL((refine_aggregate_kernel<T, D>), dim3(ngroups, B * H), dim3(256), lds2, stream,
                        (const T *)K, (const T *)V, (const T *)parents, (const T *)children, sqnorm, H,
                        N, M0, C, nchunks, (flags & 1u) ? 1 : 0, ws.sorted, ws.chunk_off, vsum, count,
-                       leaf);
+                       leaf, (unsigned char *)pack);
     return hipGetLastError();
 }
 
 hipError_t launch_assign_aggregate(const void *K, const void *V, const void *parents,
                                    const void *children, const float *sqnorm, int B, int H, int N,
                                    int d, int M0, int C, int dtype, unsigned flags, float *vsum,
-                                   int32_t *count, int32_t *leaf, const AssignWorkspace &ws,
-                                   hipStream_t stream)
+                                   int32_t *count, int32_t *leaf, void *pack,
+                                   const AssignWorkspace &ws, hipStream_t stream)
 {
     if (dtype == 1) {
         if (d == 64)
-            return launch_t<bf16, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
-        return launch_t<bf16, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
+            return launch_t<bf16, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
+        return launch_t<bf16, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
     }
     if (d == 64)
-        return launch_t<float, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
-    return launch_t<float, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
+        return launch_t<float, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
+    return launch_t<float, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
 }
 
 }  // namespace avq

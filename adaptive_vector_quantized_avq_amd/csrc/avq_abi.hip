@@ -93,12 +93,18 @@ size_t avq_assign_aggregate_workspace_size(int B, int H, int N, int M0, int C, i
     return avq::assign_workspace_bytes(B, H, N, M0);
 }
 
+size_t avq_operand_pack_size(int B, int H, int M0, int C, int d, int dtype)
+{
+    if (check_tree(H, M0, C, d, dtype) != AVQ_OK || B < 1) return 0;
+    return (size_t)B * H * avq::pack_layout(M0, C, d, dtype == AVQ_BF16 ? 2 : 4).bytes;
+}
+
 int avq_assign_aggregate(const void *K, const void *V, const void *parents, const void *children,
                          const float *sqnorm, int B, int H, int N, int d, int M0, int C, int dtype,
                          unsigned flags, float *vsum_out, int32_t *count_out, int32_t *leaf_out,
-                         void *workspace, size_t workspace_bytes, void *stream)
+                         void *pack_out, void *workspace, size_t workspace_bytes, void *stream)
 {
-    AVQ_REQUIRE(K && V && parents && children && sqnorm && vsum_out && count_out && workspace,
+    AVQ_REQUIRE(K && V && parents && children && sqnorm && vsum_out && count_out && pack_out && workspace,
                 AVQ_ERR_INVALID_ARG, "null pointer argument");
     AVQ_REQUIRE((flags & ~(unsigned)AVQ_FLAG_FORCE_CHILD) == 0, AVQ_ERR_INVALID_ARG, "unknown flag bits");
     int st = check_tree(H, M0, C, d, dtype);
@@ -110,16 +116,15 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents, cons
     AVQ_REQUIRE(((uintptr_t)workspace & 255u) == 0, AVQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     const avq::AssignWorkspace ws = avq::carve_assign_workspace(workspace, B, H, N, M0);
     return hip_status(avq::launch_assign_aggregate(K, V, parents, children, sqnorm, B, H, N, d, M0, C,
-                                                   dtype, flags, vsum_out, count_out, leaf_out, ws,
-                                                   (hipStream_t)stream));
+                                                   dtype, flags, vsum_out, count_out, leaf_out,
+                                                   pack_out, ws, (hipStream_t)stream));
 }
 
-int avq_attention_fwd(const void *Q, const void *parents, const void *children, const float *vsum,
-                      const int32_t *count, int B, int H, int N, int d, int M0, int C, int P, int tile,
-                      float scale, int dtype, void *Y_out, int32_t *sel_out, float *importance_out,
-                      void *stream)
+int avq_attention_fwd(const void *Q, const void *parents, const void *children, const void *pack,
+                      int B, int H, int N, int d, int M0, int C, int P, int tile, float scale,
+                      int dtype, void *Y_out, int32_t *sel_out, float *importance_out, void *stream)
 {
-    AVQ_REQUIRE(Q && parents && children && vsum && count && Y_out, AVQ_ERR_INVALID_ARG,
+    AVQ_REQUIRE(Q && parents && children && pack && Y_out, AVQ_ERR_INVALID_ARG,
                 "null pointer argument");
     int st = check_tree(H, M0, C, d, dtype);
     if (st != AVQ_OK) return st;
@@ -128,12 +133,12 @@ int avq_attention_fwd(const void *Q, const void *parents, const void *children, 
     AVQ_REQUIRE(P >= 0 && P <= M0, AVQ_ERR_INVALID_ARG, "P must satisfy 0 <= P <= M0");
     AVQ_REQUIRE(tile >= 1, AVQ_ERR_INVALID_ARG, "tile must be >= 1");
     AVQ_REQUIRE(isfinite(scale), AVQ_ERR_INVALID_ARG, "scale must be finite");
-    AVQ_REQUIRE(tile == 16 || tile == 32 || tile == 64 || tile == 128, AVQ_ERR_UNSUPPORTED,
-                "tile must be 16, 32, 64 or 128");
-    AVQ_REQUIRE(avq::attention_lds_bytes(d, M0, tile, dtype) <= 160 * 1024, AVQ_ERR_UNSUPPORTED,
-                "codebook does not fit in LDS for this dtype/d/M0");
-    return hip_status(avq::launch_attention_fwd(Q, parents, children, vsum, count, B, H, N, d, M0, C, P,
-                                                tile, scale, dtype, Y_out, sel_out, importance_out,
+    AVQ_REQUIRE(tile == 32 || tile == 64 || tile == 128 || tile == 256, AVQ_ERR_UNSUPPORTED,
+                "tile must be 32, 64, 128 or 256");
+    AVQ_REQUIRE(avq::attention_child_chunk(d, M0, C, P, tile, dtype) > 0, AVQ_ERR_UNSUPPORTED,
+                "codebook does not fit in LDS for this dtype/d/M0/P");
+    return hip_status(avq::launch_attention_fwd(Q, parents, children, pack, B, H, N, d, M0, C, P, tile,
+                                                scale, dtype, Y_out, sel_out, importance_out,
                                                 (hipStream_t)stream));
 }
 

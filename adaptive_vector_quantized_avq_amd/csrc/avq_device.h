@@ -186,6 +186,49 @@ __device__ __forceinline__ float row16_sum(float x)
     return x;
 }
 
+#define AVQ_DPP_ROW_ROR8 0x128       // rotate by 8 inside a row: lane i <-> i ^ 8
+
+// One halving step of a 16-lane reduce-scatter: lanes with `up` set keep the
+// upper half of the N blocks, the others the lower half; each adds the half
+// its DPP partner gives away (the partner differs from it in the split bit).
+template <int N, int CTRL>
+__device__ __forceinline__ void halve_blocks(f32x4 *t, bool up)
+{
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float keep = up ? t[j + N / 2][r] : t[j][r];
+            const float give = up ? t[j][r] : t[j + N / 2][r];
+            t[j][r] = keep + dpp<CTRL>(give);
+        }
+    }
+}
+
+// Reduce-scatter over the 16 lanes of each row: on entry every lane holds
+// NRB blocks of 4 values; on exit t[0] holds, summed over the row's 16 lanes,
+// block (i16 >> (4 - log2 NRB)).  The partner masks 8, 7, 2, 1 (row_ror:8,
+// row_half_mirror, quad_perm xor 2, quad_perm xor 1) span all 16 lanes, so
+// every sum covers each lane exactly once; lanes left after log2 NRB halving
+// steps finish with an all-reduce on the remaining masks.
+template <int NRB>
+__device__ __forceinline__ f32x4 row16_reduce_scatter(f32x4 *t, int i16)
+{
+    static_assert(NRB == 2 || NRB == 4 || NRB == 8 || NRB == 16, "NRB");
+    halve_blocks<NRB, AVQ_DPP_ROW_ROR8>(t, (i16 & 8) != 0);
+    if constexpr (NRB >= 4) halve_blocks<NRB / 2, AVQ_DPP_ROW_HALF_MIRROR>(t, (i16 & 4) != 0);
+    if constexpr (NRB >= 8) halve_blocks<NRB / 4, AVQ_DPP_QUAD_XOR2>(t, (i16 & 2) != 0);
+    if constexpr (NRB >= 16) halve_blocks<NRB / 8, AVQ_DPP_QUAD_XOR1>(t, (i16 & 1) != 0);
+    f32x4 v = t[0];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if constexpr (NRB <= 2) v[r] += dpp<AVQ_DPP_ROW_HALF_MIRROR>(v[r]);
+        if constexpr (NRB <= 4) v[r] += dpp<AVQ_DPP_QUAD_XOR2>(v[r]);
+        if constexpr (NRB <= 8) v[r] += dpp<AVQ_DPP_QUAD_XOR1>(v[r]);
+    }
+    return v;
+}
+
 // across the four lane groups g (lanes i, i+16, i+32, i+48)
 __device__ __forceinline__ float xgroup_sum(float x)
 {
@@ -220,6 +263,31 @@ __device__ __forceinline__ void xgroup_argmin(float &v, int &idx)
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// max of three finite floats in one VALU op (no NaN canonicalisation)
+__device__ __forceinline__ float max3f(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// flip the sign of every element of a fragment
+__device__ __forceinline__ Frag<bf16> negate(const Frag<bf16> &f)
+{
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 u = __builtin_bit_cast(u32x4, f.v) ^ 0x80008000u;
+    Frag<bf16> o;
+    o.v = __builtin_bit_cast(bf16x8, u);
+    return o;
+}
+__device__ __forceinline__ Frag<float> negate(const Frag<float> &f)
+{
+    Frag<float> o;
+    o.lo = -f.lo;
+    o.hi = -f.hi;
+    return o;
+}
 
 __device__ __forceinline__ int mbcnt(unsigned long long mask)
 {

@@ -23,6 +23,38 @@ struct AssignWorkspace {
     size_t bytes;
 };
 
+// Aggregates rearranged as stage-2 MFMA operands (written by stage 1 next to
+// the fp32 value sums).  Per (b, h), byte offsets into one block of
+// `bytes` bytes, element type T (the input dtype):
+//   pvt [D][M0p]  T      parent value sums, transposed; column of parent j
+//                        at (j & ~31) + perm32(j & 31), zero for j >= M0
+//   pn  [M0p]     float  parent counts (zero for j >= M0)
+//   cvt [M0][D][C] T     child value sums, children innermost
+//   cn  [M0][C]   float  child counts
+// with M0p = padded_parents(M0).
+struct PackLayout {
+    size_t pvt, pn, cvt, cn, bytes;
+};
+// parents padded to a power of two >= 32, so that the stage-2 kernel can be
+// specialised on the number of 16-row MFMA blocks
+__host__ __device__ inline int padded_parents(int M0)
+{
+    return M0 <= 32 ? 32 : M0 <= 64 ? 64 : M0 <= 128 ? 128 : 256;
+}
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline PackLayout pack_layout(int M0, int C, int D, int esize)
+{
+    const int M0p = padded_parents(M0);
+    PackLayout L;
+    size_t o = 0;
+    L.pvt = o; o = align256(o + (size_t)D * M0p * esize);
+    L.pn = o;  o = align256(o + (size_t)M0p * 4);
+    L.cvt = o; o = align256(o + (size_t)M0 * D * C * esize);
+    L.cn = o;  o = align256(o + (size_t)M0 * C * 4);
+    L.bytes = o;
+    return L;
+}
+
 size_t assign_workspace_bytes(int B, int H, int N, int M0);
 AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0);
 
@@ -32,16 +64,18 @@ hipError_t launch_build_tree(const void *children, int H, int M0, int C, int d, 
 hipError_t launch_assign_aggregate(const void *K, const void *V, const void *parents,
                                    const void *children, const float *sqnorm, int B, int H, int N,
                                    int d, int M0, int C, int dtype, unsigned flags, float *vsum,
-                                   int32_t *count, int32_t *leaf, const AssignWorkspace &ws,
-                                   hipStream_t stream);
+                                   int32_t *count, int32_t *leaf, void *pack,
+                                   const AssignWorkspace &ws, hipStream_t stream);
 
 // returns hipErrorInvalidConfiguration when the shape does not fit the
 // kernel's on-chip budget
 hipError_t launch_attention_fwd(const void *Q, const void *parents, const void *children,
-                                const float *vsum, const int32_t *count, int B, int H, int N, int d,
-                                int M0, int C, int P, int tile, float scale, int dtype, void *Y,
-                                int32_t *sel, float *importance, hipStream_t stream);
-size_t attention_lds_bytes(int d, int M0, int tile, int dtype);
+                                const void *pack, int B, int H, int N, int d, int M0, int C, int P,
+                                int tile, float scale, int dtype, void *Y, int32_t *sel,
+                                float *importance, hipStream_t stream);
+// rows of children staged per tile and per step by the attention kernel, or
+// 0 if the shape does not fit its LDS budget
+int attention_child_chunk(int d, int M0, int C, int P, int tile, int dtype);
 
 hipError_t launch_exact_attention(const void *Q, const void *K, const void *V, int B, int H, int N,
                                   int d, float scale, int dtype, void *Y, hipStream_t stream);

@@ -118,9 +118,12 @@ def main():
     ap.add_argument("--P", type=int, default=None)
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--exact-context", action="store_true",
                     help="also time the in-repo exact softmax attention at the same shape")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy 5 times (a kernel of known "
+                         "traffic, to calibrate the profiler's byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -164,6 +167,8 @@ def main():
     B, H, N, d, S = inp.B, inp.H, inp.N, inp.d, inp.S_tot
     vsum = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
     count = torch.empty((B, H, S), dtype=torch.int32, device=dev)
+    pack = torch.empty(avq.operand_pack_size(B, H, inp.M0, inp.C, d, sets[0][0].dtype),
+                       dtype=torch.uint8, device=dev)
     ws = torch.empty(avq.assign_aggregate_workspace_size(B, H, N, inp.M0, inp.C, d),
                      dtype=torch.uint8, device=dev)
     Y = torch.empty_like(sets[0][0])
@@ -172,10 +177,10 @@ def main():
         Q, K, V = sets[i % len(sets)]
         if ev is not None:
             ev[0].record()
-        avq.assign_aggregate(K, V, parents, ch, sq, workspace=ws, out=(vsum, count))
+        avq.assign_aggregate(K, V, parents, ch, sq, workspace=ws, out=(vsum, count, pack))
         if ev is not None:
             ev[1].record()
-        avq.attention_fwd(Q, parents, ch, vsum, count, P, inp.T, inp.scale, out=Y)
+        avq.attention_fwd(Q, parents, ch, pack, P, inp.T, inp.scale, out=Y)
         if ev is not None:
             ev[2].record()
 
@@ -262,6 +267,20 @@ def main():
             "ms": round(ex_ms, 4),
             "TFLOPs": round(4.0 * N * N * d * B * H / (ex_ms * 1e-3) / 1e12, 1),
             "speedup_avq": round(ex_ms / ms_step, 1)}
+
+    if args.copy_probe:
+        nbytes = 256 << 20
+        xa = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+        ya = torch.empty_like(xa)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            ya.copy_(xa)
+        c1.record()
+        torch.cuda.synchronize()
+        out["copy_probe"] = {"bytes_read": nbytes, "bytes_written": nbytes, "launches": 5,
+                             "GBps": round(2 * nbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)}
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")

@@ -29,7 +29,8 @@
  *    avq_last_error() gives a message for the last failure on the calling
  *    thread.
  *  - Supported shapes: head dim d in {64, 128}; C in {2, 4, 8, 16} children
- *    per parent; 1 <= M0 <= 256 parents; query tile in {16, 32, 64, 128}.
+ *    per parent; 1 <= M0 <= 256 parents; 1 <= N <= 1048576; query tile in
+ *    {32, 64, 128, 256} (the pages use tiles of 32 to 128 queries, Table 8).
  *  - Codeword slots: j in [0, M0) is parent j; j = M0 + p*C + c is child c
  *    of parent p.  S_tot = M0 * (1 + C).
  *  - Calls are stateless and thread-safe; no C++ exception crosses the ABI.
@@ -91,6 +92,13 @@ int avq_build_tree(const void *children, int H, int M0, int C, int d, int dtype,
 size_t avq_assign_aggregate_workspace_size(int B, int H, int N, int M0, int C, int d);
 
 /*
+ * avq_operand_pack_size -- bytes of the operand pack written by
+ * avq_assign_aggregate and read by avq_attention_fwd (0 if the shape is
+ * invalid).
+ */
+size_t avq_operand_pack_size(int B, int H, int M0, int C, int d, int dtype);
+
+/*
  * avq_assign_aggregate -- stage 1, full-tree assignment and aggregation.
  *   Sec. 4.2: each key goes to its nearest parent among the M0 parents
  *   (Sec. 3.2 argmin of the squared distance; ties -> lowest index); it is
@@ -108,6 +116,10 @@ size_t avq_assign_aggregate_workspace_size(int B, int H, int N, int M0, int C, i
  *   count_out  [B][H][S_tot]  int32   output key counts (every slot written)
  *   leaf_out   [B][H][N]      int32   optional (NULL = not written): slot of
  *                                     each key's leaf (p*, or M0+p*C+c*)
+ *   pack_out   avq_operand_pack_size(...) bytes, 256-byte aligned: the same
+ *              value sums (rounded to dtype) and counts (as fp32) laid out
+ *              as the MFMA operands of avq_attention_fwd; its layout is
+ *              private to the library and only that call reads it.
  *   workspace  device buffer of at least
  *              avq_assign_aggregate_workspace_size(...) bytes, 256-byte
  *              aligned, used only during this call's kernels (it must not
@@ -118,8 +130,8 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents,
                          const void *children, const float *sqnorm,
                          int B, int H, int N, int d, int M0, int C, int dtype,
                          unsigned flags, float *vsum_out, int32_t *count_out,
-                         int32_t *leaf_out, void *workspace, size_t workspace_bytes,
-                         void *stream);
+                         int32_t *leaf_out, void *pack_out, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /*
  * avq_attention_fwd -- stage 2, query-tile adaptive attention.
@@ -142,8 +154,8 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents,
  *   Q          [B][H][N][d]   dtype
  *   parents    [H][M0][d]     dtype   from avq_build_tree
  *   children   [H][M0][C][d]  dtype
- *   vsum       [B][H][S_tot][d] fp32  from avq_assign_aggregate
- *   count      [B][H][S_tot]  int32
+ *   pack       operand pack written by avq_assign_aggregate for these
+ *              B, H, M0, C, d, dtype: the value sums Vbar and counts n
  *   P          0 <= P <= M0 parents refined per tile
  *   tile       queries per tile
  *   scale      finite softmax scale applied to every logit
@@ -152,12 +164,13 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents,
  *              every tile in ascending index order
  *   importance_out [B][H][ceil(N/tile)][M0] fp32, optional: w_j(I)
  *   Requires at least one key per (b, h) (every count row sums to N >= 1).
+ *   Returns AVQ_ERR_UNSUPPORTED if the codebook does not fit the kernel's
+ *   on-chip budget (large fp32 trees).
  */
 int avq_attention_fwd(const void *Q, const void *parents, const void *children,
-                      const float *vsum, const int32_t *count,
-                      int B, int H, int N, int d, int M0, int C, int P, int tile,
-                      float scale, int dtype, void *Y_out, int32_t *sel_out,
-                      float *importance_out, void *stream);
+                      const void *pack, int B, int H, int N, int d, int M0, int C,
+                      int P, int tile, float scale, int dtype, void *Y_out,
+                      int32_t *sel_out, float *importance_out, void *stream);
 
 /*
  * avq_exact_attention_fwd -- exact softmax attention, non-causal

@@ -46,6 +46,15 @@ def test_abi_version_and_status_strings(lib):
     assert lib.avq_status_string(-3) == b"AVQ_ERR_HIP"
 
 
+def test_operand_pack_size(lib):
+    f = lib.avq_operand_pack_size
+    # per (b,h): parent sums [d][256] + counts [256] + child sums [256][d][8] + counts [256][8]
+    per = 64 * 256 * 2 + 256 * 4 + 256 * 64 * 8 * 2 + 256 * 8 * 4
+    assert f(1, 8, 256, 8, 64, 1) == 8 * per
+    assert f(1, 1, 300, 8, 64, 1) == 0
+    assert f(0, 1, 16, 8, 64, 1) == 0
+
+
 def test_workspace_size(lib):
     f = lib.avq_assign_aggregate_workspace_size
     # [B*H*N] int32 key list + [B*H*ceil(N/1024)*(M0+1)] int32 offsets, each 256-aligned
@@ -65,15 +74,17 @@ def test_invalid_arguments_are_rejected_before_launch(lib):
     import adaptive_vector_quantized_avq_amd  # noqa: F401  (sets argtypes)
     p = _fake()
     af = lib.avq_attention_fwd
-    args = dict(Q=p, par=p, ch=p, vs=p, cn=p, B=1, H=1, N=128, d=64, M0=16, C=4, P=4, tile=64,
+    args = dict(Q=p, par=p, ch=p, pk=p, B=1, H=1, N=128, d=64, M0=16, C=4, P=4, tile=64,
                 scale=0.125, dt=1)
 
     def call(**kw):
         a = dict(args, **kw)
-        return af(a["Q"], a["par"], a["ch"], a["vs"], a["cn"], a["B"], a["H"], a["N"], a["d"],
+        return af(a["Q"], a["par"], a["ch"], a["pk"], a["B"], a["H"], a["N"], a["d"],
                   a["M0"], a["C"], a["P"], a["tile"], a["scale"], a["dt"], p, None, None, None)
 
     assert call(Q=None) == -1
+    assert call(pk=None) == -1
+    assert call(tile=16) == -2
     assert call(P=17) == -1
     assert call(P=-1) == -1
     assert call(N=0) == -1
@@ -90,15 +101,18 @@ def test_invalid_arguments_are_rejected_before_launch(lib):
 
     aa = lib.avq_assign_aggregate
     # a valid call template; each case below breaks exactly one argument
-    base = [p, p, p, p, p, 1, 1, 128, 64, 16, 4, 1, 0, p, p, None, p, 1 << 20, None]
+    base = [p, p, p, p, p, 1, 1, 128, 64, 16, 4, 1, 0, p, p, None, p, p, 1 << 20, None]
     bad_flags = list(base)
     bad_flags[12] = 2
     assert aa(*bad_flags) == -1
+    no_pack = list(base)
+    no_pack[16] = None
+    assert aa(*no_pack) == -1
     small_ws = list(base)
-    small_ws[17] = 16
+    small_ws[18] = 16
     assert aa(*small_ws) == -1
     misaligned = list(base)
-    misaligned[16] = ctypes.c_void_p(0x1004)
+    misaligned[17] = ctypes.c_void_p(0x1004)
     assert aa(*misaligned) == -1
     assert lib.avq_build_tree(None, 1, 4, 4, 64, 1, p, p, None) == -1
     assert lib.avq_build_tree(p, 1, 4, 4, 64, 5, p, p, None) == -1

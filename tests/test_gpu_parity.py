@@ -45,9 +45,9 @@ def run_gpu(avq, inp, P, T, force_child=False):
     ch = to_dev(inp.children, inp.dtype)
     K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
     parents, sq = avq.build_tree(ch)
-    vsum, count, leaf = avq.assign_aggregate(K, V, parents, ch, sq, force_child=force_child,
-                                             want_leaf=True)
-    Y, sel, imp = avq.attention_fwd(Q, parents, ch, vsum, count, P, T, inp.scale,
+    vsum, count, leaf, pack = avq.assign_aggregate(K, V, parents, ch, sq, force_child=force_child,
+                                                   want_leaf=True)
+    Y, sel, imp = avq.attention_fwd(Q, parents, ch, pack, P, T, inp.scale,
                                     want_sel=True, want_importance=True)
     torch.cuda.synchronize()
     return dict(parents=tensor_to_f64(parents, inp.dtype), sqnorm=sq.cpu().numpy(),
@@ -117,8 +117,10 @@ def test_workload_full_size_sampled_tiles(avq, name):
 EDGE = [
     # dtype, d, M0, C, P, T, N, force_child
     ("bf16", 64, 1, 4, 1, 64, 1, False),
-    ("bf16", 64, 1, 4, 0, 16, 37, False),
-    ("f32", 64, 5, 2, 3, 16, 300, False),
+    ("bf16", 64, 1, 4, 0, 32, 37, False),
+    ("f32", 64, 5, 2, 3, 32, 300, False),
+    ("bf16", 64, 100, 4, 9, 256, 1300, False),
+    ("bf16", 128, 256, 8, 40, 32, 700, False),
     ("bf16", 64, 17, 8, 17, 32, 777, False),
     ("bf16", 64, 33, 16, 5, 128, 2049, False),
     ("f32", 128, 24, 4, 7, 64, 1500, False),
@@ -139,6 +141,13 @@ def test_edge_shapes(avq, dtype, d, M0, C, P, T, N, force):
 def test_scale_one_and_dyadic_tree(avq):
     inp = synth.generate_dyadic(5, B=2, H=2, N=700, d=64, M0=8, C=4, P=3, T=32)
     inp.scale = 1.0 / 64.0
+    check_all(avq, inp)
+
+
+@pytest.mark.parametrize("scale", [-0.125, 1.0])
+def test_negative_and_unit_scale(avq, scale):
+    inp = synth.generate("vit-b", B=1, H=2, N=1500, M0=40, C=8, P=6, T=64, seed=31)
+    inp.scale = scale
     check_all(avq, inp)
 
 
@@ -182,8 +191,8 @@ def test_constant_values_give_constant_output(avq):
         ch = to_dev(inp.children, "bf16")
         K, V, Q = (to_dev(x, "bf16") for x in (inp.K, inp.V, inp.Q))
         parents, sq = avq.build_tree(ch)
-        vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq)
-        Y, _, _ = avq.attention_fwd(Q, parents, ch, vsum, count, P, 128, inp.scale)
+        _, _, _, pack = avq.assign_aggregate(K, V, parents, ch, sq)
+        Y, _, _ = avq.attention_fwd(Q, parents, ch, pack, P, 128, inp.scale)
         torch.cuda.synchronize()
         assert np.abs(tensor_to_f64(Y, "bf16") - 0.75).max() <= 4e-3
 
@@ -194,13 +203,15 @@ def test_invalid_arguments_raise(avq):
     ch = to_dev(inp.children, "bf16")
     K, V, Q = (to_dev(x, "bf16") for x in (inp.K, inp.V, inp.Q))
     parents, sq = avq.build_tree(ch)
-    vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq)
+    _, _, _, pack = avq.assign_aggregate(K, V, parents, ch, sq)
     with pytest.raises(avq.AvqError, match="INVALID_ARG"):
-        avq.attention_fwd(Q, parents, ch, vsum, count, 9, 128, inp.scale)   # P > M0
+        avq.attention_fwd(Q, parents, ch, pack, 9, 128, inp.scale)   # P > M0
     with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
-        avq.attention_fwd(Q, parents, ch, vsum, count, 2, 48, inp.scale)   # tile 48
+        avq.attention_fwd(Q, parents, ch, pack, 2, 48, inp.scale)   # tile 48
+    with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
+        avq.attention_fwd(Q, parents, ch, pack, 2, 16, inp.scale)   # tile 16
     with pytest.raises(avq.AvqError, match="INVALID_ARG"):
-        avq.attention_fwd(Q, parents, ch, vsum, count, 2, 128, float("nan"))
+        avq.attention_fwd(Q, parents, ch, pack, 2, 128, float("nan"))
     with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
         bad = torch.zeros((1, 8, 4, 96), dtype=torch.bfloat16, device=DEV)
         avq.build_tree(bad)   # d = 96
