@@ -51,9 +51,12 @@ AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0)
 
 // ---------------------------------------------------------------------------
 // kernel 1: nearest parent of every key + per-chunk bucketing by parent
-// grid (nchunks, B*H), 256 threads; each wave takes 64 keys per step.
+// grid (nchunks, B*H), 256 threads; each wave takes 64 keys per step and has
+// the next step's keys in flight while it computes.  NRB = parents padded to a
+// power of two >= 16, in 16-row MFMA blocks (padding rows never win: their
+// norm is +inf).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int NRB>
 __global__ __launch_bounds__(256) void assign_parent_kernel(
     const T *__restrict__ K, const T *__restrict__ parents, const float *__restrict__ sqnorm,
     int H, int N, int M0, int C, int nchunks, int32_t *__restrict__ sorted,
@@ -62,7 +65,8 @@ __global__ __launch_bounds__(256) void assign_parent_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int LDP = D + 8;
     constexpr int KS = D / 32;
-    const int M0p = round16(M0);
+    constexpr int M0p = 16 * NRB;
+    constexpr int kIters = kAssignChunk / 256;
     T *Pm2 = reinterpret_cast<T *>(smem);
     float *pn = reinterpret_cast<float *>(smem + (size_t)M0p * LDP * sizeof(T));
     int *pst = reinterpret_cast<int *>(pn + M0p);      // [kAssignChunk]
@@ -75,30 +79,45 @@ __global__ __launch_bounds__(256) void assign_parent_kernel(
     const int key0 = chunk * kAssignChunk;
     const int S = M0 * (1 + C);
 
-    // stage -2 * parents and the parent norms
+    auto load_keys = [&](int it, Frag<T> (&b)[4][KS]) {
+        const int kw = key0 + it * 256 + wave * 64;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            // keys past the end read the last key (their result is never stored);
+            // the loads stay unconditional so that they can be left in flight
+            const int key = min(kw + 16 * kb + i16, N - 1);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) b[kb][ks] = load_frag(K + (head + key) * D + 32 * ks + 8 * g);
+        }
+    };
+    Frag<T> b[4][KS];
+    load_keys(0, b);   // in flight while the parents are staged
+
+    // stage -2 * parents and the parent norms (all loads issued before the
+    // first store; rows past M0 read the last parent and store zeros)
     const T *Ph = parents + (int64_t)h * M0 * D;
-    for (int e = tid * 8; e < M0p * D; e += 256 * 8) {
-        const int r = e / D, c = e % D;
-        Frag<T> f = r < M0 ? load_frag(Ph + (int64_t)r * D + c) : zero_frag<T>();
-        T *dst = Pm2 + r * LDP + c;
-        store_scaled_frag(dst, f, -2.0f);
+    constexpr int kStage = (M0p * D + 256 * 8 - 1) / (256 * 8);
+    Frag<T> sf[kStage];
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+        const int e = (tid + 256 * k) * 8, r = min(e / D, M0 - 1), c = e % D;
+        sf[k] = load_frag(Ph + (int64_t)r * D + c);
     }
-    for (int r = tid; r < M0p; r += 256) pn[r] = r < M0 ? sqnorm[(int64_t)h * S + r] : INFINITY;
+    float snorm = sqnorm[(int64_t)h * S + min(tid, M0 - 1)];
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+        const int e = (tid + 256 * k) * 8, r = e / D, c = e % D;
+        if (e < M0p * D) store_scaled_frag(Pm2 + r * LDP + c, r < M0 ? sf[k] : zero_frag<T>(), -2.0f);
+    }
+    if (tid < M0p) pn[tid] = tid < M0 ? snorm : INFINITY;
     for (int r = tid; r < 257; r += 256) hist[r] = 0;
     __syncthreads();
 
-    const int nrb = M0p / 16;
-    for (int it = 0; it < kAssignChunk / 256; ++it) {
+    for (int it = 0; it < kIters; ++it) {
         const int kw = key0 + it * 256 + wave * 64;
         if (kw >= N) break;
-        Frag<T> b[4][KS];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int key = kw + 16 * kb + i16;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                b[kb][ks] = key < N ? load_frag(K + (head + key) * D + 32 * ks + 8 * g) : zero_frag<T>();
-        }
+        Frag<T> nb[4][KS];
+        if (it + 1 < kIters) load_keys(it + 1, nb);
         float best[4];
         int bidx[4];
 #pragma unroll
@@ -106,7 +125,8 @@ __global__ __launch_bounds__(256) void assign_parent_kernel(
             best[kb] = INFINITY;
             bidx[kb] = 0;
         }
-        for (int rb = 0; rb < nrb; ++rb) {
+#pragma unroll 2
+        for (int rb = 0; rb < NRB; ++rb) {
             Frag<T> a[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) a[ks] = load_frag(Pm2 + (16 * rb + i16) * LDP + 32 * ks + 8 * g);
@@ -132,6 +152,12 @@ __global__ __launch_bounds__(256) void assign_parent_kernel(
                 const int key = kw + 16 * kb + i16;
                 if (key < N) pst[key - key0] = bidx[kb];
             }
+        }
+        if (it + 1 < kIters) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) b[kb][ks] = nb[kb][ks];
         }
     }
     __syncthreads();
@@ -163,7 +189,7 @@ __global__ __launch_bounds__(256) void assign_parent_kernel(
     }
     __syncthreads();
     int32_t *co = chunk_off + ((int64_t)bh * nchunks + chunk) * (M0 + 1);
-    for (int p = tid; p <= M0; p += 256) co[p] = hist[p];
+    for (int p = tid; p <= M0; p += 256) co[p] = p < M0 ? hist[p] : nk;
     __syncthreads();
     for (int x = tid; x < nk; x += 256) {
         const int p = pst[x];
@@ -173,200 +199,442 @@ __global__ __launch_bounds__(256) void assign_parent_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// kernel 2: child refinement and aggregation for a group of parents
-// grid (ngroups, B*H), 256 threads.
-// LDS rows: child (lp, c) at row lp*C + c, parent lp at row G*C + lp; the
-// slot accumulators use the same numbering (row G*C + lp = keys that stayed
-// at parent lp).
+// kernel 2: child refinement and aggregation for a group of G parents
+// grid (ngroups, B*H), kRefineThreads threads.
+//
+// Distances: the codeword rows of parent lp occupy a block of BR = 16 or 32
+// rows (row j < CC: child j, row CC: the parent itself, the rest padding with
+// norm +inf); one MFMA pass covers the G blocks and each key keeps only the
+// rows of its own parent's block.
+//
+// Aggregation is a product on the matrix cores: for a chunk of 32 keys,
+//   sums[slot][dim] += onehot[slot][key] * V[key][dim],  counts likewise with
+// a column of ones, accumulated in fp32 registers per wave (slot = lp*(CC+1)
+// + j with j = child index, or CC for a key that stayed at its parent).  The
+// one-hot matrix and V are exact in the input type, so every product is exact
+// and only the fp32 summation order differs from a sequential sum.  V rows
+// arrive as 16-byte fragments (8 consecutive dims of one key per lane) and
+// are transposed through a per-wave LDS tile into the operand layout (8
+// consecutive keys of one dim per lane).  (LDS float atomics are avoided:
+// measured on gfx950, a 64-lane ds_add_f32 costs ~80 ns per CU, about 70x a
+// plain LDS read-modify-write.)
+//
+// A wave takes KEYS = 16*KB consecutive list positions per step; list entries
+// are looked up two steps ahead and K/V fragments loaded one step ahead.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void refine_aggregate_kernel(
+constexpr int kRefineThreads = 256;
+
+template <typename T, int D, int CC> struct RefineCfg {
+    static constexpr int G = kRefineGroup;
+    static constexpr int NW = kRefineThreads / 64;
+    static constexpr int BR = CC + 1 <= 16 ? 16 : 32;          // rows per parent block
+    static constexpr int BRB = BR / 16;
+    static constexpr int NRB = G * BRB;                        // distance row blocks
+    static constexpr int NR = G * (CC + 1);                    // slots
+    static constexpr int NSB = (NR + 15) / 16;                 // slot blocks
+    static constexpr int NDB = D / 16;                         // dim blocks
+    static constexpr int KS = D / 32;
+    static constexpr int KB = (sizeof(T) == 2 && D == 64) ? 4 : 2;
+    static constexpr int KEYS = 16 * KB;
+    static constexpr int NCH = KEYS / 32;
+    static constexpr int LDP = D + 8;                          // codeword row stride
+    static constexpr int LDK = KEYS + 16 / (int)sizeof(T) * 2; // transposed-V row stride
+    static constexpr int LDA = D + 1;                          // accumulator row stride
+    static constexpr size_t cw_bytes = (size_t)G * BR * LDP * sizeof(T);
+    static constexpr size_t rn_bytes = (size_t)G * BR * 4;
+    static constexpr size_t vt_bytes = (size_t)NW * (D * LDK * sizeof(T) + KEYS);
+    static constexpr size_t acc_bytes = (size_t)NSB * 16 * (LDA + 1) * 4;
+    static constexpr size_t union_bytes = vt_bytes > acc_bytes ? vt_bytes : acc_bytes;
+    static size_t lds(int nchunks)
+    {
+        return cw_bytes + rn_bytes + ((union_bytes + 15) & ~(size_t)15) + (size_t)(2 * nchunks + 1) * 4;
+    }
+};
+
+// one-hot MFMA operand: element k is 1 if slot byte k of `sl` equals `target`
+template <typename T> __device__ __forceinline__ Frag<T> onehot_frag(unsigned long long sl, int target);
+template <> __device__ __forceinline__ Frag<bf16> onehot_frag<bf16>(unsigned long long sl, int target)
+{
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const unsigned b0 = (unsigned)(sl >> (16 * w)) & 0xFFu, b1 = (unsigned)(sl >> (16 * w + 8)) & 0xFFu;
+        u[w] = ((unsigned)(b0 == (unsigned)target) * 0x3F80u) | ((unsigned)(b1 == (unsigned)target) * 0x3F800000u);
+    }
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x8, u);
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> onehot_frag<float>(unsigned long long sl, int target)
+{
+    Frag<float> f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        f.lo[k] = ((unsigned)(sl >> (8 * k)) & 0xFFu) == (unsigned)target ? 1.f : 0.f;
+        f.hi[k] = ((unsigned)(sl >> (8 * k + 32)) & 0xFFu) == (unsigned)target ? 1.f : 0.f;
+    }
+    return f;
+}
+template <typename T> __device__ __forceinline__ Frag<T> ones_frag();
+template <> __device__ __forceinline__ Frag<bf16> ones_frag<bf16>()
+{
+    Frag<bf16> f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) f.v[k] = (bf16)1.0f;
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> ones_frag<float>()
+{
+    Frag<float> f;
+    f.lo = f32x4{1.f, 1.f, 1.f, 1.f};
+    f.hi = f.lo;
+    return f;
+}
+__device__ __forceinline__ void store_elem(bf16 *p, float x) { *p = (bf16)x; }
+__device__ __forceinline__ void store_elem(float *p, float x) { *p = x; }
+
+template <typename T, int D, int CC>
+__global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
     const T *__restrict__ K, const T *__restrict__ V, const T *__restrict__ parents,
-    const T *__restrict__ children, const float *__restrict__ sqnorm, int H, int N, int M0, int C,
+    const T *__restrict__ children, const float *__restrict__ sqnorm, int H, int N, int M0,
     int nchunks, int force_child, const int32_t *__restrict__ sorted,
     const int32_t *__restrict__ chunk_off, float *__restrict__ vsum, int32_t *__restrict__ count,
     int32_t *__restrict__ leaf, unsigned char *__restrict__ pack)
 {
+    using Cfg = RefineCfg<T, D, CC>;
+    constexpr int G = Cfg::G, NW = Cfg::NW, BR = Cfg::BR, BRB = Cfg::BRB, NRB = Cfg::NRB;
+    constexpr int NR = Cfg::NR, NSB = Cfg::NSB, NDB = Cfg::NDB, KS = Cfg::KS, KB = Cfg::KB;
+    constexpr int KEYS = Cfg::KEYS, NCH = Cfg::NCH, LDP = Cfg::LDP, LDK = Cfg::LDK, LDA = Cfg::LDA;
+    constexpr int NT = kRefineThreads;
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int G = kRefineGroup;
-    constexpr int LDP = D + 8;
-    constexpr int LDA = D + 1;
-    constexpr int KS = D / 32;
-    const int NR = G * (C + 1);            // codeword rows == slots
-    const int RP = round16(NR);
-    T *Cw = reinterpret_cast<T *>(smem);
-    float *rn = reinterpret_cast<float *>(smem + (size_t)RP * LDP * sizeof(T));
-    float *acc = rn + RP;                  // [NR][LDA]
-    int *cnt = reinterpret_cast<int *>(acc + (size_t)NR * LDA);   // [NR]
-    int *pre = cnt + NR;                   // [nchunks + 1]
-    int *segs = pre + nchunks + 1;         // [nchunks]
+    T *Cw = reinterpret_cast<T *>(smem);                                   // [G*BR][LDP]
+    float *rn = reinterpret_cast<float *>(smem + Cfg::cw_bytes);           // [G*BR]
+    unsigned char *un = smem + Cfg::cw_bytes + Cfg::rn_bytes;              // union region
+    int *pre = reinterpret_cast<int *>(un + ((Cfg::union_bytes + 15) & ~(size_t)15));   // [nchunks+1]
+    int *segs = pre + nchunks + 1;                                         // [nchunks]
 
     const int p0 = blockIdx.x * G, bh = blockIdx.y, h = bh % H;
     const int Gv = min(G, M0 - p0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, i16 = lane & 15;
-    const int S = M0 * (1 + C);
+    const int S = M0 * (1 + CC);
     const int64_t head = (int64_t)bh * N;
+    // this wave's transposed-V tile and slot bytes
+    T *VT = reinterpret_cast<T *>(un + (size_t)wave * (D * LDK * sizeof(T) + KEYS));
+    unsigned char *SL = reinterpret_cast<unsigned char *>(VT + D * LDK);
 
-    // stage -2 * codewords, their norms, zero accumulators
-    for (int e = tid * 8; e < RP * D; e += 256 * 8) {
-        const int r = e / D, c = e % D;
-        const T *src = nullptr;
-        if (r < G * C) {
-            const int lp = r / C;
-            if (lp < Gv) src = children + (((int64_t)h * M0 + p0 + lp) * C + (r % C)) * D + c;
-        } else if (r < NR) {
-            const int lp = r - G * C;
-            if (lp < Gv) src = parents + ((int64_t)h * M0 + p0 + lp) * D + c;
+    // ---- stage -2 * codewords (block layout) and norms; bucket sizes
+    constexpr int kRows = G * BR;
+    constexpr int kStage = (kRows * D / 8 + NT - 1) / NT;
+    const T *any_row = children + ((int64_t)h * M0 + p0) * CC * D;
+    Frag<T> sf[kStage];
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+        const int e = (tid + NT * k) * 8, r = e / D, c = e % D, lp = r / BR, j = r % BR;
+        const T *src = any_row;
+        if (e < kRows * D && lp < Gv) {
+            if (j < CC) src = children + (((int64_t)h * M0 + p0 + lp) * CC + j) * D + c;
+            else if (j == CC) src = parents + ((int64_t)h * M0 + p0 + lp) * D + c;
         }
-        Frag<T> f = src ? load_frag(src) : zero_frag<T>();
-        store_scaled_frag(Cw + r * LDP + c, f, -2.0f);
+        sf[k] = load_frag(src);
     }
-    for (int r = tid; r < RP; r += 256) {
-        float v = INFINITY;
-        if (r < G * C) {
-            const int lp = r / C;
-            if (lp < Gv) v = sqnorm[(int64_t)h * S + M0 + (p0 + lp) * C + (r % C)];
-        } else if (r < NR) {
-            const int lp = r - G * C;
-            if (lp < Gv) v = sqnorm[(int64_t)h * S + p0 + lp];
+    float nrm = INFINITY;
+    if (tid < kRows) {
+        const int lp = tid / BR, j = tid % BR;
+        if (lp < Gv) {
+            if (j < CC) nrm = sqnorm[(int64_t)h * S + M0 + (p0 + lp) * CC + j];
+            else if (j == CC) nrm = sqnorm[(int64_t)h * S + p0 + lp];
         }
-        rn[r] = v;
     }
-    for (int e = tid; e < NR * LDA; e += 256) acc[e] = 0.f;
-    for (int e = tid; e < NR; e += 256) cnt[e] = 0;
-    // this group's bucket in every chunk
-    for (int c = tid; c < nchunks; c += 256) {
+    for (int c = tid; c < nchunks; c += NT) {
         const int32_t *co = chunk_off + ((int64_t)bh * nchunks + c) * (M0 + 1);
         const int a = co[p0], b = co[p0 + Gv];
         pre[c] = b - a;
         segs[c] = c * kAssignChunk + a;
     }
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+        const int e = (tid + NT * k) * 8, r = e / D, c = e % D, lp = r / BR, j = r % BR;
+        if (e < kRows * D)
+            store_scaled_frag(Cw + r * LDP + c, (lp < Gv && j <= CC) ? sf[k] : zero_frag<T>(), -2.0f);
+    }
+    if (tid < kRows) rn[tid] = nrm;
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            const int l = pre[c];
-            pre[c] = run;
-            run += l;
+    if (wave == 0) {   // exclusive scan of the bucket sizes
+        int carry = 0;
+        for (int base = 0; base < nchunks; base += 64) {
+            const int c = base + lane;
+            const int v = c < nchunks ? pre[c] : 0;
+            int inc = v;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int t = __shfl_up(inc, off);
+                if (lane >= off) inc += t;
+            }
+            if (c < nchunks) pre[c] = carry + inc - v;
+            carry += __shfl(inc, 63);
         }
-        pre[nchunks] = run;
+        if (lane == 0) pre[nchunks] = carry;
     }
     __syncthreads();
     const int total = pre[nchunks];
-    const int nrb = RP / 16;
 
-    for (int blk = wave; blk * 16 < total; blk += 4) {
-        const int x = blk * 16 + i16;
-        const bool valid = x < total;
-        int key = 0, lp = 0;
-        if (valid) {
-            int lo = 0, hi = nchunks;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (pre[mid] <= x) lo = mid;
-                else hi = mid;
-            }
-            const unsigned e = (unsigned)sorted[head + segs[lo] + (x - pre[lo])];
-            key = (int)(e & 0xFFFFFFu);
-            lp = (int)(e >> 24) - p0;
+    // raw list entry (key | parent << 24) at position x of the group's list;
+    // positions past the end read the last entry (never used)
+    auto entry = [&](int x) -> unsigned {
+        x = min(x, total - 1);
+        int lo = 0, hi = nchunks;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            const bool right = pre[mid] <= x;
+            lo = right ? mid : lo;
+            hi = right ? hi : mid;
         }
-        Frag<T> b[KS];
+        return (unsigned)sorted[head + segs[lo] + (x - pre[lo])];
+    };
+    auto xpos = [&](int s) { return (s * NW + wave) * KEYS; };
+    auto load_kv = [&](unsigned e, Frag<T> (&kf)[KB][KS], Frag<T> (&vf)[KB][KS]) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            b[ks] = valid ? load_frag(K + (head + key) * D + 32 * ks + 8 * g) : zero_frag<T>();
+        for (int kb = 0; kb < KB; ++kb) {
+            const int key = (int)((unsigned)__shfl((int)e, 16 * kb + i16) & 0xFFFFFFu);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                kf[kb][ks] = load_frag(K + (head + key) * D + 32 * ks + 8 * g);
+                vf[kb][ks] = load_frag(V + (head + key) * D + 32 * ks + 8 * g);
+            }
+        }
+    };
 
-        float cbest = INFINITY, pe = INFINITY;
-        int crow = lp * C;
-        for (int rb = 0; rb < nrb; ++rb) {
-            f32x4 a = *reinterpret_cast<const f32x4 *>(rn + 16 * rb + 4 * g);
+    f32x4 sums[NSB][NDB], cnts[NSB];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+        cnts[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) sums[sb][db] = cnts[sb];
+    }
+    const Frag<T> ones = ones_frag<T>();
+
+    auto compute = [&](int s, unsigned e, const Frag<T> (&kf)[KB][KS], const Frag<T> (&vf)[KB][KS]) {
+        const int x0 = xpos(s);
+        int key[KB], lp[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const unsigned ek = (unsigned)__shfl((int)e, 16 * kb + i16);
+            key[kb] = (int)(ek & 0xFFFFFFu);
+            lp[kb] = (int)(ek >> 24) - p0;
+        }
+        // distances to every codeword row; keep the key's own parent block
+        f32x4 own[KB][BRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            Frag<T> a[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) a[ks] = load_frag(Cw + (16 * rb + i16) * LDP + 32 * ks + 8 * g);
+            const f32x4 seed = *reinterpret_cast<const f32x4 *>(rn + 16 * rb + 4 * g);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                f32x4 d = seed;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) d = mma(a[ks], kf[kb][ks], d);
+                const bool mine = rb / BRB == lp[kb];
+                own[kb][rb % BRB] = mine ? d : (rb < BRB ? d : own[kb][rb % BRB]);
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            float cbest = INFINITY, pe = INFINITY;
+            int crow = 0;
+#pragma unroll
+            for (int q = 0; q < BRB; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * q + 4 * g + r;   // row inside the parent block
+                    const float v = own[kb][q][r];
+                    const bool lt = j < CC && v < cbest;
+                    cbest = lt ? v : cbest;
+                    crow = lt ? j : crow;
+                    pe = j == CC ? v : pe;
+                }
+            xgroup_argmin(cbest, crow);
+            pe = xgroup_min(pe);
+            const bool to_child = force_child || cbest < pe;
+            const int j = to_child ? crow : CC;
+            const bool valid = x0 + 16 * kb + i16 < total;
+            if (g == 0) {
+                SL[16 * kb + i16] = valid ? (unsigned char)(lp[kb] * (CC + 1) + j) : (unsigned char)0xFF;
+                if (valid && leaf)
+                    leaf[head + key[kb]] = to_child ? M0 + (p0 + lp[kb]) * CC + crow : p0 + lp[kb];
+            }
+            // transpose this column block's values into VT[dim][key]
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                a = mma(load_frag(Cw + (16 * rb + i16) * LDP + 32 * ks + 8 * g), b[ks], a);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * rb + 4 * g + r;
-                const bool mine = row >= lp * C && row < lp * C + C;
-                const bool lt = mine && a[r] < cbest;
-                cbest = lt ? a[r] : cbest;
-                crow = lt ? row : crow;
-                pe = row == G * C + lp ? a[r] : pe;
+                for (int t = 0; t < 8; ++t)
+                    VT[(32 * ks + 8 * g + t) * LDK + 16 * kb + i16] = from_float<T>(frag_elem(vf[kb][ks], t));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const unsigned long long sl = *reinterpret_cast<const unsigned long long *>(SL + 32 * c + 8 * g);
+            Frag<T> b[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) b[db] = load_frag(VT + (16 * db + i16) * LDK + 32 * c + 8 * g);
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                const Frag<T> oh = onehot_frag<T>(sl, 16 * sb + i16);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) sums[sb][db] = mma(oh, b[db], sums[sb][db]);
+                cnts[sb] = mma(oh, ones, cnts[sb]);
             }
         }
-        xgroup_argmin(cbest, crow);
-        pe = xgroup_min(pe);
-        const bool to_child = force_child || cbest < pe;
-        const int slot = to_child ? crow : G * C + lp;
-        if (valid) {
-            if (leaf && g == 0)
-                leaf[head + key] = to_child ? M0 + (p0 + lp) * C + (crow - lp * C) : p0 + lp;
-            const T *vr = V + (head + key) * D + g * (D / 4);
-            float *ar = acc + slot * LDA + g * (D / 4);
-#pragma unroll
-            for (int t = 0; t < D / 4; t += 8) {
-                const Frag<T> f = load_frag(vr + t);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) atomicAdd(ar + t + k, frag_elem(f, k));
-            }
-            if (g == 0) atomicAdd(&cnt[slot], 1);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    const int nsteps = total > wave * KEYS ? (total - wave * KEYS + NW * KEYS - 1) / (NW * KEYS) : 0;
+    if (nsteps > 0) {
+        Frag<T> kA[KB][KS], vA[KB][KS], kB_[KB][KS], vB_[KB][KS];
+        unsigned e0 = entry(xpos(0) + lane), e1 = entry(xpos(1) + lane);
+        load_kv(e0, kA, vA);
+        for (int s = 0; s < nsteps; s += 2) {
+            const unsigned e2 = entry(xpos(s + 2) + lane);
+            if (s + 1 < nsteps) load_kv(e1, kB_, vB_);
+            compute(s, e0, kA, vA);
+            if (s + 1 >= nsteps) break;
+            const unsigned e3 = entry(xpos(s + 3) + lane);
+            if (s + 2 < nsteps) load_kv(e2, kA, vA);
+            compute(s + 1, e1, kB_, vB_);
+            e0 = e2;
+            e1 = e3;
         }
     }
     __syncthreads();
 
-    // children slots as accumulated; parent slot = stayed + all children
-    float *vs = vsum + (int64_t)bh * S * D;
-    int32_t *cs = count + (int64_t)bh * S;
-    for (int e = tid; e < Gv * C * D; e += 256) {
-        const int lp = e / (C * D), rem = e % (C * D), c = rem / D, t = rem % D;
-        vs[((int64_t)M0 + (p0 + lp) * C + c) * D + t] = acc[(lp * C + c) * LDA + t];
-    }
-    for (int e = tid; e < Gv * D; e += 256) {
-        const int lp = e / D, t = e % D;
-        float s = acc[(G * C + lp) * LDA + t];
-        for (int c = 0; c < C; ++c) s += acc[(lp * C + c) * LDA + t];
-        vs[(int64_t)(p0 + lp) * D + t] = s;
-    }
-    for (int e = tid; e < Gv * C; e += 256) cs[M0 + (p0 + e / C) * C + e % C] = cnt[e];
-    for (int lp = tid; lp < Gv; lp += 256) {
-        int s = cnt[G * C + lp];
-        for (int c = 0; c < C; ++c) s += cnt[lp * C + c];
-        cs[p0 + lp] = s;
+    // ---- sum the waves' partial results into LDS (the V tiles are dead now)
+    float *acc = reinterpret_cast<float *>(un);     // [NSB*16][LDA]
+    float *cntf = acc + NSB * 16 * LDA;             // [NSB*16]
+    for (int w = 0; w < NW; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * sb + 4 * g + r;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        float *pa = acc + row * LDA + 16 * db + i16;
+                        *pa = (w == 0 ? 0.f : *pa) + sums[sb][db][r];
+                    }
+                    if (i16 == 0) cntf[row] = (w == 0 ? 0.f : cntf[row]) + cnts[sb][r];
+                }
+        }
+        __syncthreads();
     }
 
-    // the same aggregates as stage-2 operands (layout in PackLayout)
-    const PackLayout PL = pack_layout(M0, C, D, (int)sizeof(T));
+    // ---- outputs: child slots as accumulated; parent = stayed + children
+    float *vs = vsum + (int64_t)bh * S * D;
+    int32_t *cs = count + (int64_t)bh * S;
+    for (int e = tid; e < Gv * CC * D; e += NT) {
+        const int lp = e / (CC * D), c = (e / D) % CC, t = e % D;
+        vs[((int64_t)M0 + p0 * CC) * D + e] = acc[(lp * (CC + 1) + c) * LDA + t];
+    }
+    for (int e = tid; e < Gv * D; e += NT) {
+        const int lp = e / D, t = e % D;
+        float s = acc[(lp * (CC + 1) + CC) * LDA + t];
+#pragma unroll
+        for (int c = 0; c < CC; ++c) s += acc[(lp * (CC + 1) + c) * LDA + t];
+        vs[(int64_t)(p0 + lp) * D + t] = s;
+    }
+    for (int e = tid; e < Gv * CC; e += NT) cs[M0 + p0 * CC + e] = (int)cntf[(e / CC) * (CC + 1) + e % CC];
+    for (int lp = tid; lp < Gv; lp += NT) {
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c <= CC; ++c) s += cntf[lp * (CC + 1) + c];
+        cs[p0 + lp] = (int)s;
+    }
+
+    // ---- the same aggregates as stage-2 operands (layout in PackLayout)
+    const PackLayout PL = pack_layout(M0, CC, D, (int)sizeof(T));
     const int M0p = padded_parents(M0);
     unsigned char *pk = pack + (size_t)bh * PL.bytes;
     T *pvt = reinterpret_cast<T *>(pk + PL.pvt);
     float *pnp = reinterpret_cast<float *>(pk + PL.pn);
     T *cvt = reinterpret_cast<T *>(pk + PL.cvt);
     float *cnp = reinterpret_cast<float *>(pk + PL.cn);
-    for (int e = tid; e < Gv * D; e += 256) {
-        const int lp = e / D, t = e % D, j = p0 + lp;
-        float s = acc[(G * C + lp) * LDA + t];
-        for (int c = 0; c < C; ++c) s += acc[(lp * C + c) * LDA + t];
-        pvt[(size_t)t * M0p + (j & ~31) + perm32(j & 31)] = from_float<T>(s);
+    for (int e = tid; e < G * D; e += NT) {
+        const int lp = e % G, t = e / G, j = p0 + lp;
+        if (lp >= Gv) continue;
+        float s = acc[(lp * (CC + 1) + CC) * LDA + t];
+#pragma unroll
+        for (int c = 0; c < CC; ++c) s += acc[(lp * (CC + 1) + c) * LDA + t];
+        store_elem(pvt + (size_t)t * M0p + (j & ~31) + perm32(j & 31), s);
     }
-    for (int lp = tid; lp < Gv; lp += 256) {
-        int s = cnt[G * C + lp];
-        for (int c = 0; c < C; ++c) s += cnt[lp * C + c];
-        pnp[p0 + lp] = (float)s;
+    for (int lp = tid; lp < Gv; lp += NT) {
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c <= CC; ++c) s += cntf[lp * (CC + 1) + c];
+        pnp[p0 + lp] = s;
     }
-    for (int e = tid; e < Gv * D * C; e += 256) {
-        const int lp = e / (D * C), rem = e % (D * C), t = rem / C, c = rem % C;
-        cvt[((size_t)(p0 + lp) * D + t) * C + c] = from_float<T>(acc[(lp * C + c) * LDA + t]);
+    for (int e = tid; e < Gv * D * CC; e += NT) {
+        const int lp = e / (D * CC), rem = e % (D * CC), t = rem / CC, c = rem % CC;
+        store_elem(cvt + ((size_t)(p0 + lp) * D + t) * CC + c, acc[(lp * (CC + 1) + c) * LDA + t]);
     }
-    for (int e = tid; e < Gv * C; e += 256) cnp[(size_t)p0 * C + e] = (float)cnt[e];
+    for (int e = tid; e < Gv * CC; e += NT) cnp[(size_t)p0 * CC + e] = cntf[(e / CC) * (CC + 1) + e % CC];
     if (p0 + Gv == M0) {   // padding columns of the parent operands
-        for (int e = tid; e < (M0p - M0) * D; e += 256) {
+        for (int e = tid; e < (M0p - M0) * D; e += NT) {
             const int j = M0 + e / D, t = e % D;
-            pvt[(size_t)t * M0p + (j & ~31) + perm32(j & 31)] = from_float<T>(0.f);
+            store_elem(pvt + (size_t)t * M0p + (j & ~31) + perm32(j & 31), 0.f);
         }
-        for (int j = M0 + tid; j < M0p; j += 256) pnp[j] = 0.f;
+        for (int j = M0 + tid; j < M0p; j += NT) pnp[j] = 0.f;
     }
 }
 
 // ---------------------------------------------------------------------------
+
+template <typename T, int D, int NRB>
+static hipError_t launch_assign(const void *K, const void *parents, const float *sqnorm, int B, int H,
+                                int N, int M0, int C, const AssignWorkspace &ws, hipStream_t stream)
+{
+    const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
+    const size_t lds = (size_t)16 * NRB * (D + 8) * sizeof(T) + (size_t)16 * NRB * 4 +
+                       kAssignChunk * 4 + 257 * 4;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void *)assign_parent_kernel<T, D, NRB>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr = true;
+    }
+    hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(256), lds, stream,
+                       (const T *)K, (const T *)parents, sqnorm, H, N, M0, C, nchunks, ws.sorted,
+                       ws.chunk_off);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int CC>
+static hipError_t launch_refine(const void *K, const void *V, const void *parents,
+                                const void *children, const float *sqnorm, int B, int H, int N,
+                                int M0, unsigned flags, float *vsum, int32_t *count, int32_t *leaf,
+                                void *pack, const AssignWorkspace &ws, hipStream_t stream)
+{
+    const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
+    const size_t lds = RefineCfg<T, D, CC>::lds(nchunks);
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void *)refine_aggregate_kernel<T, D, CC>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr = true;
+    }
+    const int ngroups = (M0 + kRefineGroup - 1) / kRefineGroup;
+    hipLaunchKernelGGL((refine_aggregate_kernel<T, D, CC>), dim3(ngroups, B * H), dim3(kRefineThreads),
+                       lds, stream, (const T *)K, (const T *)V, (const T *)parents,
+                       (const T *)children, sqnorm, H, N, M0, nchunks, (flags & 1u) ? 1 : 0,
+                       ws.sorted, ws.chunk_off, vsum, count, leaf, (unsigned char *)pack);
+    return hipGetLastError();
+}
 
 template <typename T, int D>
 static hipError_t launch_t(const void *K, const void *V, const void *parents, const void *children,
@@ -374,37 +642,23 @@ static hipError_t launch_t(const void *K, const void *V, const void *parents, co
                            float *vsum, int32_t *count, int32_t *leaf, void *pack,
                            const AssignWorkspace &ws, hipStream_t stream)
 {
-    const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
-    const int M0p = round16(M0);
-    const size_t lds1 = (size_t)M0p * (D + 8) * sizeof(T) + (size_t)M0p * 4 + kAssignChunk * 4 + 257 * 4;
-    static bool attr1 = false;
-    if (!attr1) {
-        (void)hipFuncSetAttribute((const void *)assign_parent_kernel<T, D>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr1 = true;
-    }
-    hipLaunchKernelGGL((assign_parent_kernel<T, D>), dim3(nchunks, B * H), dim3(256), lds1, stream,
-                       (const T *)K, (const T *)parents, sqnorm, H, N, M0, C, nchunks, ws.sorted,
-                       ws.chunk_off);
-    hipError_t err = hipGetLastError();
+    const int m = round16(M0);
+    hipError_t err;
+    if (m <= 16) err = launch_assign<T, D, 1>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    else if (m <= 32) err = launch_assign<T, D, 2>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    else if (m <= 64) err = launch_assign<T, D, 4>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    else if (m <= 128) err = launch_assign<T, D, 8>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    else err = launch_assign<T, D, 16>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
     if (err != hipSuccess) return err;
-
-    const int G = kRefineGroup;
-    const int NR = G * (C + 1), RP = round16(NR);
-    const size_t lds2 = (size_t)RP * (D + 8) * sizeof(T) + (size_t)RP * 4 + (size_t)NR * (D + 1) * 4 +
-                        (size_t)NR * 4 + (size_t)(2 * nchunks + 1) * 4;
-    static bool attr2 = false;
-    if (!attr2) {
-        (void)hipFuncSetAttribute((const void *)refine_aggregate_kernel<T, D>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr2 = true;
+#define AVQ_REFINE(CCV) \
+    launch_refine<T, D, CCV>(K, V, parents, children, sqnorm, B, H, N, M0, flags, vsum, count, leaf, pack, ws, stream)
+    switch (C) {
+    case 2: return AVQ_REFINE(2);
+    case 4: return AVQ_REFINE(4);
+    case 8: return AVQ_REFINE(8);
+    default: return AVQ_REFINE(16);
     }
-    const int ngroups = (M0 + G - 1) / G;
-    hipLaunchKernelGGL((refine_aggregate_kernel<T, D>), dim3(ngroups, B * H), dim3(256), lds2, stream,
-                       (const T *)K, (const T *)V, (const T *)parents, (const T *)children, sqnorm, H,
-                       N, M0, C, nchunks, (flags & 1u) ? 1 : 0, ws.sorted, ws.chunk_off, vsum, count,
-                       leaf, (unsigned char *)pack);
-    return hipGetLastError();
+#undef AVQ_REFINE
 }
 
 hipError_t launch_assign_aggregate(const void *K, const void *V, const void *parents,
