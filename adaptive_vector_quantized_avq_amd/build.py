@@ -36,9 +36,18 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 
 
+# per-source extra flags: keep MFMA results in VGPRs (no accumulator-register
+# copies before the VALU reads them) where the kernel's VALU consumes every
+# MFMA result
+EXTRA = {
+    "assign_parent.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
+    extra = EXTRA.get(os.path.basename(src), [])
+    cmd = [_hipcc(), *COMMON, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if r.returncode != 0:

@@ -1,0 +1,238 @@
+// Stage 1, first kernel: nearest parent of every key ("AVQ-Attention",
+// Sec. 4.2; the argmin of Sec. 3.2), and a counting sort of each chunk's keys
+// by parent so that the second kernel (refine_aggregate.hip) can visit the
+// keys of a group of parents.
+//
+// Distances use ||c||^2 - 2 k.c (the ||k||^2 term is common to all
+// candidates): the MFMA accumulator starts at ||c||^2 and the LDS copy of the
+// parents holds -2c (exact in bf16 and fp32).  Ties go to the lowest parent
+// index.
+#include <float.h>
+
+#include "avq_kernels.h"
+
+namespace avq {
+
+size_t assign_workspace_bytes(int B, int H, int N, int M0)
+{
+    const int64_t nchunks = (N + kAssignChunk - 1) / kAssignChunk;
+    size_t a = (size_t)B * H * N * sizeof(int32_t);
+    a = (a + 255) & ~(size_t)255;
+    size_t b = (size_t)B * H * nchunks * (M0 + 1) * sizeof(int32_t);
+    return a + ((b + 255) & ~(size_t)255);
+}
+
+AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0)
+{
+    AssignWorkspace ws;
+    size_t a = (size_t)B * H * N * sizeof(int32_t);
+    a = (a + 255) & ~(size_t)255;
+    ws.sorted = (int32_t *)base;
+    ws.chunk_off = (int32_t *)((char *)base + a);
+    ws.bytes = assign_workspace_bytes(B, H, N, M0);
+    return ws;
+}
+
+// ---------------------------------------------------------------------------
+// kernel 1: nearest parent of every key + per-chunk bucketing by parent
+// grid (nchunks, B*H), 256 threads; each wave takes 64 keys per step and has
+// the next step's keys in flight while it computes.  NRB = parents padded to a
+// power of two >= 16, in 16-row MFMA blocks (padding rows never win: their
+// norm is FLT_MAX).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NRB>
+__global__ __launch_bounds__(256) void assign_parent_kernel(
+    const T *__restrict__ K, const T *__restrict__ parents, const float *__restrict__ sqnorm,
+    int H, int N, int M0, int C, int nchunks, int32_t *__restrict__ sorted,
+    int32_t *__restrict__ chunk_off)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int LDP = D + 8;
+    constexpr int KS = D / 32;
+    constexpr int M0p = 16 * NRB;
+    constexpr int kIters = kAssignChunk / 256;
+    T *Pm2 = reinterpret_cast<T *>(smem);
+    float *pn = reinterpret_cast<float *>(smem + (size_t)M0p * LDP * sizeof(T));
+    int *pst = reinterpret_cast<int *>(pn + M0p);      // [kAssignChunk]
+    int *hist = pst + kAssignChunk;                      // [257]
+
+    const int chunk = blockIdx.x, bh = blockIdx.y, h = bh % H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, i16 = lane & 15;
+    const int64_t head = (int64_t)bh * N;
+    const int key0 = chunk * kAssignChunk;
+    const int S = M0 * (1 + C);
+
+    auto load_keys = [&](int it, Frag<T> (&b)[4][KS]) {
+        const int kw = key0 + it * 256 + wave * 64;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            // keys past the end read the last key (their result is never stored);
+            // the loads stay unconditional so that they can be left in flight
+            const int key = min(kw + 16 * kb + i16, N - 1);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) b[kb][ks] = load_frag(K + (head + key) * D + 32 * ks + 8 * g);
+        }
+    };
+    Frag<T> b[4][KS];
+    load_keys(0, b);   // in flight while the parents are staged
+
+    // stage -2 * parents and the parent norms (all loads issued before the
+    // first store; rows past M0 read the last parent and store zeros)
+    const T *Ph = parents + (int64_t)h * M0 * D;
+    constexpr int kStage = (M0p * D + 256 * 8 - 1) / (256 * 8);
+    Frag<T> sf[kStage];
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+        const int e = (tid + 256 * k) * 8, r = min(e / D, M0 - 1), c = e % D;
+        sf[k] = load_frag(Ph + (int64_t)r * D + c);
+    }
+    float snorm = sqnorm[(int64_t)h * S + min(tid, M0 - 1)];
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+        const int e = (tid + 256 * k) * 8, r = e / D, c = e % D;
+        if (e < M0p * D) store_scaled_frag(Pm2 + r * LDP + c, r < M0 ? sf[k] : zero_frag<T>(), -2.0f);
+    }
+    if (tid < M0p) pn[tid] = tid < M0 ? snorm : FLT_MAX;   // padding rows never win
+    for (int r = tid; r < 257; r += 256) hist[r] = 0;
+    __syncthreads();
+
+    for (int it = 0; it < kIters; ++it) {
+        const int kw = key0 + it * 256 + wave * 64;
+        if (kw >= N) break;
+        Frag<T> nb[4][KS];
+        if (it + 1 < kIters) load_keys(it + 1, nb);
+        // Running minimum per key column.  The row inside the lane's group of
+        // four travels in the two lowest mantissa bits of the compared value
+        // (the comparison keeps 22 of fp32's 24 significand bits), so the
+        // four rows of an MFMA tile reduce with two v_min3 and the block
+        // index is the only thing tracked by a select.
+        float best[4];
+        int brb[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            best[kb] = FLT_MAX;
+            brb[kb] = 0;
+        }
+#pragma unroll 2
+        for (int rb = 0; rb < NRB; ++rb) {
+            Frag<T> a[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) a[ks] = load_frag(Pm2 + (16 * rb + i16) * LDP + 32 * ks + 8 * g);
+            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(pn + 16 * rb + 4 * g);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                f32x4 acc = c0;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) acc = mma(a[ks], b[kb][ks], acc);
+                float q[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) q[r] = __uint_as_float((__float_as_uint(acc[r]) & ~3u) | (unsigned)r);
+                const float m = min3f(min3f(q[0], q[1], q[2]), q[3], best[kb]);
+                brb[kb] = m < best[kb] ? rb : brb[kb];
+                best[kb] = m;
+            }
+        }
+        int bidx[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            bidx[kb] = 16 * brb[kb] + 4 * g + (int)(__float_as_uint(best[kb]) & 3u);
+            xgroup_argmin(best[kb], bidx[kb]);
+        }
+        if (g == 0) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int key = kw + 16 * kb + i16;
+                if (key < N) pst[key - key0] = bidx[kb];
+            }
+        }
+        if (it + 1 < kIters) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) b[kb][ks] = nb[kb][ks];
+        }
+    }
+    __syncthreads();
+
+    // counting sort of the chunk's keys by parent
+    const int nk = min(kAssignChunk, N - key0);
+    for (int x = tid; x < nk; x += 256) atomicAdd(&hist[pst[x]], 1);
+    __syncthreads();
+    if (wave == 0) {
+        int v[4], s = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = hist[4 * lane + k];
+            s += v[k];
+        }
+        int inc = s;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(inc, off);
+            if (lane >= off) inc += t;
+        }
+        int run = inc - s;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            hist[4 * lane + k] = run;
+            run += v[k];
+        }
+        if (lane == 63) hist[256] = nk;
+    }
+    __syncthreads();
+    int32_t *co = chunk_off + ((int64_t)bh * nchunks + chunk) * (M0 + 1);
+    for (int p = tid; p <= M0; p += 256) co[p] = p < M0 ? hist[p] : nk;
+    __syncthreads();
+    for (int x = tid; x < nk; x += 256) {
+        const int p = pst[x];
+        const int pos = atomicAdd(&hist[p], 1);
+        sorted[head + key0 + pos] = (int32_t)((unsigned)(key0 + x) | ((unsigned)p << 24));
+    }
+}
+
+template <typename T, int D, int NRB>
+static hipError_t launch_assign(const void *K, const void *parents, const float *sqnorm, int B, int H,
+                                int N, int M0, int C, const AssignWorkspace &ws, hipStream_t stream)
+{
+    const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
+    const size_t lds = (size_t)16 * NRB * (D + 8) * sizeof(T) + (size_t)16 * NRB * 4 +
+                       kAssignChunk * 4 + 257 * 4;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void *)assign_parent_kernel<T, D, NRB>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr = true;
+    }
+    hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(256), lds, stream,
+                       (const T *)K, (const T *)parents, sqnorm, H, N, M0, C, nchunks, ws.sorted,
+                       ws.chunk_off);
+    return hipGetLastError();
+}
+
+
+template <typename T, int D>
+static hipError_t launch_parent_t(const void *K, const void *parents, const float *sqnorm, int B, int H,
+                                  int N, int M0, int C, const AssignWorkspace &ws, hipStream_t stream)
+{
+    const int m = round16(M0);
+    if (m <= 16) return launch_assign<T, D, 1>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    if (m <= 32) return launch_assign<T, D, 2>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    if (m <= 64) return launch_assign<T, D, 4>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    if (m <= 128) return launch_assign<T, D, 8>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    return launch_assign<T, D, 16>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+}
+
+hipError_t launch_assign_parent(const void *K, const void *parents, const float *sqnorm, int B, int H,
+                                int N, int d, int M0, int C, int dtype, const AssignWorkspace &ws,
+                                hipStream_t stream)
+{
+    if (dtype == 1) {
+        if (d == 64) return launch_parent_t<bf16, 64>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+        return launch_parent_t<bf16, 128>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    }
+    if (d == 64) return launch_parent_t<float, 64>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    return launch_parent_t<float, 128>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+}
+
+}  // namespace avq

@@ -254,9 +254,10 @@ __device__ __forceinline__ void xgroup_argmin(float &v, int &idx)
 {
 #pragma unroll
     for (int m = 16; m <= 32; m <<= 1) {
-        float ov = __shfl_xor(v, m);
-        int oi = __shfl_xor(idx, m);
-        bool take = (ov < v) || (ov == v && oi < idx);
+        const float ov = __shfl_xor(v, m);
+        const int oi = __shfl_xor(idx, m);
+        // bitwise, not short-circuit, so that no branch is emitted
+        const bool take = (ov < v) | ((ov == v) & (oi < idx));
         v = take ? ov : v;
         idx = take ? oi : idx;
     }
@@ -269,6 +270,14 @@ __device__ __forceinline__ float max3f(float a, float b, float c)
 {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// min of three finite floats in one VALU op (no NaN canonicalisation)
+__device__ __forceinline__ float min3f(float a, float b, float c)
+{
+    float r;
+    asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
     return r;
 }
 

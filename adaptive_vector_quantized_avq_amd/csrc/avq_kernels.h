@@ -61,6 +61,11 @@ AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0);
 hipError_t launch_build_tree(const void *children, int H, int M0, int C, int d, int dtype,
                              void *parents, float *sqnorm, hipStream_t stream);
 
+// first stage-1 kernel alone (nearest parent + per-chunk bucketing)
+hipError_t launch_assign_parent(const void *K, const void *parents, const float *sqnorm, int B, int H,
+                                int N, int d, int M0, int C, int dtype, const AssignWorkspace &ws,
+                                hipStream_t stream);
+
 hipError_t launch_assign_aggregate(const void *K, const void *V, const void *parents,
                                    const void *children, const float *sqnorm, int B, int H, int N,
                                    int d, int M0, int C, int dtype, unsigned flags, float *vsum,

@@ -1,205 +1,18 @@
-// Stage 1 of the AVQ-Attention forward pass: full-tree assignment and
-// aggregation ("AVQ-Attention", Sec. 4.2).
-//
-// Every key goes to its nearest parent (Sec. 3.2 argmin), then is compared
-// with that parent's C children only and moves to the nearest child if it is
-// strictly closer than the parent.  Value sums and counts are accumulated at
-// both levels: a parent slot covers its whole cell, a child slot the keys that
-// moved to it.
-//
-// gfx950 design (differs from the single fused pass on the pages, see the
-// design notes): the C children of every parent do not fit in LDS for the
-// large trees (M0*C*d bf16 = 256 KiB at M0=256, C=8, d=64), and gathering a
-// key's 8 children from L2 costs 8x the key's own bytes.  So the work is split
-// in two kernels that each keep their codewords on chip:
-//   1. assign_parent_kernel: K . parents^T on MFMA with the parents in LDS,
-//      argmin per key, then a counting sort of the chunk's keys by parent
-//      (workspace: bucketed key list + per-chunk bucket offsets).
-//   2. refine_aggregate_kernel: one work-group per group of kRefineGroup
-//      parents; their children and the parents sit in LDS, the group's keys
-//      are gathered through the bucket lists, child distances come from MFMA,
-//      and values are summed into LDS slot accumulators that are written out
-//      once (every output slot is written by exactly one work-group, so no
-//      global atomics and no pre-zeroing).
-// Distances use ||c||^2 - 2 k.c (the ||k||^2 term is common to all
-// candidates): the MFMA accumulator starts at ||c||^2 and the LDS copy of the
-// codewords holds -2c (exact in bf16 and fp32).
+// Stage 1, second kernel: child refinement and aggregation ("AVQ-Attention",
+// Sec. 4.2).  Each key, already assigned to its nearest parent by
+// assign_parent.hip, is compared with that parent's C children only and moves
+// to the nearest child (ties -> lowest index) if that child is strictly closer
+// than the parent.  Value sums and counts are accumulated at both levels: a
+// parent slot covers its whole cell, a child slot the keys that moved to it.
+// One work-group owns a group of parents and writes every output slot of
+// those parents exactly once (no global atomics, no pre-zeroing); it also
+// writes the same aggregates as the stage-2 operand pack.
 #include "avq_kernels.h"
 
 namespace avq {
 
-
-size_t assign_workspace_bytes(int B, int H, int N, int M0)
-{
-    const int64_t nchunks = (N + kAssignChunk - 1) / kAssignChunk;
-    size_t a = (size_t)B * H * N * sizeof(int32_t);
-    a = (a + 255) & ~(size_t)255;
-    size_t b = (size_t)B * H * nchunks * (M0 + 1) * sizeof(int32_t);
-    return a + ((b + 255) & ~(size_t)255);
-}
-
-AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0)
-{
-    AssignWorkspace ws;
-    size_t a = (size_t)B * H * N * sizeof(int32_t);
-    a = (a + 255) & ~(size_t)255;
-    ws.sorted = (int32_t *)base;
-    ws.chunk_off = (int32_t *)((char *)base + a);
-    ws.bytes = assign_workspace_bytes(B, H, N, M0);
-    return ws;
-}
-
 // ---------------------------------------------------------------------------
-// kernel 1: nearest parent of every key + per-chunk bucketing by parent
-// grid (nchunks, B*H), 256 threads; each wave takes 64 keys per step and has
-// the next step's keys in flight while it computes.  NRB = parents padded to a
-// power of two >= 16, in 16-row MFMA blocks (padding rows never win: their
-// norm is +inf).
-// ---------------------------------------------------------------------------
-template <typename T, int D, int NRB>
-__global__ __launch_bounds__(256) void assign_parent_kernel(
-    const T *__restrict__ K, const T *__restrict__ parents, const float *__restrict__ sqnorm,
-    int H, int N, int M0, int C, int nchunks, int32_t *__restrict__ sorted,
-    int32_t *__restrict__ chunk_off)
-{
-    extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int LDP = D + 8;
-    constexpr int KS = D / 32;
-    constexpr int M0p = 16 * NRB;
-    constexpr int kIters = kAssignChunk / 256;
-    T *Pm2 = reinterpret_cast<T *>(smem);
-    float *pn = reinterpret_cast<float *>(smem + (size_t)M0p * LDP * sizeof(T));
-    int *pst = reinterpret_cast<int *>(pn + M0p);      // [kAssignChunk]
-    int *hist = pst + kAssignChunk;                      // [257]
-
-    const int chunk = blockIdx.x, bh = blockIdx.y, h = bh % H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, i16 = lane & 15;
-    const int64_t head = (int64_t)bh * N;
-    const int key0 = chunk * kAssignChunk;
-    const int S = M0 * (1 + C);
-
-    auto load_keys = [&](int it, Frag<T> (&b)[4][KS]) {
-        const int kw = key0 + it * 256 + wave * 64;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            // keys past the end read the last key (their result is never stored);
-            // the loads stay unconditional so that they can be left in flight
-            const int key = min(kw + 16 * kb + i16, N - 1);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) b[kb][ks] = load_frag(K + (head + key) * D + 32 * ks + 8 * g);
-        }
-    };
-    Frag<T> b[4][KS];
-    load_keys(0, b);   // in flight while the parents are staged
-
-    // stage -2 * parents and the parent norms (all loads issued before the
-    // first store; rows past M0 read the last parent and store zeros)
-    const T *Ph = parents + (int64_t)h * M0 * D;
-    constexpr int kStage = (M0p * D + 256 * 8 - 1) / (256 * 8);
-    Frag<T> sf[kStage];
-#pragma unroll
-    for (int k = 0; k < kStage; ++k) {
-        const int e = (tid + 256 * k) * 8, r = min(e / D, M0 - 1), c = e % D;
-        sf[k] = load_frag(Ph + (int64_t)r * D + c);
-    }
-    float snorm = sqnorm[(int64_t)h * S + min(tid, M0 - 1)];
-#pragma unroll
-    for (int k = 0; k < kStage; ++k) {
-        const int e = (tid + 256 * k) * 8, r = e / D, c = e % D;
-        if (e < M0p * D) store_scaled_frag(Pm2 + r * LDP + c, r < M0 ? sf[k] : zero_frag<T>(), -2.0f);
-    }
-    if (tid < M0p) pn[tid] = tid < M0 ? snorm : INFINITY;
-    for (int r = tid; r < 257; r += 256) hist[r] = 0;
-    __syncthreads();
-
-    for (int it = 0; it < kIters; ++it) {
-        const int kw = key0 + it * 256 + wave * 64;
-        if (kw >= N) break;
-        Frag<T> nb[4][KS];
-        if (it + 1 < kIters) load_keys(it + 1, nb);
-        float best[4];
-        int bidx[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            best[kb] = INFINITY;
-            bidx[kb] = 0;
-        }
-#pragma unroll 2
-        for (int rb = 0; rb < NRB; ++rb) {
-            Frag<T> a[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) a[ks] = load_frag(Pm2 + (16 * rb + i16) * LDP + 32 * ks + 8 * g);
-            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(pn + 16 * rb + 4 * g);
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                f32x4 acc = c0;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = mma(a[ks], b[kb][ks], acc);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool lt = acc[r] < best[kb];
-                    best[kb] = lt ? acc[r] : best[kb];
-                    bidx[kb] = lt ? 16 * rb + 4 * g + r : bidx[kb];
-                }
-            }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) xgroup_argmin(best[kb], bidx[kb]);
-        if (g == 0) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int key = kw + 16 * kb + i16;
-                if (key < N) pst[key - key0] = bidx[kb];
-            }
-        }
-        if (it + 1 < kIters) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) b[kb][ks] = nb[kb][ks];
-        }
-    }
-    __syncthreads();
-
-    // counting sort of the chunk's keys by parent
-    const int nk = min(kAssignChunk, N - key0);
-    for (int x = tid; x < nk; x += 256) atomicAdd(&hist[pst[x]], 1);
-    __syncthreads();
-    if (wave == 0) {
-        int v[4], s = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[k] = hist[4 * lane + k];
-            s += v[k];
-        }
-        int inc = s;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(inc, off);
-            if (lane >= off) inc += t;
-        }
-        int run = inc - s;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            hist[4 * lane + k] = run;
-            run += v[k];
-        }
-        if (lane == 63) hist[256] = nk;
-    }
-    __syncthreads();
-    int32_t *co = chunk_off + ((int64_t)bh * nchunks + chunk) * (M0 + 1);
-    for (int p = tid; p <= M0; p += 256) co[p] = p < M0 ? hist[p] : nk;
-    __syncthreads();
-    for (int x = tid; x < nk; x += 256) {
-        const int p = pst[x];
-        const int pos = atomicAdd(&hist[p], 1);
-        sorted[head + key0 + pos] = (int32_t)((unsigned)(key0 + x) | ((unsigned)p << 24));
-    }
-}
-
-// ---------------------------------------------------------------------------
-// kernel 2: child refinement and aggregation for a group of G parents
+// child refinement and aggregation for a group of G parents
 // grid (ngroups, B*H), kRefineThreads threads.
 //
 // Distances: the codeword rows of parent lp occupy a block of BR = 16 or 32
@@ -304,7 +117,7 @@ __global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
 {
     using Cfg = RefineCfg<T, D, CC>;
     constexpr int G = Cfg::G, NW = Cfg::NW, BR = Cfg::BR, BRB = Cfg::BRB, NRB = Cfg::NRB;
-    constexpr int NR = Cfg::NR, NSB = Cfg::NSB, NDB = Cfg::NDB, KS = Cfg::KS, KB = Cfg::KB;
+    constexpr int NSB = Cfg::NSB, NDB = Cfg::NDB, KS = Cfg::KS, KB = Cfg::KB;
     constexpr int KEYS = Cfg::KEYS, NCH = Cfg::NCH, LDP = Cfg::LDP, LDK = Cfg::LDK, LDA = Cfg::LDA;
     constexpr int NT = kRefineThreads;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -593,27 +406,6 @@ __global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------
-
-template <typename T, int D, int NRB>
-static hipError_t launch_assign(const void *K, const void *parents, const float *sqnorm, int B, int H,
-                                int N, int M0, int C, const AssignWorkspace &ws, hipStream_t stream)
-{
-    const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
-    const size_t lds = (size_t)16 * NRB * (D + 8) * sizeof(T) + (size_t)16 * NRB * 4 +
-                       kAssignChunk * 4 + 257 * 4;
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute((const void *)assign_parent_kernel<T, D, NRB>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr = true;
-    }
-    hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(256), lds, stream,
-                       (const T *)K, (const T *)parents, sqnorm, H, N, M0, C, nchunks, ws.sorted,
-                       ws.chunk_off);
-    return hipGetLastError();
-}
-
 template <typename T, int D, int CC>
 static hipError_t launch_refine(const void *K, const void *V, const void *parents,
                                 const void *children, const float *sqnorm, int B, int H, int N,
@@ -637,19 +429,11 @@ static hipError_t launch_refine(const void *K, const void *V, const void *parent
 }
 
 template <typename T, int D>
-static hipError_t launch_t(const void *K, const void *V, const void *parents, const void *children,
-                           const float *sqnorm, int B, int H, int N, int M0, int C, unsigned flags,
-                           float *vsum, int32_t *count, int32_t *leaf, void *pack,
-                           const AssignWorkspace &ws, hipStream_t stream)
+static hipError_t launch_refine_t(const void *K, const void *V, const void *parents, const void *children,
+                                  const float *sqnorm, int B, int H, int N, int M0, int C, unsigned flags,
+                                  float *vsum, int32_t *count, int32_t *leaf, void *pack,
+                                  const AssignWorkspace &ws, hipStream_t stream)
 {
-    const int m = round16(M0);
-    hipError_t err;
-    if (m <= 16) err = launch_assign<T, D, 1>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-    else if (m <= 32) err = launch_assign<T, D, 2>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-    else if (m <= 64) err = launch_assign<T, D, 4>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-    else if (m <= 128) err = launch_assign<T, D, 8>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-    else err = launch_assign<T, D, 16>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-    if (err != hipSuccess) return err;
 #define AVQ_REFINE(CCV) \
     launch_refine<T, D, CCV>(K, V, parents, children, sqnorm, B, H, N, M0, flags, vsum, count, leaf, pack, ws, stream)
     switch (C) {
@@ -667,14 +451,16 @@ hipError_t launch_assign_aggregate(const void *K, const void *V, const void *par
                                    int32_t *count, int32_t *leaf, void *pack,
                                    const AssignWorkspace &ws, hipStream_t stream)
 {
+    hipError_t err = launch_assign_parent(K, parents, sqnorm, B, H, N, d, M0, C, dtype, ws, stream);
+    if (err != hipSuccess) return err;
     if (dtype == 1) {
         if (d == 64)
-            return launch_t<bf16, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
-        return launch_t<bf16, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
+            return launch_refine_t<bf16, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
+        return launch_refine_t<bf16, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
     }
     if (d == 64)
-        return launch_t<float, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
-    return launch_t<float, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
+        return launch_refine_t<float, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
+    return launch_refine_t<float, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
 }
 
 }  // namespace avq
