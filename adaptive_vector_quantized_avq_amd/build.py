@@ -41,6 +41,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # MFMA result
 EXTRA = {
     "assign_parent.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "refine_aggregate.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

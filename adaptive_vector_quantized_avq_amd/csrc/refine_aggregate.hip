@@ -33,7 +33,8 @@ namespace avq {
 // plain LDS read-modify-write.)
 //
 // A wave takes KEYS = 16*KB consecutive list positions per step; list entries
-// are looked up two steps ahead and K/V fragments loaded one step ahead.
+// are looked up two steps ahead, and the next step's K and V fragments are
+// loaded into the registers of the current ones as soon as these are consumed.
 // ---------------------------------------------------------------------------
 constexpr int kRefineThreads = 256;
 
@@ -228,7 +229,12 @@ __global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
     }
     const Frag<T> ones = ones_frag<T>();
 
-    auto compute = [&](int s, unsigned e, const Frag<T> (&kf)[KB][KS], const Frag<T> (&vf)[KB][KS]) {
+    // One step: distances from kf, transposed values from vf, aggregation.
+    // kf is reloaded with the keys of entry `en` as soon as the distance
+    // MFMAs have consumed it, vf as soon as it has been transposed, so the
+    // next step's rows are in flight during the rest of this one.
+    auto compute = [&](int s, unsigned e, bool more, unsigned en, Frag<T> (&kf)[KB][KS],
+                       Frag<T> (&vf)[KB][KS]) {
         const int x0 = xpos(s);
         int key[KB], lp[KB];
 #pragma unroll
@@ -253,6 +259,16 @@ __global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
                 const bool mine = rb / BRB == lp[kb];
                 own[kb][rb % BRB] = mine ? d : (rb < BRB ? d : own[kb][rb % BRB]);
             }
+        }
+        int nkey[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) nkey[kb] = (int)((unsigned)__shfl((int)en, 16 * kb + i16) & 0xFFFFFFu);
+        if (more) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kf[kb][ks] = load_frag(K + (head + nkey[kb]) * D + 32 * ks + 8 * g);
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -286,6 +302,13 @@ __global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
                 for (int t = 0; t < 8; ++t)
                     VT[(32 * ks + 8 * g + t) * LDK + 16 * kb + i16] = from_float<T>(frag_elem(vf[kb][ks], t));
         }
+        if (more) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    vf[kb][ks] = load_frag(V + (head + nkey[kb]) * D + 32 * ks + 8 * g);
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -310,19 +333,14 @@ __global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
 
     const int nsteps = total > wave * KEYS ? (total - wave * KEYS + NW * KEYS - 1) / (NW * KEYS) : 0;
     if (nsteps > 0) {
-        Frag<T> kA[KB][KS], vA[KB][KS], kB_[KB][KS], vB_[KB][KS];
+        Frag<T> kf[KB][KS], vf[KB][KS];
         unsigned e0 = entry(xpos(0) + lane), e1 = entry(xpos(1) + lane);
-        load_kv(e0, kA, vA);
-        for (int s = 0; s < nsteps; s += 2) {
-            const unsigned e2 = entry(xpos(s + 2) + lane);
-            if (s + 1 < nsteps) load_kv(e1, kB_, vB_);
-            compute(s, e0, kA, vA);
-            if (s + 1 >= nsteps) break;
-            const unsigned e3 = entry(xpos(s + 3) + lane);
-            if (s + 2 < nsteps) load_kv(e2, kA, vA);
-            compute(s + 1, e1, kB_, vB_);
-            e0 = e2;
-            e1 = e3;
+        load_kv(e0, kf, vf);
+        for (int s = 0; s < nsteps; ++s) {
+            const unsigned e2 = entry(xpos(s + 2) + lane);   // two steps ahead
+            compute(s, e0, s + 1 < nsteps, e1, kf, vf);
+            e0 = e1;
+            e1 = e2;
         }
     }
     __syncthreads();
