@@ -36,12 +36,16 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 
 
-# per-source extra flags: keep MFMA results in VGPRs (no accumulator-register
-# copies before the VALU reads them) where the kernel's VALU consumes every
-# MFMA result
+# per-source extra flags:
+#  -amdgpu-mfma-vgpr-form   keep MFMA results in VGPRs (no accumulator-register
+#                           copies) where the VALU consumes every MFMA result;
+#  -fno-honor-nans          every operand is finite by contract, so fminf /
+#                           fmaxf lower to single v_min3 / v_max3 without NaN
+#                           canonicalisation (the kernels' max3f / min3f)
 EXTRA = {
-    "assign_parent.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "assign_parent.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
     "refine_aggregate.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attention_fwd.hip": ["-fno-honor-nans"],
 }
 
 

@@ -265,20 +265,19 @@ __device__ __forceinline__ void xgroup_argmin(float &v, int &idx)
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
-// max of three finite floats in one VALU op (no NaN canonicalisation)
+// max / min of three floats.  Written with the compiler builtins (not inline
+// asm) so that the compiler's hazard recognizer sees the reads: an inline-asm
+// VALU reading an MFMA result gets no wait states and can read the
+// register's previous contents.  The sources that call these are compiled
+// with -fno-honor-nans, so they lower to single v_max3 / v_min3 without
+// NaN canonicalisation.
 __device__ __forceinline__ float max3f(float a, float b, float c)
 {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
 }
-
-// min of three finite floats in one VALU op (no NaN canonicalisation)
 __device__ __forceinline__ float min3f(float a, float b, float c)
 {
-    float r;
-    asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return __builtin_fminf(a, __builtin_fminf(b, c));
 }
 
 // flip the sign of every element of a fragment

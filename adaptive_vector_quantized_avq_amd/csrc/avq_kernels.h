@@ -29,8 +29,10 @@ struct AssignWorkspace {
 //   pvt [D][M0p]  T      parent value sums, transposed; column of parent j
 //                        at (j & ~31) + perm32(j & 31), zero for j >= M0
 //   pn  [M0p]     float  parent counts (zero for j >= M0)
-//   cvt [M0][D][C] T     child value sums, children innermost
-//   cn  [M0][C]   float  child counts
+//   cvt [M0+1][D][C] T   child value sums, children innermost; entry M0 is
+//                        all zero (read for the padding children of a
+//                        partly filled chunk)
+//   cn  [M0+1][C] float  child counts; entry M0 is all zero
 // with M0p = padded_parents(M0).
 struct PackLayout {
     size_t pvt, pn, cvt, cn, bytes;
@@ -49,8 +51,8 @@ __host__ __device__ inline PackLayout pack_layout(int M0, int C, int D, int esiz
     size_t o = 0;
     L.pvt = o; o = align256(o + (size_t)D * M0p * esize);
     L.pn = o;  o = align256(o + (size_t)M0p * 4);
-    L.cvt = o; o = align256(o + (size_t)M0 * D * C * esize);
-    L.cn = o;  o = align256(o + (size_t)M0 * C * 4);
+    L.cvt = o; o = align256(o + (size_t)(M0 + 1) * D * C * esize);
+    L.cn = o;  o = align256(o + (size_t)(M0 + 1) * C * 4);
     L.bytes = o;
     return L;
 }

@@ -415,12 +415,14 @@ __global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
         store_elem(cvt + ((size_t)(p0 + lp) * D + t) * CC + c, acc[(lp * (CC + 1) + c) * LDA + t]);
     }
     for (int e = tid; e < Gv * CC; e += NT) cnp[(size_t)p0 * CC + e] = cntf[(e / CC) * (CC + 1) + e % CC];
-    if (p0 + Gv == M0) {   // padding columns of the parent operands
+    if (p0 + Gv == M0) {   // padding columns of the parent operands, zero child entry M0
         for (int e = tid; e < (M0p - M0) * D; e += NT) {
             const int j = M0 + e / D, t = e % D;
             store_elem(pvt + (size_t)t * M0p + (j & ~31) + perm32(j & 31), 0.f);
         }
         for (int j = M0 + tid; j < M0p; j += NT) pnp[j] = 0.f;
+        for (int e = tid; e < D * CC; e += NT) store_elem(cvt + (size_t)M0 * D * CC + e, 0.f);
+        for (int e = tid; e < CC; e += NT) cnp[(size_t)M0 * CC + e] = 0.f;
     }
 }
 

@@ -48,8 +48,10 @@ def test_abi_version_and_status_strings(lib):
 
 def test_operand_pack_size(lib):
     f = lib.avq_operand_pack_size
-    # per (b,h): parent sums [d][256] + counts [256] + child sums [256][d][8] + counts [256][8]
-    per = 64 * 256 * 2 + 256 * 4 + 256 * 64 * 8 * 2 + 256 * 8 * 4
+    # per (b,h): parent sums [d][256] + counts [256] + child sums [257][d][8] +
+    # counts [257][8] (one all-zero entry), each section 256-byte aligned
+    al = lambda x: (x + 255) // 256 * 256
+    per = al(64 * 256 * 2) + al(256 * 4) + al(257 * 64 * 8 * 2) + al(257 * 8 * 4)
     assert f(1, 8, 256, 8, 64, 1) == 8 * per
     assert f(1, 1, 300, 8, 64, 1) == 0
     assert f(0, 1, 16, 8, 64, 1) == 0
