@@ -18,7 +18,6 @@ this host's cores.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -49,40 +48,27 @@ def algorithmic(inp, P):
     return dict(s1_bytes=s1_bytes, s1_flops=s1_flops, s2_bytes=s2_bytes, s2_flops=s2_flops)
 
 
-def source_digest(files):
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-KERNEL_SOURCES = {
-    "attention_kernel": ["adaptive_vector_quantized_avq_amd/csrc/attention_fwd.hip",
-                         "adaptive_vector_quantized_avq_amd/csrc/avq_device.h"],
-    "assign_aggregate": ["adaptive_vector_quantized_avq_amd/csrc/assign_aggregate.hip",
-                         "adaptive_vector_quantized_avq_amd/csrc/avq_device.h"],
-}
-
-
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic_<kernel>_<workload>.json), if it was taken on the
+    current kernel source; else None."""
+    from adaptive_vector_quantized_avq_amd import profiling
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        if rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
+        if rec.get("source_digest") != profiling.source_digest(kernel):
             return None
-        return rec.get("bytes_per_launch")
+        return round(rec["bytes_per_launch"])
     except Exception:
         return None
 
 
 def cpu_baseline(inp, P, heads):
-    """The CPU oracle, as it stands, on `heads` (b, h) units of the workload:
-    stage 1 on all their keys, stage 2 on all their query tiles."""
+    """The CPU oracle, as it stands, on the first `heads` heads of batch 0 of
+    the workload: stage 1 on all their keys, stage 2 on all their query
+    tiles."""
     import numpy as np
     import oracle
     import synth
@@ -118,7 +104,8 @@ def main():
     ap.add_argument("--P", type=int, default=None)
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads of batch 0 the CPU oracle runs on (0 = all of them)")
     ap.add_argument("--exact-context", action="store_true",
                     help="also time the in-repo exact softmax attention at the same shape")
     ap.add_argument("--copy-probe", action="store_true",
@@ -217,11 +204,16 @@ def main():
             roof = dict(kernel="attention_kernel", bound="hbm", achieved=round(s2_gbs, 1),
                         peak=HBM_PEAK_GBS, unit="GB/s", frac=round(s2_gbs / HBM_PEAK_GBS, 4))
         roof["traffic"] = measured_traffic("attention_kernel", inp.name)
+        roof["traffic_unit"] = "bytes per launch"
         roof["launch_ms"] = round(s2_ms, 5)
     else:
-        roof = dict(kernel="assign_aggregate", bound="hbm", achieved=round(s1_gbs, 1),
-                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(s1_gbs / HBM_PEAK_GBS, 4),
-                    traffic=measured_traffic("assign_aggregate", inp.name), launch_ms=round(s1_ms, 5))
+        t1 = measured_traffic("assign_parent_kernel", inp.name)
+        t2 = measured_traffic("refine_aggregate_kernel", inp.name)
+        roof = dict(kernel="assign_aggregate (assign_parent_kernel + refine_aggregate_kernel)", bound="hbm",
+                    achieved=round(s1_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(s1_gbs / HBM_PEAK_GBS, 4),
+                    traffic=(t1 + t2) if (t1 is not None and t2 is not None) else None,
+                    traffic_unit="bytes per launch", launch_ms=round(s1_ms, 5))
 
     out = {
         "metric": METRIC,
@@ -284,7 +276,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
-        out["cpu_baseline"] = cpu_baseline(inp, P, max(1, min(args.cpu_heads, B * H)))
+        out["cpu_baseline"] = cpu_baseline(inp, P, max(1, min(args.cpu_heads or H, H)))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
