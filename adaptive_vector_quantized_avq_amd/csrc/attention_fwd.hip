@@ -410,21 +410,21 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                                   (sel_out && w == tw0 && tg < ntiles) ? sel_out + ((size_t)bh * ntiles + tg) * P : nullptr);
         }
 
-        // ---- child correction, up to SCH chunks of 32 children at a time.
-        // A chunk position ph >= P*C (padding of the last chunk) takes the
+        // ---- child correction, SCH chunks of 32 children at a time.
+        // A position ph >= P*C (padding of the last chunks) takes the
         // codeword of child 0 of the first selected parent, whose logit is
         // already among the real ones (so the shift is unchanged), and the
-        // all-zero count and value-sum entry M0 (so it adds nothing).
+        // all-zero count and value-sum entry M0 (so it adds nothing); every
+        // chunk is therefore processed the same way, without guards.
         float dz0 = 0.f, dz1 = 0.f;
         const float sl2c = sl2 * (1.0f / (float)CC);   // mean over CC children, scaled
         for (int c0 = 0; c0 < PC; c0 += 32 * SCH) {
-            const int nch = min(SCH, (PC - c0 + 31) >> 5);
             // codeword fragments: output row 4g+r of tile A is child 8g+r of the
             // chunk, of tile B child 8g+4+r
             Frag<T> ca[SCH][KS], cb[SCH][KS];
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
-                if (q < nch) {
+                {
                     const int phA = c0 + 32 * q + 8 * (i16 >> 2) + (i16 & 3), phB = phA + 4;
                     const int ia = phA < PC ? mysel[phA >> LC] * CC + (phA & (CC - 1)) : mysel[0] * CC;
                     const int ib = phB < PC ? mysel[phB >> LC] * CC + (phB & (CC - 1)) : mysel[0] * CC;
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
             f32x4 nA[SCH], nB[SCH];
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
-                if (q < nch) {
+                {
                     const int ph0 = c0 + 32 * q + 8 * g;
                     if constexpr (CC >= 8) {   // the 8 children share one parent
                         const float *cp = cnp + (ph0 < PC ? mysel[ph0 >> LC] * CC + (ph0 & (CC - 1)) : M0 * CC);
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
             float c0m = -INFINITY, c1m = -INFINITY;
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
-                if (q < nch) {
+                {
                     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, b0 = a0, a1 = a0, b1 = a0;
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
             }
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
-                if (q < nch) {
+                {
                     const int ph0 = c0 + 32 * q + 8 * g;
                     // value-sum operands: lane (g, i) supplies dim 16*db+i of
                     // the chunk's children 8g..8g+7
