@@ -418,65 +418,90 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
         // chunk is therefore processed the same way, without guards.
         float dz0 = 0.f, dz1 = 0.f;
         const float sl2c = sl2 * (1.0f / (float)CC);   // mean over CC children, scaled
-        for (int c0 = 0; c0 < PC; c0 += 32 * SCH) {
-            // codeword fragments: output row 4g+r of tile A is child 8g+r of the
-            // chunk, of tile B child 8g+4+r
-            Frag<T> ca[SCH][KS], cb[SCH][KS];
+        constexpr int SC = 32 * SCH;                    // children per super-chunk
+
+        // codeword fragments of the super-chunk starting at c0: output row
+        // 4g+r of tile A is child 8g+r of a chunk, of tile B child 8g+4+r
+        struct CwBuf {
+            Frag<T> a[SCH][KS], b[SCH][KS];
+        };
+        auto load_cw = [&](int c0, CwBuf &cw) {
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
-                {
-                    const int phA = c0 + 32 * q + 8 * (i16 >> 2) + (i16 & 3), phB = phA + 4;
-                    const int ia = phA < PC ? mysel[phA >> LC] * CC + (phA & (CC - 1)) : mysel[0] * CC;
-                    const int ib = phB < PC ? mysel[phB >> LC] * CC + (phB & (CC - 1)) : mysel[0] * CC;
-                    const T *ra = Ch + (size_t)ia * D + 8 * g;
-                    const T *rb_ = Ch + (size_t)ib * D + 8 * g;
+                const int phA = c0 + 32 * q + 8 * (i16 >> 2) + (i16 & 3), phB = phA + 4;
+                // (indices clamped so that the LDS reads are unconditional)
+                const int sa = mysel[phA < PC ? phA >> LC : 0], sb = mysel[phB < PC ? phB >> LC : 0];
+                const int ia = sa * CC + (phA < PC ? (phA & (CC - 1)) : 0);
+                const int ib = sb * CC + (phB < PC ? (phB & (CC - 1)) : 0);
+                const T *ra = Ch + (size_t)ia * D + 8 * g;
+                const T *rb_ = Ch + (size_t)ib * D + 8 * g;
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        ca[q][ks] = load_frag(ra + 32 * ks);
-                        cb[q][ks] = load_frag(rb_ + 32 * ks);
-                    }
+                for (int ks = 0; ks < KS; ++ks) {
+                    cw.a[q][ks] = load_frag(ra + 32 * ks);
+                    cw.b[q][ks] = load_frag(rb_ + 32 * ks);
                 }
             }
-            // counts of this lane group's 8 children of every chunk
+        };
+        // one super-chunk: its counts and value sums are loaded first (they
+        // are needed last), the next super-chunk's codewords are loaded into
+        // `nxt` while this one computes
+        auto super_chunk = [&](int c0, const CwBuf &cw, CwBuf &nxt, bool more) {
             f32x4 nA[SCH], nB[SCH];
+            Frag<T> vc[SCH][DB];
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
-                {
-                    const int ph0 = c0 + 32 * q + 8 * g;
-                    if constexpr (CC >= 8) {   // the 8 children share one parent
-                        const float *cp = cnp + (ph0 < PC ? mysel[ph0 >> LC] * CC + (ph0 & (CC - 1)) : M0 * CC);
-                        nA[q] = *reinterpret_cast<const f32x4 *>(cp);
-                        nB[q] = *reinterpret_cast<const f32x4 *>(cp + 4);
-                    } else {
+                const int ph0 = c0 + 32 * q + 8 * g;
+                if constexpr (CC >= 8) {   // the 8 children share one parent
+                    const int ps = mysel[ph0 < PC ? ph0 >> LC : 0];
+                    const int pp = ph0 < PC ? ps : M0;
+                    const float *cp = cnp + pp * CC + (ph0 & (CC - 1));
+                    nA[q] = *reinterpret_cast<const f32x4 *>(cp);
+                    nB[q] = *reinterpret_cast<const f32x4 *>(cp + 4);
+                    const T *vp = cvt + ((size_t)pp * D + i16) * CC + (ph0 & (CC - 1));
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int pA = ph0 + r, pB = ph0 + 4 + r;
-                            nA[q][r] = cnp[pA < PC ? mysel[pA >> LC] * CC + (pA & (CC - 1)) : M0 * CC];
-                            nB[q][r] = cnp[pB < PC ? mysel[pB >> LC] * CC + (pB & (CC - 1)) : M0 * CC];
-                        }
+                    for (int db = 0; db < DB; ++db) vc[q][db] = load_frag(vp + (size_t)16 * db * CC);
+                } else {
+                    int pk8[8];   // slot (parent index, or the zero entry M0) of children ph0..ph0+7
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const int ph = ph0 + k;
+                        const int ps = mysel[ph < PC ? ph >> LC : 0];
+                        pk8[k] = ph < PC ? ps : M0;
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        nA[q][r] = cnp[pk8[r] * CC + ((ph0 + r) & (CC - 1))];
+                        nB[q][r] = cnp[pk8[4 + r] * CC + ((ph0 + 4 + r) & (CC - 1))];
+                    }
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        float v[8];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            v[k] = to_float(cvt[((size_t)pk8[k] * D + 16 * db + i16) * CC + ((ph0 + k) & (CC - 1))]);
+                        vc[q][db] = frag_from8<T>(v);
                     }
                 }
             }
+            if (more) load_cw(c0 + SC, nxt);
             // child logits and their maximum
             f32x4 SA0[SCH], SB0[SCH], SA1[SCH], SB1[SCH];
             float c0m = -INFINITY, c1m = -INFINITY;
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
-                {
-                    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, b0 = a0, a1 = a0, b1 = a0;
+                f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, b0 = a0, a1 = a0, b1 = a0;
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        a0 = mma(ca[q][ks], qa[ks], a0);
-                        b0 = mma(cb[q][ks], qa[ks], b0);
-                        a1 = mma(ca[q][ks], qb[ks], a1);
-                        b1 = mma(cb[q][ks], qb[ks], b1);
-                    }
-                    SA0[q] = a0; SB0[q] = b0; SA1[q] = a1; SB1[q] = b1;
-                    c0m = max3f(c0m, max3f(a0[0], a0[1], a0[2]), max3f(a0[3], b0[0], b0[1]));
-                    c0m = max3f(c0m, b0[2], b0[3]);
-                    c1m = max3f(c1m, max3f(a1[0], a1[1], a1[2]), max3f(a1[3], b1[0], b1[1]));
-                    c1m = max3f(c1m, b1[2], b1[3]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    a0 = mma(cw.a[q][ks], qa[ks], a0);
+                    b0 = mma(cw.b[q][ks], qa[ks], b0);
+                    a1 = mma(cw.a[q][ks], qb[ks], a1);
+                    b1 = mma(cw.b[q][ks], qb[ks], b1);
                 }
+                SA0[q] = a0; SB0[q] = b0; SA1[q] = a1; SB1[q] = b1;
+                c0m = max3f(c0m, max3f(a0[0], a0[1], a0[2]), max3f(a0[3], b0[0], b0[1]));
+                c0m = max3f(c0m, b0[2], b0[3]);
+                c1m = max3f(c1m, max3f(a1[0], a1[1], a1[2]), max3f(a1[3], b1[0], b1[1]));
+                c1m = max3f(c1m, b1[2], b1[3]);
             }
             // raise the shift to cover the child logits, rescale X and Z
             {
@@ -490,74 +515,60 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
             }
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
-                {
-                    const int ph0 = c0 + 32 * q + 8 * g;
-                    // value-sum operands: lane (g, i) supplies dim 16*db+i of
-                    // the chunk's children 8g..8g+7
-                    Frag<T> vc[DB];
-                    if constexpr (CC >= 8) {
-                        const T *vp = cvt + ((size_t)(ph0 < PC ? mysel[ph0 >> LC] : M0) * D + i16) * CC + (ph0 & (CC - 1));
-#pragma unroll
-                        for (int db = 0; db < DB; ++db) vc[db] = load_frag(vp + (size_t)16 * db * CC);
-                    } else {
-#pragma unroll
-                        for (int db = 0; db < DB; ++db) {
-                            float v[8];
-#pragma unroll
-                            for (int k = 0; k < 8; ++k) {
-                                const int ph = ph0 + k;
-                                const int pp = ph < PC ? mysel[ph >> LC] : M0;
-                                v[k] = to_float(cvt[((size_t)pp * D + 16 * db + i16) * CC + (ph & (CC - 1))]);
-                            }
-                            vc[db] = frag_from8<T>(v);
-                        }
+                // exp of the recovered parent logit of each child's parent
+                float eA0[2], eB0[2], eA1[2], eB1[2];   // [r >> 1]
+                if constexpr (CC >= 8) {
+                    float u0 = (SA0[q][0] + SA0[q][1]) + (SA0[q][2] + SA0[q][3]) +
+                               ((SB0[q][0] + SB0[q][1]) + (SB0[q][2] + SB0[q][3]));
+                    float u1 = (SA1[q][0] + SA1[q][1]) + (SA1[q][2] + SA1[q][3]) +
+                               ((SB1[q][0] + SB1[q][1]) + (SB1[q][2] + SB1[q][3]));
+                    if constexpr (CC == 16) {
+                        u0 += __shfl_xor(u0, 16);
+                        u1 += __shfl_xor(u1, 16);
                     }
-                    // exp of the recovered parent logit of each child's parent
-                    float eA0[2], eB0[2], eA1[2], eB1[2];   // [r >> 1]
-                    if constexpr (CC >= 8) {
-                        float u0 = (SA0[q][0] + SA0[q][1]) + (SA0[q][2] + SA0[q][3]) +
-                                   ((SB0[q][0] + SB0[q][1]) + (SB0[q][2] + SB0[q][3]));
-                        float u1 = (SA1[q][0] + SA1[q][1]) + (SA1[q][2] + SA1[q][3]) +
-                                   ((SB1[q][0] + SB1[q][1]) + (SB1[q][2] + SB1[q][3]));
-                        if constexpr (CC == 16) {
-                            u0 += __shfl_xor(u0, 16);
-                            u1 += __shfl_xor(u1, 16);
-                        }
-                        const float f0 = __builtin_amdgcn_exp2f(fmaf(u0, sl2c, -m0));
-                        const float f1 = __builtin_amdgcn_exp2f(fmaf(u1, sl2c, -m1));
-                        eA0[0] = eA0[1] = eB0[0] = eB0[1] = f0;
-                        eA1[0] = eA1[1] = eB1[0] = eB1[1] = f1;
-                    } else if constexpr (CC == 4) {
-                        eA0[0] = eA0[1] = __builtin_amdgcn_exp2f(fmaf((SA0[q][0] + SA0[q][1]) + (SA0[q][2] + SA0[q][3]), sl2c, -m0));
-                        eB0[0] = eB0[1] = __builtin_amdgcn_exp2f(fmaf((SB0[q][0] + SB0[q][1]) + (SB0[q][2] + SB0[q][3]), sl2c, -m0));
-                        eA1[0] = eA1[1] = __builtin_amdgcn_exp2f(fmaf((SA1[q][0] + SA1[q][1]) + (SA1[q][2] + SA1[q][3]), sl2c, -m1));
-                        eB1[0] = eB1[1] = __builtin_amdgcn_exp2f(fmaf((SB1[q][0] + SB1[q][1]) + (SB1[q][2] + SB1[q][3]), sl2c, -m1));
-                    } else {   // CC == 2
+                    const float f0 = __builtin_amdgcn_exp2f(fmaf(u0, sl2c, -m0));
+                    const float f1 = __builtin_amdgcn_exp2f(fmaf(u1, sl2c, -m1));
+                    eA0[0] = eA0[1] = eB0[0] = eB0[1] = f0;
+                    eA1[0] = eA1[1] = eB1[0] = eB1[1] = f1;
+                } else if constexpr (CC == 4) {
+                    eA0[0] = eA0[1] = __builtin_amdgcn_exp2f(fmaf((SA0[q][0] + SA0[q][1]) + (SA0[q][2] + SA0[q][3]), sl2c, -m0));
+                    eB0[0] = eB0[1] = __builtin_amdgcn_exp2f(fmaf((SB0[q][0] + SB0[q][1]) + (SB0[q][2] + SB0[q][3]), sl2c, -m0));
+                    eA1[0] = eA1[1] = __builtin_amdgcn_exp2f(fmaf((SA1[q][0] + SA1[q][1]) + (SA1[q][2] + SA1[q][3]), sl2c, -m1));
+                    eB1[0] = eB1[1] = __builtin_amdgcn_exp2f(fmaf((SB1[q][0] + SB1[q][1]) + (SB1[q][2] + SB1[q][3]), sl2c, -m1));
+                } else {   // CC == 2
 #pragma unroll
-                        for (int k = 0; k < 2; ++k) {
-                            eA0[k] = __builtin_amdgcn_exp2f(fmaf(SA0[q][2 * k] + SA0[q][2 * k + 1], sl2c, -m0));
-                            eB0[k] = __builtin_amdgcn_exp2f(fmaf(SB0[q][2 * k] + SB0[q][2 * k + 1], sl2c, -m0));
-                            eA1[k] = __builtin_amdgcn_exp2f(fmaf(SA1[q][2 * k] + SA1[q][2 * k + 1], sl2c, -m1));
-                            eB1[k] = __builtin_amdgcn_exp2f(fmaf(SB1[q][2 * k] + SB1[q][2 * k + 1], sl2c, -m1));
-                        }
-                    }
-                    f32x4 dA0, dB0, dA1, dB1;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        dA0[r] = __builtin_amdgcn_exp2f(fmaf(SA0[q][r], sl2, -m0)) - eA0[r >> 1];
-                        dB0[r] = __builtin_amdgcn_exp2f(fmaf(SB0[q][r], sl2, -m0)) - eB0[r >> 1];
-                        dA1[r] = __builtin_amdgcn_exp2f(fmaf(SA1[q][r], sl2, -m1)) - eA1[r >> 1];
-                        dB1[r] = __builtin_amdgcn_exp2f(fmaf(SB1[q][r], sl2, -m1)) - eB1[r >> 1];
-                        dz0 = fmaf(dA0[r], nA[q][r], fmaf(dB0[r], nB[q][r], dz0));
-                        dz1 = fmaf(dA1[r], nA[q][r], fmaf(dB1[r], nB[q][r], dz1));
-                    }
-                    const Frag<T> b0 = pack_frag<T>(dA0, dB0), b1 = pack_frag<T>(dA1, dB1);
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        X0[db] = mma(vc[db], b0, X0[db]);
-                        X1[db] = mma(vc[db], b1, X1[db]);
+                    for (int k = 0; k < 2; ++k) {
+                        eA0[k] = __builtin_amdgcn_exp2f(fmaf(SA0[q][2 * k] + SA0[q][2 * k + 1], sl2c, -m0));
+                        eB0[k] = __builtin_amdgcn_exp2f(fmaf(SB0[q][2 * k] + SB0[q][2 * k + 1], sl2c, -m0));
+                        eA1[k] = __builtin_amdgcn_exp2f(fmaf(SA1[q][2 * k] + SA1[q][2 * k + 1], sl2c, -m1));
+                        eB1[k] = __builtin_amdgcn_exp2f(fmaf(SB1[q][2 * k] + SB1[q][2 * k + 1], sl2c, -m1));
                     }
                 }
+                f32x4 dA0, dB0, dA1, dB1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    dA0[r] = __builtin_amdgcn_exp2f(fmaf(SA0[q][r], sl2, -m0)) - eA0[r >> 1];
+                    dB0[r] = __builtin_amdgcn_exp2f(fmaf(SB0[q][r], sl2, -m0)) - eB0[r >> 1];
+                    dA1[r] = __builtin_amdgcn_exp2f(fmaf(SA1[q][r], sl2, -m1)) - eA1[r >> 1];
+                    dB1[r] = __builtin_amdgcn_exp2f(fmaf(SB1[q][r], sl2, -m1)) - eB1[r >> 1];
+                    dz0 = fmaf(dA0[r], nA[q][r], fmaf(dB0[r], nB[q][r], dz0));
+                    dz1 = fmaf(dA1[r], nA[q][r], fmaf(dB1[r], nB[q][r], dz1));
+                }
+                const Frag<T> b0 = pack_frag<T>(dA0, dB0), b1 = pack_frag<T>(dA1, dB1);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    X0[db] = mma(vc[q][db], b0, X0[db]);
+                    X1[db] = mma(vc[q][db], b1, X1[db]);
+                }
+            }
+        };
+        if (PC > 0) {
+            CwBuf cwA, cwB;
+            load_cw(0, cwA);
+            for (int c0 = 0; c0 < PC; c0 += 2 * SC) {
+                super_chunk(c0, cwA, cwB, c0 + SC < PC);
+                if (c0 + SC >= PC) break;
+                super_chunk(c0 + SC, cwB, cwA, c0 + 2 * SC < PC);
             }
         }
 
