@@ -35,26 +35,51 @@ AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0)
 
 // ---------------------------------------------------------------------------
 // kernel 1: nearest parent of every key + per-chunk bucketing by parent
-// grid (nchunks, B*H), 256 threads; each wave takes 64 keys per step and has
-// the next step's keys in flight while it computes.  NRB = parents padded to a
+// grid (nchunks, B*H), kAssignThreads threads (8 waves, two work-groups per
+// CU, four waves per SIMD).  Each wave takes 16*KB keys per step; the next
+// step's keys are loaded as soon as the last distance MFMAs have read the
+// current ones.  NRB = parents padded to a
 // power of two >= 16, in 16-row MFMA blocks (padding rows never win: their
 // norm is FLT_MAX).
+//
+// The row-block loop is software pipelined: the MFMAs of block rb+1 are
+// issued before the argmin update of block rb, whose operands were loaded
+// from LDS one block earlier still, so the matrix cores, the VALU and LDS
+// work on three different blocks at a time.
 // ---------------------------------------------------------------------------
+constexpr int kAssignThreads = 512;
+
+template <typename T, int D> constexpr int assign_key_blocks()
+{
+    return (sizeof(T) == 2 && D == 64) ? 4 : 2;   // bounded by the key registers
+}
+// waves per SIMD the register budget is sized for (fp32 with d = 128 needs
+// more than 128 registers for its key and codeword fragments)
+template <typename T, int D> constexpr int assign_waves_per_simd()
+{
+    return (sizeof(T) == 4 && D == 128) ? 2 : 4;
+}
+
 template <typename T, int D, int NRB>
-__global__ __launch_bounds__(256) void assign_parent_kernel(
+__global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(assign_waves_per_simd<T, D>()))) void assign_parent_kernel(
     const T *__restrict__ K, const T *__restrict__ parents, const float *__restrict__ sqnorm,
     int H, int N, int M0, int C, int nchunks, int32_t *__restrict__ sorted,
     int32_t *__restrict__ chunk_off)
 {
     extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int NT = kAssignThreads;
+    constexpr int NWV = NT / 64;
     constexpr int LDP = D + 8;
     constexpr int KS = D / 32;
+    constexpr int KB = assign_key_blocks<T, D>();
+    constexpr int KEYS = 16 * KB;                        // keys per wave per step
     constexpr int M0p = 16 * NRB;
-    constexpr int kIters = kAssignChunk / 256;
+    constexpr int kIters = kAssignChunk / (NWV * KEYS);
+    static_assert(kAssignChunk % (NWV * KEYS) == 0, "chunk must be a whole number of steps");
     T *Pm2 = reinterpret_cast<T *>(smem);
     float *pn = reinterpret_cast<float *>(smem + (size_t)M0p * LDP * sizeof(T));
-    int *pst = reinterpret_cast<int *>(pn + M0p);      // [kAssignChunk]
-    int *hist = pst + kAssignChunk;                      // [257]
+    unsigned char *pst = reinterpret_cast<unsigned char *>(pn + M0p);   // [kAssignChunk]
+    int *hist = reinterpret_cast<int *>(pst + kAssignChunk);           // [257]
 
     const int chunk = blockIdx.x, bh = blockIdx.y, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -63,10 +88,10 @@ __global__ __launch_bounds__(256) void assign_parent_kernel(
     const int key0 = chunk * kAssignChunk;
     const int S = M0 * (1 + C);
 
-    auto load_keys = [&](int it, Frag<T> (&b)[4][KS]) {
-        const int kw = key0 + it * 256 + wave * 64;
+    auto load_keys = [&](int it, Frag<T> (&b)[KB][KS]) {
+        const int kw = key0 + (it * NWV + wave) * KEYS;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             // keys past the end read the last key (their result is never stored);
             // the loads stay unconditional so that they can be left in flight
             const int key = min(kw + 16 * kb + i16, N - 1);
@@ -74,90 +99,123 @@ __global__ __launch_bounds__(256) void assign_parent_kernel(
             for (int ks = 0; ks < KS; ++ks) b[kb][ks] = load_frag(K + (head + key) * D + 32 * ks + 8 * g);
         }
     };
-    Frag<T> b[4][KS];
+    Frag<T> b[KB][KS];
     load_keys(0, b);   // in flight while the parents are staged
 
     // stage -2 * parents and the parent norms (all loads issued before the
     // first store; rows past M0 read the last parent and store zeros)
     const T *Ph = parents + (int64_t)h * M0 * D;
-    constexpr int kStage = (M0p * D + 256 * 8 - 1) / (256 * 8);
+    constexpr int kStage = (M0p * D + NT * 8 - 1) / (NT * 8);
     Frag<T> sf[kStage];
 #pragma unroll
     for (int k = 0; k < kStage; ++k) {
-        const int e = (tid + 256 * k) * 8, r = min(e / D, M0 - 1), c = e % D;
+        const int e = (tid + NT * k) * 8, r = min(e / D, M0 - 1), c = e % D;
         sf[k] = load_frag(Ph + (int64_t)r * D + c);
     }
     float snorm = sqnorm[(int64_t)h * S + min(tid, M0 - 1)];
 #pragma unroll
     for (int k = 0; k < kStage; ++k) {
-        const int e = (tid + 256 * k) * 8, r = e / D, c = e % D;
+        const int e = (tid + NT * k) * 8, r = e / D, c = e % D;
         if (e < M0p * D) store_scaled_frag(Pm2 + r * LDP + c, r < M0 ? sf[k] : zero_frag<T>(), -2.0f);
     }
     if (tid < M0p) pn[tid] = tid < M0 ? snorm : FLT_MAX;   // padding rows never win
-    for (int r = tid; r < 257; r += 256) hist[r] = 0;
+    for (int r = tid; r < 257; r += NT) hist[r] = 0;
     __syncthreads();
 
+    // codeword fragments and norms of row block rb
+    auto load_rows = [&](int rb, Frag<T> (&a)[KS], f32x4 &c0) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[ks] = load_frag(Pm2 + (16 * rb + i16) * LDP + 32 * ks + 8 * g);
+        c0 = *reinterpret_cast<const f32x4 *>(pn + 16 * rb + 4 * g);
+    };
+
+#pragma unroll 1
     for (int it = 0; it < kIters; ++it) {
-        const int kw = key0 + it * 256 + wave * 64;
+        const int kw = key0 + (it * NWV + wave) * KEYS;
         if (kw >= N) break;
-        Frag<T> nb[4][KS];
-        if (it + 1 < kIters) load_keys(it + 1, nb);
         // Running minimum per key column.  The row inside the lane's group of
         // four travels in the two lowest mantissa bits of the compared value
         // (the comparison keeps 22 of fp32's 24 significand bits), so the
         // four rows of an MFMA tile reduce with two v_min3 and the block
         // index is the only thing tracked by a select.
-        float best[4];
-        int brb[4];
+        float best[KB];
+        int brb[KB];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             best[kb] = FLT_MAX;
             brb[kb] = 0;
         }
-#pragma unroll 2
-        for (int rb = 0; rb < NRB; ++rb) {
-            Frag<T> a[KS];
+        Frag<T> a[2][KS];
+        f32x4 c0[2], acc[2][KB];
+        // distances of row block s into acc[s & 1] (operands in buffer s & 1)
+        auto issue = [&](int buf) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) a[ks] = load_frag(Pm2 + (16 * rb + i16) * LDP + 32 * ks + 8 * g);
-            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(pn + 16 * rb + 4 * g);
+            for (int kb = 0; kb < KB; ++kb) {
+                f32x4 t = c0[buf];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                f32x4 acc = c0;
+                for (int ks = 0; ks < KS; ++ks) t = mma(a[buf][ks], b[kb][ks], t);
+                acc[buf][kb] = t;
+            }
+        };
+        auto consume = [&](int rb, int buf) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = mma(a[ks], b[kb][ks], acc);
+            for (int kb = 0; kb < KB; ++kb) {
+                const f32x4 v = acc[buf][kb];
                 float q[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) q[r] = __uint_as_float((__float_as_uint(acc[r]) & ~3u) | (unsigned)r);
+                for (int r = 0; r < 4; ++r) q[r] = __uint_as_float((__float_as_uint(v[r]) & ~3u) | (unsigned)r);
                 const float m = min3f(min3f(q[0], q[1], q[2]), q[3], best[kb]);
                 brb[kb] = m < best[kb] ? rb : brb[kb];
                 best[kb] = m;
             }
+        };
+        const bool more = it + 1 < kIters;
+        load_rows(0, a[0], c0[0]);
+        if constexpr (NRB == 1) {
+            issue(0);
+            // the distance MFMAs have read the keys: load the next step's keys
+            // into the same registers while the last blocks are reduced
+            if (more) load_keys(it + 1, b);
+            consume(0, 0);
+        } else {
+            load_rows(1, a[1], c0[1]);
+            issue(0);
+            // pairs of row blocks (even block in buffer 0, odd in buffer 1);
+            // at block rb the MFMAs of rb+1 are issued and the operands of
+            // rb+2 are read before rb is reduced
+#pragma unroll 1
+            for (int rp = 0; rp < NRB - 2; rp += 2) {
+                issue(1);
+                load_rows(rp + 2, a[0], c0[0]);
+                consume(rp, 0);
+                issue(0);
+                load_rows(rp + 3, a[1], c0[1]);
+                consume(rp + 1, 1);
+            }
+            issue(1);
+            if (more) load_keys(it + 1, b);   // (see above)
+            consume(NRB - 2, 0);
+            consume(NRB - 1, 1);
         }
-        int bidx[4];
+        int bidx[KB];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             bidx[kb] = 16 * brb[kb] + 4 * g + (int)(__float_as_uint(best[kb]) & 3u);
             xgroup_argmin(best[kb], bidx[kb]);
         }
         if (g == 0) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
                 const int key = kw + 16 * kb + i16;
-                if (key < N) pst[key - key0] = bidx[kb];
+                if (key < N) pst[key - key0] = (unsigned char)bidx[kb];
             }
-        }
-        if (it + 1 < kIters) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) b[kb][ks] = nb[kb][ks];
         }
     }
     __syncthreads();
 
     // counting sort of the chunk's keys by parent
     const int nk = min(kAssignChunk, N - key0);
-    for (int x = tid; x < nk; x += 256) atomicAdd(&hist[pst[x]], 1);
+    for (int x = tid; x < nk; x += NT) atomicAdd(&hist[pst[x]], 1);
     __syncthreads();
     if (wave == 0) {
         int v[4], s = 0;
@@ -182,9 +240,9 @@ __global__ __launch_bounds__(256) void assign_parent_kernel(
     }
     __syncthreads();
     int32_t *co = chunk_off + ((int64_t)bh * nchunks + chunk) * (M0 + 1);
-    for (int p = tid; p <= M0; p += 256) co[p] = p < M0 ? hist[p] : nk;
+    for (int p = tid; p <= M0; p += NT) co[p] = p < M0 ? hist[p] : nk;
     __syncthreads();
-    for (int x = tid; x < nk; x += 256) {
+    for (int x = tid; x < nk; x += NT) {
         const int p = pst[x];
         const int pos = atomicAdd(&hist[p], 1);
         sorted[head + key0 + pos] = (int32_t)((unsigned)(key0 + x) | ((unsigned)p << 24));
@@ -197,14 +255,14 @@ static hipError_t launch_assign(const void *K, const void *parents, const float 
 {
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     const size_t lds = (size_t)16 * NRB * (D + 8) * sizeof(T) + (size_t)16 * NRB * 4 +
-                       kAssignChunk * 4 + 257 * 4;
+                       kAssignChunk + 257 * 4;
     static bool attr = false;
     if (!attr) {
         (void)hipFuncSetAttribute((const void *)assign_parent_kernel<T, D, NRB>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr = true;
     }
-    hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(256), lds, stream,
+    hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(kAssignThreads), lds, stream,
                        (const T *)K, (const T *)parents, sqnorm, H, N, M0, C, nchunks, ws.sorted,
                        ws.chunk_off);
     return hipGetLastError();

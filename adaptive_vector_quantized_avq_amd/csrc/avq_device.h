@@ -271,13 +271,15 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 // register's previous contents.  The sources that call these are compiled
 // with -fno-honor-nans, so they lower to single v_max3 / v_min3 without
 // NaN canonicalisation.
+// (Left-nested, so that a chain min3f(min3f(a, b, c), d, e) folds into two
+// instructions.)
 __device__ __forceinline__ float max3f(float a, float b, float c)
 {
-    return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 __device__ __forceinline__ float min3f(float a, float b, float c)
 {
-    return __builtin_fminf(a, __builtin_fminf(b, c));
+    return __builtin_fminf(__builtin_fminf(a, b), c);
 }
 
 // flip the sign of every element of a fragment

@@ -57,7 +57,10 @@ template <typename T, int D, int CC> struct RefineCfg {
     static constexpr size_t cw_bytes = (size_t)G * BR * LDP * sizeof(T);
     static constexpr size_t rn_bytes = (size_t)G * BR * 4;
     static constexpr size_t vt_bytes = (size_t)NW * (D * LDK * sizeof(T) + KEYS);
-    static constexpr size_t acc_bytes = (size_t)NSB * 16 * (LDA + 1) * 4;
+    static constexpr size_t acc1_bytes = (size_t)NSB * 16 * (LDA + 1) * 4;
+    // partial-sum slices summed in parallel (one per wave) when they fit
+    static constexpr int NSL = NW * acc1_bytes + (size_t)G * BR * (LDP * sizeof(T) + 4) <= 96 * 1024 ? NW : 1;
+    static constexpr size_t acc_bytes = NSL * acc1_bytes;
     static constexpr size_t union_bytes = vt_bytes > acc_bytes ? vt_bytes : acc_bytes;
     static size_t lds(int nchunks)
     {
@@ -345,25 +348,55 @@ __global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
     }
     __syncthreads();
 
-    // ---- sum the waves' partial results into LDS (the V tiles are dead now)
-    float *acc = reinterpret_cast<float *>(un);     // [NSB*16][LDA]
-    float *cntf = acc + NSB * 16 * LDA;             // [NSB*16]
-    for (int w = 0; w < NW; ++w) {
-        if (wave == w) {
+    // ---- sum the waves' partial results into LDS (the V tiles are dead now):
+    // every wave writes its own slice and the slices are summed in parallel
+    // when they fit, else the waves add theirs in turn
+    float *acc = reinterpret_cast<float *>(un);     // [NSL][NSB*16][LDA], slice 0 = total
+    constexpr int NSL = Cfg::NSL;
+    float *cntf = acc + NSL * NSB * 16 * LDA;       // [NSL][NSB*16]
+    if constexpr (NSL == NW) {
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb)
+        for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * sb + 4 * g + r;
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * sb + 4 * g + r;
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        float *pa = acc + row * LDA + 16 * db + i16;
-                        *pa = (w == 0 ? 0.f : *pa) + sums[sb][db][r];
-                    }
-                    if (i16 == 0) cntf[row] = (w == 0 ? 0.f : cntf[row]) + cnts[sb][r];
-                }
+                for (int db = 0; db < NDB; ++db) acc[(wave * NSB * 16 + row) * LDA + 16 * db + i16] = sums[sb][db][r];
+                if (i16 == 0) cntf[wave * NSB * 16 + row] = cnts[sb][r];
+            }
+        __syncthreads();
+        for (int e = tid; e < NSB * 16 * D; e += NT) {
+            const int row = e / D, t = e % D;
+            float s = acc[row * LDA + t];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) s += acc[(w * NSB * 16 + row) * LDA + t];
+            acc[row * LDA + t] = s;
+        }
+        for (int e = tid; e < NSB * 16; e += NT) {
+            float s = cntf[e];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) s += cntf[w * NSB * 16 + e];
+            cntf[e] = s;
         }
         __syncthreads();
+    } else {
+        for (int w = 0; w < NW; ++w) {
+            if (wave == w) {
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * sb + 4 * g + r;
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+                            float *pa = acc + row * LDA + 16 * db + i16;
+                            *pa = (w == 0 ? 0.f : *pa) + sums[sb][db][r];
+                        }
+                        if (i16 == 0) cntf[row] = (w == 0 ? 0.f : cntf[row]) + cnts[sb][r];
+                    }
+            }
+            __syncthreads();
+        }
     }
 
     // ---- outputs: child slots as accumulated; parent = stayed + children
