@@ -32,13 +32,14 @@
 //                fp32 bit patterns of w (w >= 0), ties to the lower index
 //                ("Child spawning");
 //   correction   the selected parents' children are read straight from
-//                global memory into MFMA operands, up to 128 children at a
-//                time.  Codeword rows are permuted so that lane group g holds
+//                global memory into MFMA operands, 32 children at a time
+//                (the next 32 in flight).  Codeword rows are permuted so that lane group g holds
 //                8 consecutive children, i.e. whole parents for C >= 8, and
 //                the recovered parent logit (mean of the C child logits,
 //                "Child attention") is an in-lane sum (plus one exchange for
-//                C = 16).  The shift is raised to cover the child logits (X, Z
-//                rescaled) and X^T += Vbar_c^T . dA^T, Z += sum dA n_c with
+//                C = 16).  The shift is raised if a child logit exceeds it
+//                by more than 2^32 (X, Z rescaled) and X^T += Vbar_c^T . dA^T,
+//                Z += sum dA n_c with
 //                dA = exp(S_c - m) - exp(S_p - m);
 //   Y = X / Z.
 #include <type_traits>
@@ -72,6 +73,10 @@ __host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave)
 // Exact top-P of w (w >= 0, M0 <= 256 values, lane l holds w[l + 64 i] in
 // wv[i]) by one wave; ties go to the lower index.  Writes the selected
 // indices in ascending order to selL (and sel_out if not null).
+// The threshold is found by bisection on the bit patterns (monotone in w for
+// w >= 0), from the top bit down; it stops early once exactly P values lie at
+// or above the candidate, which for distinct values happens after a few bits
+// past the first one that separates the P-th and (P+1)-th largest.
 __device__ void select_top_p_regs(const float (&wv)[4], int M0, int P, int *selL, int32_t *sel_out)
 {
     const int lane = lane_id();
@@ -86,7 +91,11 @@ __device__ void select_top_p_regs(const float (&wv)[4], int M0, int P, int *selL
             const unsigned cand = tau | (1u << bit);
             const int cnt = __popcll(__ballot(u[0] >= cand)) + __popcll(__ballot(u[1] >= cand)) +
                             __popcll(__ballot(u[2] >= cand)) + __popcll(__ballot(u[3] >= cand));
-            tau = cnt >= P ? cand : tau;
+            if (cnt == P) {        // exactly P values >= cand: they are the top P
+                tau = cand - 1u;
+                break;
+            }
+            tau = cnt > P ? cand : tau;
         }
     }
     int gt = 0;
@@ -163,11 +172,11 @@ template <> __device__ __forceinline__ void store_row4<float, 8>(float *y, const
     for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4 *>(y + 16 * db) = x[db] * s;
 }
 
-// children of the tile processed together (up to 4 chunks of 32), bounded by
-// the registers their codeword fragments take
+// chunks of 32 children processed together: one (two held the double-buffered
+// codeword fragments in registers the rest of the step needs)
 template <typename T, int D> constexpr int attn_super_chunks()
 {
-    return (D / 32) * (int)sizeof(T) == 4 ? 2 : 1;
+    return 1;
 }
 
 // NRB = number of 16-row parent blocks (padded_parents(M0) / 16).
@@ -504,14 +513,20 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                 c1m = max3f(c1m, b1[2], b1[3]);
             }
             // raise the shift to cover the child logits, rescale X and Z
+            // The shift only has to keep the weights in range: child weights
+            // up to 2^32 above it are harmless in fp32 and bf16, so it is
+            // raised (and X, Z rescaled) only when a child logit exceeds it
+            // by more than that, which takes extreme logit ranges.
             {
                 const float n0 = fmaxf(m0, sl2 * xgroup_max(c0m));
                 const float n1 = fmaxf(m1, sl2 * xgroup_max(c1m));
-                const float a0 = __builtin_amdgcn_exp2f(m0 - n0), a1 = __builtin_amdgcn_exp2f(m1 - n1);
-                m0 = n0; m1 = n1;
-                Zf0 *= a0; dz0 *= a0; Zf1 *= a1; dz1 *= a1;
+                if (__ballot((n0 > m0 + 32.f) | (n1 > m1 + 32.f))) {
+                    const float a0 = __builtin_amdgcn_exp2f(m0 - n0), a1 = __builtin_amdgcn_exp2f(m1 - n1);
+                    m0 = n0; m1 = n1;
+                    Zf0 *= a0; dz0 *= a0; Zf1 *= a1; dz1 *= a1;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) { X0[db] *= a0; X1[db] *= a1; }
+                    for (int db = 0; db < DB; ++db) { X0[db] *= a0; X1[db] *= a1; }
+                }
             }
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {

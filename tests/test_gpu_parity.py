@@ -151,6 +151,26 @@ def test_negative_and_unit_scale(avq, scale):
     check_all(avq, inp)
 
 
+def test_child_logits_far_above_the_shift(avq):
+    # children spread six times wider around their parents than the workload
+    # generator makes them: child logits of selected parents exceed the
+    # parents' maximum logit by more than 32 (log2 units), past which the
+    # kernel raises its softmax shift and rescales X and Z; the importance
+    # values stay well inside fp32's range
+    inp = synth.generate("vit-b", B=1, H=2, N=1500, M0=40, C=8, P=6, T=64, seed=31)
+    ch = inp.f64("children")
+    par = ch.mean(axis=2, keepdims=True)
+    inp.children = synth.to_storage(par + 6.0 * (ch - par), inp.dtype)
+    inp.scale = 0.5
+    Q64, ch64 = inp.f64("Q"), inp.f64("children")
+    par64, _ = oracle.build_tree(ch64, inp.dtype)
+    l2e = inp.scale / np.log(2.0)
+    sp = np.einsum("bhnd,hmd->bhnm", Q64, par64) * l2e
+    sc = np.einsum("bhnd,hmcd->bhnmc", Q64, ch64) * l2e
+    assert (sc.max(axis=(3, 4)) - sp.max(axis=3)).max() > 40.0   # the branch is taken
+    check_all(avq, inp)
+
+
 # ------------------------------------------------------------------ invariants
 
 
