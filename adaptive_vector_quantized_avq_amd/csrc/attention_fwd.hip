@@ -538,8 +538,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                     float u1 = (SA1[q][0] + SA1[q][1]) + (SA1[q][2] + SA1[q][3]) +
                                ((SB1[q][0] + SB1[q][1]) + (SB1[q][2] + SB1[q][3]));
                     if constexpr (CC == 16) {
-                        u0 += __shfl_xor(u0, 16);
-                        u1 += __shfl_xor(u1, 16);
+                        u0 = pair16_sum(u0);
+                        u1 = pair16_sum(u1);
                     }
                     const float f0 = __builtin_amdgcn_exp2f(fmaf(u0, sl2c, -m0));
                     const float f1 = __builtin_amdgcn_exp2f(fmaf(u1, sl2c, -m1));

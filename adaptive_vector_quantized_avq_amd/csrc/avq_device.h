@@ -229,24 +229,65 @@ __device__ __forceinline__ f32x4 row16_reduce_scatter(f32x4 *t, int i16)
     return v;
 }
 
-// across the four lane groups g (lanes i, i+16, i+32, i+48)
+// Across the four lane groups g (lanes i, i+16, i+32, i+48), with gfx950's
+// v_permlane16_swap / v_permlane32_swap (VALU lane exchanges, no LDS round
+// trip).  Called with the same register as both operands, the 16-lane swap
+// returns {rows 0,0,2,2} and {rows 1,1,3,3} of it and the 32-lane swap
+// {rows 0-1,0-1} and {rows 2-3,2-3}, so combining the two halves of each
+// result is symmetric: every lane of a pair gets the same value without a
+// lane-dependent select.
+__device__ __forceinline__ void xswap16(float x, float &a, float &b)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void xswap32(float x, float &a, float &b)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void xswap16(int x, int &a, int &b)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    a = (int)p[0];
+    b = (int)p[1];
+}
+__device__ __forceinline__ void xswap32(int x, int &a, int &b)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    a = (int)p[0];
+    b = (int)p[1];
+}
+
+// sum over rows r and r^1 (lanes i and i^16) of a 16-lane row pair
+__device__ __forceinline__ float pair16_sum(float x)
+{
+    float a, b;
+    xswap16(x, a, b);
+    return a + b;
+}
 __device__ __forceinline__ float xgroup_sum(float x)
 {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    float a, b;
+    xswap16(x, a, b);
+    xswap32(a + b, a, b);
+    return a + b;
 }
 __device__ __forceinline__ float xgroup_max(float x)
 {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+    float a, b;
+    xswap16(x, a, b);
+    xswap32(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
 }
 __device__ __forceinline__ float xgroup_min(float x)
 {
-    x = fminf(x, __shfl_xor(x, 16));
-    x = fminf(x, __shfl_xor(x, 32));
-    return x;
+    float a, b;
+    xswap16(x, a, b);
+    xswap32(fminf(a, b), a, b);
+    return fminf(a, b);
 }
 
 // (value, index) minimum across the lane groups; ties -> smaller index
@@ -254,12 +295,19 @@ __device__ __forceinline__ void xgroup_argmin(float &v, int &idx)
 {
 #pragma unroll
     for (int m = 16; m <= 32; m <<= 1) {
-        const float ov = __shfl_xor(v, m);
-        const int oi = __shfl_xor(idx, m);
+        float v0, v1;
+        int i0, i1;
+        if (m == 16) {
+            xswap16(v, v0, v1);
+            xswap16(idx, i0, i1);
+        } else {
+            xswap32(v, v0, v1);
+            xswap32(idx, i0, i1);
+        }
         // bitwise, not short-circuit, so that no branch is emitted
-        const bool take = (ov < v) | ((ov == v) & (oi < idx));
-        v = take ? ov : v;
-        idx = take ? oi : idx;
+        const bool take = (v1 < v0) | ((v1 == v0) & (i1 < i0));
+        v = take ? v1 : v0;
+        idx = take ? i1 : i0;
     }
 }
 
