@@ -3,7 +3,8 @@
 //
 // Work decomposition (gfx950): persistent work-groups of NWV waves (4, or 8
 // for 256-query tiles); each wave owns 32 queries as two 16-query MFMA column
-// blocks, a work-group step covers NWV*32 queries (whole tiles).  A
+// blocks, a work-group step covers NWV*32 queries (whole tiles).  Barriers
+// per step: one after the importance partials, one after the selection.  A
 // work-group stages its head's parents, their value sums (transposed) and
 // counts in LDS once; LDS holds nothing else but the per-wave importance
 // partials, so two work-groups share a CU and hide each other's barrier and
@@ -24,13 +25,12 @@
 //                E = exp2(scale*log2(e)*s - m'), Z = sum_j E n_j,
 //                X^T = Vbar^T E^T ("Tiled VQ-attention");
 //   importance   w_j = n_j sum_i E_ij / Z_i: reduced over the 16 queries of
-//                each block with DPP, written per wave to LDS (double
-//                buffered, so one barrier per step suffices), summed over
-//                the tile's waves ("Codeword importance");
-//   top-P        every wave of a tile selects the tile's P parents itself
-//                (identical inputs, identical result): exact bisection on the
-//                fp32 bit patterns of w (w >= 0), ties to the lower index
-//                ("Child spawning");
+//                each block with DPP, written per wave to LDS (alternating
+//                between two buffers from step to step), summed over the
+//                tile's waves ("Codeword importance");
+//   top-P        the first wave of each tile selects the tile's P parents
+//                into LDS: exact bisection on the fp32 bit patterns of w
+//                (w >= 0), ties to the lower index ("Child spawning");
 //   correction   the selected parents' children are read straight from
 //                global memory into MFMA operands, 32 children at a time
 //                (the next 32 in flight).  Codeword rows are permuted so that lane group g holds
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
 
     const int wpt = (1 << ltile) / kQPW;         // waves per tile
     const int tw0 = (w / wpt) * wpt;             // first wave of this wave's tile
-    int *mysel = selS + w * selStride;           // this wave's copy of its tile's selection
+    int *mysel = selS + (w / wpt) * selStride;   // the tile's selection
     const int PC = P * CC;
 
     int buf = 0;
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
             }
         }
         float Zf0 = xgroup_sum(z0), Zf1 = xgroup_sum(z1);
-        const float r0 = v0 ? 1.0f / Zf0 : 0.f, r1 = v1 ? 1.0f / Zf1 : 0.f;
+        const float r0 = v0 ? __builtin_amdgcn_rcpf(Zf0) : 0.f, r1 = v1 ? __builtin_amdgcn_rcpf(Zf1) : 0.f;
 
         // ---- E as MFMA operands; the fp32 copy becomes the importance terms
         // t = E0 / Z0 + E1 / Z1 (this wave's two queries of every lane)
@@ -392,22 +392,26 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
         }
         __syncthreads();       // every wave's importance partials are in Wp[buf]
 
-        // ---- tile importance and top-P (each wave of the tile, same result)
+        // ---- tile importance and top-P, by the first wave of each tile (the
+        // tile's other waves wait at the barrier below)
         const int tg = ((st * STEP) >> ltile) + (w / wpt);   // global tile index
-        if (P > 0 || imp_out) {
-            const float *wb = Wp + (buf * NWV + tw0) * M0p;
+        if ((P > 0 || imp_out) && w == tw0) {
+            // sum of the tile's wave partials (all NWV slots are read, those of
+            // other tiles are masked out, so the loop has no branches)
+            const float *wb = Wp + buf * NWV * M0p;
             float wv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int j = lane + 64 * i;
+                const int j = lane + 64 * i, jc = j < M0p ? j : 0;
                 float a = 0.f;
-                if (j < M0) {
-                    for (int ww = 0; ww < wpt; ++ww) a += wb[ww * M0p + j];
-                    a *= nP[j];
+#pragma unroll
+                for (int ww = 0; ww < NWV; ++ww) {
+                    const float x = wb[((tw0 + ww) & (NWV - 1)) * M0p + jc];
+                    a += ww < wpt ? x : 0.f;
                 }
-                wv[i] = a;
+                wv[i] = j < M0 ? a * nP[jc] : 0.f;
             }
-            if (imp_out && w == tw0 && tg < ntiles) {
+            if (imp_out && tg < ntiles) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int j = lane + 64 * i;
@@ -416,8 +420,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
             }
             if (P > 0)
                 select_top_p_regs(wv, M0, P, mysel,
-                                  (sel_out && w == tw0 && tg < ntiles) ? sel_out + ((size_t)bh * ntiles + tg) * P : nullptr);
+                                  (sel_out && tg < ntiles) ? sel_out + ((size_t)bh * ntiles + tg) * P : nullptr);
         }
+        if (P > 0 && wpt > 1) __syncthreads();   // the selection is in LDS
 
         // ---- child correction, SCH chunks of 32 children at a time.
         // A position ph >= P*C (padding of the last chunks) takes the
@@ -589,8 +594,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
 
         // ---- Y = X / Z: lane (g, i) holds dims 16*db + 4g .. +3 of its query
         const float Z0 = Zf0 + xgroup_sum(dz0), Z1 = Zf1 + xgroup_sum(dz1);
-        if (v0) store_row4<T, DB>(Yh + (size_t)q0 * D + 4 * g, X0, 1.0f / Z0);
-        if (v1) store_row4<T, DB>(Yh + (size_t)q1 * D + 4 * g, X1, 1.0f / Z1);
+        if (v0) store_row4<T, DB>(Yh + (size_t)q0 * D + 4 * g, X0, __builtin_amdgcn_rcpf(Z0));
+        if (v1) store_row4<T, DB>(Yh + (size_t)q1 * D + 4 * g, X1, __builtin_amdgcn_rcpf(Z1));
     }
 }
 
