@@ -5,8 +5,12 @@
 //
 // Distances use ||c||^2 - 2 k.c (the ||k||^2 term is common to all
 // candidates): the MFMA accumulator starts at ||c||^2 and the LDS copy of the
-// parents holds -2c (exact in bf16 and fp32).  Ties go to the lowest parent
-// index.
+// parents holds -2c (exact in bf16 and fp32).  Candidates are compared on 22
+// of fp32's 24 significand bits; ties go to the lowest row block, and inside
+// a lane's group of four rows to the lower row when the compared value is
+// non-negative and to the higher one when it is negative (it is ||c||^2 -
+// 2 k.c, not the full distance).  Such ties lie far below the comparison
+// protocol's near-tie bound, under which either parent is accepted.
 #include <float.h>
 
 #include "avq_kernels.h"
