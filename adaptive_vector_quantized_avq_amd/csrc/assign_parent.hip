@@ -1,7 +1,9 @@
 // Stage 1, first kernel: nearest parent of every key ("AVQ-Attention",
 // Sec. 4.2; the argmin of Sec. 3.2), and a counting sort of each chunk's keys
 // by parent so that the second kernel (refine_aggregate.hip) can visit the
-// keys of a group of parents.
+// keys of a group of parents; each group's segment of every chunk's list is
+// recorded group-major, so that the second kernel reads its table in one
+// contiguous piece.
 //
 // Distances use ||c||^2 - 2 k.c (the ||k||^2 term is common to all
 // candidates): the MFMA accumulator starts at ||c||^2 and the LDS copy of the
@@ -20,9 +22,10 @@ namespace avq {
 size_t assign_workspace_bytes(int B, int H, int N, int M0)
 {
     const int64_t nchunks = (N + kAssignChunk - 1) / kAssignChunk;
+    const int64_t ngroups = (M0 + kRefineGroup - 1) / kRefineGroup;
     size_t a = (size_t)B * H * N * sizeof(int32_t);
     a = (a + 255) & ~(size_t)255;
-    size_t b = (size_t)B * H * nchunks * (M0 + 1) * sizeof(int32_t);
+    size_t b = (size_t)B * H * ngroups * nchunks * sizeof(int2);
     return a + ((b + 255) & ~(size_t)255);
 }
 
@@ -32,7 +35,7 @@ AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0)
     size_t a = (size_t)B * H * N * sizeof(int32_t);
     a = (a + 255) & ~(size_t)255;
     ws.sorted = (int32_t *)base;
-    ws.chunk_off = (int32_t *)((char *)base + a);
+    ws.seg = (int2 *)((char *)base + a);
     ws.bytes = assign_workspace_bytes(B, H, N, M0);
     return ws;
 }
@@ -68,7 +71,7 @@ template <typename T, int D, int NRB>
 __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(assign_waves_per_simd<T, D>()))) void assign_parent_kernel(
     const T *__restrict__ K, const T *__restrict__ parents, const float *__restrict__ sqnorm,
     int H, int N, int M0, int C, int nchunks, int32_t *__restrict__ sorted,
-    int32_t *__restrict__ chunk_off)
+    int2 *__restrict__ seg)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NT = kAssignThreads;
@@ -243,8 +246,13 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
         if (lane == 63) hist[256] = nk;
     }
     __syncthreads();
-    int32_t *co = chunk_off + ((int64_t)bh * nchunks + chunk) * (M0 + 1);
-    for (int p = tid; p <= M0; p += NT) co[p] = p < M0 ? hist[p] : nk;
+    // each refinement group's segment of this chunk's list (hist[p] for
+    // p >= M0 equals nk: those parents have no keys)
+    const int ngroups = (M0 + kRefineGroup - 1) / kRefineGroup;
+    for (int gr = tid; gr < ngroups; gr += NT) {
+        const int a = hist[gr * kRefineGroup], b = hist[min((gr + 1) * kRefineGroup, M0)];
+        seg[((int64_t)bh * ngroups + gr) * nchunks + chunk] = int2{a, b - a};
+    }
     __syncthreads();
     for (int x = tid; x < nk; x += NT) {
         const int p = pst[x];
@@ -268,7 +276,7 @@ static hipError_t launch_assign(const void *K, const void *parents, const float 
     }
     hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(kAssignThreads), lds, stream,
                        (const T *)K, (const T *)parents, sqnorm, H, N, M0, C, nchunks, ws.sorted,
-                       ws.chunk_off);
+                       ws.seg);
     return hipGetLastError();
 }
 

@@ -18,8 +18,9 @@ constexpr int kAssignChunk = 1024;
 constexpr int kRefineGroup = 4;
 
 struct AssignWorkspace {
-    int32_t *sorted;      // [B*H][N]            key index | parent << 24, bucketed per chunk
-    int32_t *chunk_off;   // [B*H][nchunks][M0+1] bucket starts inside each chunk
+    int32_t *sorted;      // [B*H][N]  key index | parent << 24, bucketed per chunk
+    int2 *seg;            // [B*H][ceil(M0/kRefineGroup)][nchunks] {start, length} of
+                          // each refinement group's keys inside each chunk's list
     size_t bytes;
 };
 

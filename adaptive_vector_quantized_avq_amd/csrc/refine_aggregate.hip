@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
     const T *__restrict__ K, const T *__restrict__ V, const T *__restrict__ parents,
     const T *__restrict__ children, const float *__restrict__ sqnorm, int H, int N, int M0,
     int nchunks, int force_child, const int32_t *__restrict__ sorted,
-    const int32_t *__restrict__ chunk_off, float *__restrict__ vsum, int32_t *__restrict__ count,
+    const int2 *__restrict__ seg, float *__restrict__ vsum, int32_t *__restrict__ count,
     int32_t *__restrict__ leaf, unsigned char *__restrict__ pack)
 {
     using Cfg = RefineCfg<T, D, CC>;
@@ -165,10 +165,9 @@ __global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
         }
     }
     for (int c = tid; c < nchunks; c += NT) {
-        const int32_t *co = chunk_off + ((int64_t)bh * nchunks + c) * (M0 + 1);
-        const int a = co[p0], b = co[p0 + Gv];
-        pre[c] = b - a;
-        segs[c] = c * kAssignChunk + a;
+        const int2 sg = seg[((int64_t)bh * gridDim.x + blockIdx.x) * nchunks + c];
+        pre[c] = sg.y;
+        segs[c] = c * kAssignChunk + sg.x;
     }
 #pragma unroll
     for (int k = 0; k < kStage; ++k) {
@@ -477,7 +476,7 @@ static hipError_t launch_refine(const void *K, const void *V, const void *parent
     hipLaunchKernelGGL((refine_aggregate_kernel<T, D, CC>), dim3(ngroups, B * H), dim3(kRefineThreads),
                        lds, stream, (const T *)K, (const T *)V, (const T *)parents,
                        (const T *)children, sqnorm, H, N, M0, nchunks, (flags & 1u) ? 1 : 0,
-                       ws.sorted, ws.chunk_off, vsum, count, leaf, (unsigned char *)pack);
+                       ws.sorted, ws.seg, vsum, count, leaf, (unsigned char *)pack);
     return hipGetLastError();
 }
 

@@ -59,8 +59,9 @@ def test_operand_pack_size(lib):
 
 def test_workspace_size(lib):
     f = lib.avq_assign_aggregate_workspace_size
-    # [B*H*N] int32 key list + [B*H*ceil(N/1024)*(M0+1)] int32 offsets, each 256-aligned
-    assert f(1, 8, 65536, 256, 8, 64) == 8 * 65536 * 4 + ((8 * 64 * 257 * 4 + 255) // 256) * 256
+    # [B*H*N] int32 key list + [B*H][ceil(M0/4) groups][ceil(N/1024) chunks] int2
+    # segments, each 256-aligned
+    assert f(1, 8, 65536, 256, 8, 64) == 8 * 65536 * 4 + ((8 * 64 * 64 * 8 + 255) // 256) * 256
     assert f(1, 1, 1, 1, 4, 64) > 0
     assert f(1, 1, 1, 300, 4, 64) == 0      # M0 > 256 unsupported
     assert f(1, 1, 1, 8, 3, 64) == 0        # C = 3 unsupported
