@@ -19,24 +19,25 @@
 
 namespace avq {
 
-size_t assign_workspace_bytes(int B, int H, int N, int M0)
+size_t assign_workspace_bytes(int B, int H, int N, int M0, int C, int D)
 {
     const int64_t nchunks = (N + kAssignChunk - 1) / kAssignChunk;
-    const int64_t ngroups = (M0 + kRefineGroup - 1) / kRefineGroup;
+    const int group = refine_group(C, D);
+    const int64_t ngroups = (M0 + group - 1) / group;
     size_t a = (size_t)B * H * N * sizeof(int32_t);
     a = (a + 255) & ~(size_t)255;
     size_t b = (size_t)B * H * ngroups * nchunks * sizeof(int2);
     return a + ((b + 255) & ~(size_t)255);
 }
 
-AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0)
+AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0, int C, int D)
 {
     AssignWorkspace ws;
     size_t a = (size_t)B * H * N * sizeof(int32_t);
     a = (a + 255) & ~(size_t)255;
     ws.sorted = (int32_t *)base;
     ws.seg = (int2 *)((char *)base + a);
-    ws.bytes = assign_workspace_bytes(B, H, N, M0);
+    ws.bytes = assign_workspace_bytes(B, H, N, M0, C, D);
     return ws;
 }
 
@@ -248,9 +249,10 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
     // each refinement group's segment of this chunk's list (hist[p] for
     // p >= M0 equals nk: those parents have no keys)
-    const int ngroups = (M0 + kRefineGroup - 1) / kRefineGroup;
+    const int group = refine_group(C, D);
+    const int ngroups = (M0 + group - 1) / group;
     for (int gr = tid; gr < ngroups; gr += NT) {
-        const int a = hist[gr * kRefineGroup], b = hist[min((gr + 1) * kRefineGroup, M0)];
+        const int a = hist[gr * group], b = hist[min((gr + 1) * group, M0)];
         seg[((int64_t)bh * ngroups + gr) * nchunks + chunk] = int2{a, b - a};
     }
     __syncthreads();

@@ -90,7 +90,7 @@ int avq_build_tree(const void *children, int H, int M0, int C, int d, int dtype,
 size_t avq_assign_aggregate_workspace_size(int B, int H, int N, int M0, int C, int d)
 {
     if (check_tree(H, M0, C, d, AVQ_BF16) != AVQ_OK || check_seq(B, N) != AVQ_OK) return 0;
-    return avq::assign_workspace_bytes(B, H, N, M0);
+    return avq::assign_workspace_bytes(B, H, N, M0, C, d);
 }
 
 size_t avq_operand_pack_size(int B, int H, int M0, int C, int d, int dtype)
@@ -111,10 +111,10 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents, cons
     if (st != AVQ_OK) return st;
     st = check_seq(B, N);
     if (st != AVQ_OK) return st;
-    const size_t need = avq::assign_workspace_bytes(B, H, N, M0);
+    const size_t need = avq::assign_workspace_bytes(B, H, N, M0, C, d);
     AVQ_REQUIRE(workspace_bytes >= need, AVQ_ERR_INVALID_ARG, "workspace too small");
     AVQ_REQUIRE(((uintptr_t)workspace & 255u) == 0, AVQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    const avq::AssignWorkspace ws = avq::carve_assign_workspace(workspace, B, H, N, M0);
+    const avq::AssignWorkspace ws = avq::carve_assign_workspace(workspace, B, H, N, M0, C, d);
     return hip_status(avq::launch_assign_aggregate(K, V, parents, children, sqnorm, B, H, N, d, M0, C,
                                                    dtype, flags, vsum_out, count_out, leaf_out,
                                                    pack_out, ws, (hipStream_t)stream));

@@ -14,12 +14,17 @@ namespace avq {
 // keys per chunk of the parent-assignment kernel; a chunk's keys are
 // bucketed by parent in the workspace
 constexpr int kAssignChunk = 1024;
-// parents per work-group of the child-refinement / aggregation kernel
-constexpr int kRefineGroup = 4;
+// parents per work-group of the child-refinement / aggregation kernel: 4,
+// or 2 for C = 16 at d = 128 (four such parents make 68 slots, whose fp32
+// accumulators would hold the kernel to one wave per SIMD)
+__host__ __device__ constexpr int refine_group(int C, int D)
+{
+    return C == 16 && D == 128 ? 2 : 4;
+}
 
 struct AssignWorkspace {
     int32_t *sorted;      // [B*H][N]  key index | parent << 24, bucketed per chunk
-    int2 *seg;            // [B*H][ceil(M0/kRefineGroup)][nchunks] {start, length} of
+    int2 *seg;            // [B*H][ceil(M0/refine_group)][nchunks] {start, length} of
                           // each refinement group's keys inside each chunk's list
     size_t bytes;
 };
@@ -58,8 +63,8 @@ __host__ __device__ inline PackLayout pack_layout(int M0, int C, int D, int esiz
     return L;
 }
 
-size_t assign_workspace_bytes(int B, int H, int N, int M0);
-AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0);
+size_t assign_workspace_bytes(int B, int H, int N, int M0, int C, int D);
+AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0, int C, int D);
 
 hipError_t launch_build_tree(const void *children, int H, int M0, int C, int d, int dtype,
                              void *parents, float *sqnorm, hipStream_t stream);

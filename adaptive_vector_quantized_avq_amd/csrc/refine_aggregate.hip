@@ -39,7 +39,7 @@ namespace avq {
 constexpr int kRefineThreads = 256;
 
 template <typename T, int D, int CC> struct RefineCfg {
-    static constexpr int G = kRefineGroup;
+    static constexpr int G = refine_group(CC, D);
     static constexpr int NW = kRefineThreads / 64;
     static constexpr int BR = CC + 1 <= 16 ? 16 : 32;          // rows per parent block
     static constexpr int BRB = BR / 16;
@@ -111,8 +111,17 @@ template <> __device__ __forceinline__ Frag<float> ones_frag<float>()
 __device__ __forceinline__ void store_elem(bf16 *p, float x) { *p = (bf16)x; }
 __device__ __forceinline__ void store_elem(float *p, float x) { *p = x; }
 
+// waves per SIMD the register allocation is held to (1: no limit beyond the
+// hardware's).  bf16 at d = 128 with C >= 8 lands a few registers past two
+// waves without it.
+template <typename T, int D, int CC> constexpr int refine_waves_per_simd()
+{
+    return sizeof(T) == 2 && D == 128 && CC >= 8 ? 2 : 1;
+}
+
 template <typename T, int D, int CC>
-__global__ __launch_bounds__(kRefineThreads) void refine_aggregate_kernel(
+__global__ __launch_bounds__(kRefineThreads) __attribute__((amdgpu_waves_per_eu(refine_waves_per_simd<T, D, CC>())))
+void refine_aggregate_kernel(
     const T *__restrict__ K, const T *__restrict__ V, const T *__restrict__ parents,
     const T *__restrict__ children, const float *__restrict__ sqnorm, int H, int N, int M0,
     int nchunks, int force_child, const int32_t *__restrict__ sorted,
@@ -472,7 +481,7 @@ static hipError_t launch_refine(const void *K, const void *V, const void *parent
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr = true;
     }
-    const int ngroups = (M0 + kRefineGroup - 1) / kRefineGroup;
+    const int ngroups = (M0 + RefineCfg<T, D, CC>::G - 1) / RefineCfg<T, D, CC>::G;
     hipLaunchKernelGGL((refine_aggregate_kernel<T, D, CC>), dim3(ngroups, B * H), dim3(kRefineThreads),
                        lds, stream, (const T *)K, (const T *)V, (const T *)parents,
                        (const T *)children, sqnorm, H, N, M0, nchunks, (flags & 1u) ? 1 : 0,

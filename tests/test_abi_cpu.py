@@ -59,9 +59,11 @@ def test_operand_pack_size(lib):
 
 def test_workspace_size(lib):
     f = lib.avq_assign_aggregate_workspace_size
-    # [B*H*N] int32 key list + [B*H][ceil(M0/4) groups][ceil(N/1024) chunks] int2
-    # segments, each 256-aligned
+    # [B*H*N] int32 key list + [B*H][ceil(M0/group) groups][ceil(N/1024) chunks]
+    # int2 segments, each 256-aligned; groups of 4 parents, of 2 for C = 16 at
+    # d = 128
     assert f(1, 8, 65536, 256, 8, 64) == 8 * 65536 * 4 + ((8 * 64 * 64 * 8 + 255) // 256) * 256
+    assert f(2, 10, 32768, 256, 16, 128) == 20 * 32768 * 4 + ((20 * 128 * 32 * 8 + 255) // 256) * 256
     assert f(1, 1, 1, 1, 4, 64) > 0
     assert f(1, 1, 1, 300, 4, 64) == 0      # M0 > 256 unsupported
     assert f(1, 1, 1, 8, 3, 64) == 0        # C = 3 unsupported
