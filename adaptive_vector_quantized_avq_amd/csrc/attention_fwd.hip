@@ -1,15 +1,18 @@
 // Stage 2 of the AVQ-Attention forward pass: query-tile adaptive attention
 // ("AVQ-Attention", Sec. 4.3).
 //
-// Work decomposition (gfx950): persistent work-groups of NWV waves (whole
-// tiles, at least 4 waves); each wave owns 16*QB queries as QB 16-query MFMA
-// column blocks (QB = 2, see attn_qb), a work-group step covers NWV*16*QB
-// queries.  Barriers
+// Work decomposition (gfx950): persistent work-groups of NWV waves (4; 8 for
+// 256-query tiles and for bf16 at d = 128); each wave owns 32 queries as two
+// 16-query MFMA column blocks (each codeword fragment read feeds two MFMAs;
+// one block per wave, at twice the operand traffic per MFMA, measured ~1.6x
+// slower), a work-group step covers NWV*32 queries (whole tiles).  Barriers
 // per step: one after the importance partials, one after the selection.  A
 // work-group stages its head's parents, their value sums (transposed) and
 // counts in LDS once; LDS holds nothing else but the per-wave importance
 // partials, so two work-groups share a CU and hide each other's barrier and
-// load stalls.  Work-groups are assigned to (head, query slice) so that
+// load stalls (at d = 128 the value sums no longer fit beside a second
+// work-group's parents: bf16 keeps them in LDS with one 8-wave work-group
+// per CU, fp32 reads them from L2).  Work-groups are assigned to (head, query slice) so that
 // consecutive work-group ids, which the dispatcher spreads over the 8 XCDs,
 // give every XCD a contiguous range of heads: a head's children and value
 // sums then live in one XCD's L2.
@@ -26,8 +29,9 @@
 //                E = exp2(scale*log2(e)*s - m'), Z = sum_j E n_j,
 //                X^T = Vbar^T E^T ("Tiled VQ-attention");
 //   importance   w_j = n_j sum_i E_ij / Z_i: reduced over the 16 queries of
-//                each block with DPP, written per wave to LDS, summed over
-//                the tile's waves ("Codeword importance");
+//                each block with DPP, written per wave to LDS (alternating
+//                between two buffers from step to step), summed over the
+//                tile's waves ("Codeword importance");
 //   top-P        the first wave of each tile selects the tile's P parents
 //                into LDS: exact bisection on the fp32 bit patterns of w
 //                (w >= 0), ties to the lower index ("Child spawning");
@@ -49,14 +53,14 @@
 namespace avq {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQPW = 32;   // queries per wave
 
 struct AttnLds {
     size_t ps, vt, np, wp, sel, total;
 };
 
-// nwave waves per work-group, ntile query tiles per work-group step
 template <typename T, int D, bool VT_LDS>
-__host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave, int ntile)
+__host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave)
 {
     const int M0p = padded_parents(M0);
     AttnLds L;
@@ -64,8 +68,8 @@ __host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave, int ntile)
     L.ps = o;  o += (size_t)M0p * (D + 8) * sizeof(T);
     L.vt = o;  if (VT_LDS) o += (size_t)D * (M0p + 8) * sizeof(T);
     L.np = o;  o += (size_t)M0p * 4;
-    L.wp = o;  o += (size_t)nwave * M0p * 4;
-    L.sel = o; o += (size_t)ntile * ((P + 3) & ~3) * 4;
+    L.wp = o;  o += (size_t)2 * nwave * M0p * 4;
+    L.sel = o; o += (size_t)nwave * ((P + 3) & ~3) * 4;
     L.total = o;
     return L;
 }
@@ -179,28 +183,11 @@ template <typename T, int D> constexpr int attn_super_chunks()
     return 1;
 }
 
-// 16-query MFMA column blocks per wave.  With two, each codeword and
-// value-sum fragment read from LDS or L2 feeds two MFMAs.  One block per wave
-// halves the registers a lane holds (4 waves per SIMD at d = 64), but the
-// doubled operand traffic per MFMA made stage 2 ~1.6x slower at both d = 64
-// and d = 128 (measured), so every shape uses two.
-template <typename T, int D> constexpr int attn_qb()
-{
-    return 2;
-}
-// waves per SIMD the register allocation is held to
-template <typename T, int D, int QB> constexpr int attn_waves_per_simd()
-{
-    return 2;
-}
-
-// NRB = number of 16-row parent blocks (padded_parents(M0) / 16); QB =
-// 16-query column blocks per wave.
+// NRB = number of 16-row parent blocks (padded_parents(M0) / 16).
 // sl2 = |scale| * log2(e); neg != 0 flips the sign of Q (scale < 0), so the
 // softmax shift is always a maximum.
-template <typename T, int D, bool VT_LDS, int NRB, int CC, int NWV, int QB>
-__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(attn_waves_per_simd<T, D, QB>())))
-void attention_kernel(
+template <typename T, int D, bool VT_LDS, int NRB, int CC, int NWV>
+__global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const T *__restrict__ Q, const T *__restrict__ parents, const T *__restrict__ children,
     const unsigned char *__restrict__ pack, int H, int N, int M0, int P, int ltile, float sl2,
     int neg, int ntiles, int nsteps, int per_bh, int nbh, T *__restrict__ Y,
@@ -212,13 +199,11 @@ void attention_kernel(
     constexpr int LDP = D + 8;
     constexpr int M0p = 16 * NRB;
     constexpr int LDV = M0p + 8;
-    constexpr int QPW = 16 * QB;   // queries per wave
-    constexpr int STEP = NWV * QPW;
+    constexpr int STEP = NWV * kQPW;
     constexpr int LC = CC == 2 ? 1 : CC == 4 ? 2 : CC == 8 ? 3 : 4;
     constexpr int SCH = attn_super_chunks<T, D>();
     const int selStride = (P + 3) & ~3;
-    const int wpt = (1 << ltile) / QPW;          // waves per tile
-    const AttnLds L = attn_lds<T, D, VT_LDS>(M0, P, NWV, NWV / wpt);
+    const AttnLds L = attn_lds<T, D, VT_LDS>(M0, P, NWV);
     T *Ps = reinterpret_cast<T *>(smem + L.ps);
     T *Vt = reinterpret_cast<T *>(smem + L.vt);
     float *nP = reinterpret_cast<float *>(smem + L.np);
@@ -259,35 +244,35 @@ void attention_kernel(
     for (int j = tid; j < M0p; j += 64 * NWV) nP[j] = pnp[j];
     __syncthreads();
 
+    const int wpt = (1 << ltile) / kQPW;         // waves per tile
     const int tw0 = (w / wpt) * wpt;             // first wave of this wave's tile
     int *mysel = selS + (w / wpt) * selStride;   // the tile's selection
     const int PC = P * CC;
 
-    for (int st = slice; st < nsteps; st += per_bh) {
-        int qi[QB];
-        bool qv[QB];
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-            qi[b] = st * STEP + QPW * w + 16 * b + i16;
-            qv[b] = qi[b] < N;
-        }
+    int buf = 0;
+    for (int st = slice; st < nsteps; st += per_bh, buf ^= 1) {
+        const int q0 = st * STEP + kQPW * w + i16, q1 = q0 + 16;
+        const bool v0 = q0 < N, v1 = q1 < N;
         // query fragments (queries past N read the last query; never stored)
-        Frag<T> qf[QB][KS];
+        Frag<T> qa[KS], qb[KS];
         auto load_q = [&]() {
+            const T *qra = Qh + (size_t)min(q0, N - 1) * D + 8 * g, *qrb = Qh + (size_t)min(q1, N - 1) * D + 8 * g;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int b = 0; b < QB; ++b) {
-                    qf[b][ks] = load_frag(Qh + (size_t)min(qi[b], N - 1) * D + 8 * g + 32 * ks);
-                    if (neg) qf[b][ks] = negate(qf[b][ks]);
+            for (int ks = 0; ks < KS; ++ks) {
+                qa[ks] = load_frag(qra + 32 * ks);
+                qb[ks] = load_frag(qrb + 32 * ks);
+                if (neg) {
+                    qa[ks] = negate(qa[ks]);
+                    qb[ks] = negate(qb[ks]);
                 }
+            }
         };
         load_q();
 
         // ---- parent logits (raw dot products, sign of the scale folded in)
         // (codeword fragments of the next row block are read from LDS while
         // the current block's MFMAs run)
-        f32x4 S[QB][NRB];
+        f32x4 S0[NRB], S1[NRB];
         if constexpr (KS == 2) {
             Frag<T> pa[2][KS];
 #pragma unroll
@@ -299,103 +284,84 @@ void attention_kernel(
                     for (int ks = 0; ks < KS; ++ks)
                         pa[(rb + 1) & 1][ks] = load_frag(Ps + (16 * (rb + 1) + i16) * LDP + 32 * ks + 8 * g);
                 }
-                f32x4 acc[QB];
+                f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
-                for (int b = 0; b < QB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int b = 0; b < QB; ++b) acc[b] = mma(pa[rb & 1][ks], qf[b][ks], acc[b]);
-#pragma unroll
-                for (int b = 0; b < QB; ++b) S[b][rb] = acc[b];
+                for (int ks = 0; ks < KS; ++ks) {
+                    a0 = mma(pa[rb & 1][ks], qa[ks], a0);
+                    a1 = mma(pa[rb & 1][ks], qb[ks], a1);
+                }
+                S0[rb] = a0;
+                S1[rb] = a1;
             }
         } else {
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
-                f32x4 acc[QB];
-#pragma unroll
-                for (int b = 0; b < QB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const Frag<T> a = load_frag(Ps + (16 * rb + i16) * LDP + 32 * ks + 8 * g);
-#pragma unroll
-                    for (int b = 0; b < QB; ++b) acc[b] = mma(a, qf[b][ks], acc[b]);
+                    a0 = mma(a, qa[ks], a0);
+                    a1 = mma(a, qb[ks], a1);
                 }
-#pragma unroll
-                for (int b = 0; b < QB; ++b) S[b][rb] = acc[b];
+                S0[rb] = a0;
+                S1[rb] = a1;
             }
         }
         // ---- shift: largest logit of each query
-        float m[QB];
-        {
-            float e[QB];
+        float e0 = -INFINITY, e1 = -INFINITY;
 #pragma unroll
-            for (int b = 0; b < QB; ++b) e[b] = -INFINITY;
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-                for (int b = 0; b < QB; ++b) {
-                    e[b] = max3f(e[b], S[b][rb][0], S[b][rb][1]);
-                    e[b] = max3f(e[b], S[b][rb][2], S[b][rb][3]);
-                }
-#pragma unroll
-            for (int b = 0; b < QB; ++b) m[b] = sl2 * xgroup_max(e[b]);
+        for (int rb = 0; rb < NRB; ++rb) {
+            e0 = max3f(e0, S0[rb][0], S0[rb][1]);
+            e0 = max3f(e0, S0[rb][2], S0[rb][3]);
+            e1 = max3f(e1, S1[rb][0], S1[rb][1]);
+            e1 = max3f(e1, S1[rb][2], S1[rb][3]);
         }
+        float m0 = sl2 * xgroup_max(e0), m1 = sl2 * xgroup_max(e1);
 
         // ---- E = exp(scale*s - m), denominators
-        float Zf[QB], rz[QB];
-        {
-            float z[QB];
+        float z0 = 0.f, z1 = 0.f;
 #pragma unroll
-            for (int b = 0; b < QB; ++b) z[b] = 0.f;
+        for (int rb = 0; rb < NRB; ++rb) {
+            const f32x4 nv = *reinterpret_cast<const f32x4 *>(nP + 16 * rb + 4 * g);
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) {
-                const f32x4 nv = *reinterpret_cast<const f32x4 *>(nP + 16 * rb + 4 * g);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int b = 0; b < QB; ++b) {
-                        const float x = __builtin_amdgcn_exp2f(fmaf(S[b][rb][r], sl2, -m[b]));
-                        S[b][rb][r] = x;
-                        z[b] = fmaf(x, nv[r], z[b]);
-                    }
-            }
-#pragma unroll
-            for (int b = 0; b < QB; ++b) {
-                Zf[b] = xgroup_sum(z[b]);
-                rz[b] = qv[b] ? __builtin_amdgcn_rcpf(Zf[b]) : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const float x0 = __builtin_amdgcn_exp2f(fmaf(S0[rb][r], sl2, -m0));
+                const float x1 = __builtin_amdgcn_exp2f(fmaf(S1[rb][r], sl2, -m1));
+                S0[rb][r] = x0;
+                S1[rb][r] = x1;
+                z0 = fmaf(x0, nv[r], z0);
+                z1 = fmaf(x1, nv[r], z1);
             }
         }
+        float Zf0 = xgroup_sum(z0), Zf1 = xgroup_sum(z1);
+        const float r0 = v0 ? __builtin_amdgcn_rcpf(Zf0) : 0.f, r1 = v1 ? __builtin_amdgcn_rcpf(Zf1) : 0.f;
 
         // ---- E as MFMA operands; the fp32 copy becomes the importance terms
-        // t = sum_b E_b / Z_b over this wave's queries of every lane
-        Frag<T> E[QB][NRB / 2];
+        // t = E0 / Z0 + E1 / Z1 (this wave's two queries of every lane)
+        Frag<T> E0[NRB / 2], E1[NRB / 2];
 #pragma unroll
         for (int s = 0; s < NRB / 2; ++s) {
-#pragma unroll
-            for (int b = 0; b < QB; ++b) E[b][s] = pack_frag<T>(S[b][2 * s], S[b][2 * s + 1]);
+            E0[s] = pack_frag<T>(S0[2 * s], S0[2 * s + 1]);
+            E1[s] = pack_frag<T>(S1[2 * s], S1[2 * s + 1]);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (QB == 2)
-                        S[0][2 * s + hh][r] = fmaf(S[0][2 * s + hh][r], rz[0], S[1][2 * s + hh][r] * rz[1]);
-                    else
-                        S[0][2 * s + hh][r] *= rz[0];
-                }
+                for (int r = 0; r < 4; ++r)
+                    S0[2 * s + hh][r] = fmaf(S0[2 * s + hh][r], r0, S1[2 * s + hh][r] * r1);
         }
         // sum over the 16 queries of each row and write this wave's partials
         {
             constexpr int LG = NRB == 16 ? 4 : NRB == 8 ? 3 : NRB == 4 ? 2 : 1;
-            const f32x4 part = row16_reduce_scatter<NRB>(S[0], i16);
-            *reinterpret_cast<f32x4 *>(Wp + w * M0p + 16 * (i16 >> (4 - LG)) + 4 * g) = part;
+            const f32x4 part = row16_reduce_scatter<NRB>(S0, i16);
+            *reinterpret_cast<f32x4 *>(Wp + (buf * NWV + w) * M0p + 16 * (i16 >> (4 - LG)) + 4 * g) = part;
         }
         // X^T = Vbar^T E^T over the parents
-        f32x4 X[QB][DB];
+        f32x4 X0[DB], X1[DB];
 #pragma unroll
-        for (int b = 0; b < QB; ++b)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) X[b][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < DB; ++db) {
+            X0[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+            X1[db] = X0[db];
+        }
         // (value-sum fragments of the next 32 parents are read while the
         // current ones' MFMAs run)
         // From global memory the fragments are the same in every step; the
@@ -418,9 +384,10 @@ void attention_kernel(
                     for (int db = 0; db < DB; ++db) va[(s + 1) & 1][db] = vt_frag(s + 1, db);
                 }
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int b = 0; b < QB; ++b) X[b][db] = mma(va[s & 1][db], E[b][s], X[b][db]);
+                for (int db = 0; db < DB; ++db) {
+                    X0[db] = mma(va[s & 1][db], E0[s], X0[db]);
+                    X1[db] = mma(va[s & 1][db], E1[s], X1[db]);
+                }
             }
         } else {
 #pragma unroll
@@ -428,12 +395,12 @@ void attention_kernel(
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const Frag<T> a = vt_frag(s, db);
-#pragma unroll
-                    for (int b = 0; b < QB; ++b) X[b][db] = mma(a, E[b][s], X[b][db]);
+                    X0[db] = mma(a, E0[s], X0[db]);
+                    X1[db] = mma(a, E1[s], X1[db]);
                 }
             }
         }
-        __syncthreads();       // every wave's importance partials are in Wp
+        __syncthreads();       // every wave's importance partials are in Wp[buf]
 
         // ---- tile importance and top-P, by the first wave of each tile (the
         // tile's other waves wait at the barrier below)
@@ -441,6 +408,7 @@ void attention_kernel(
         if ((P > 0 || imp_out) && w == tw0) {
             // sum of the tile's wave partials (all NWV slots are read, those of
             // other tiles are masked out, so the loop has no branches)
+            const float *wb = Wp + buf * NWV * M0p;
             float wv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -448,7 +416,7 @@ void attention_kernel(
                 float a = 0.f;
 #pragma unroll
                 for (int ww = 0; ww < NWV; ++ww) {
-                    const float x = Wp[((tw0 + ww) & (NWV - 1)) * M0p + jc];
+                    const float x = wb[((tw0 + ww) & (NWV - 1)) * M0p + jc];
                     a += ww < wpt ? x : 0.f;
                 }
                 wv[i] = j < M0 ? a * nP[jc] : 0.f;
@@ -464,10 +432,7 @@ void attention_kernel(
                 select_top_p_regs(wv, M0, P, mysel,
                                   (sel_out && tg < ntiles) ? sel_out + ((size_t)bh * ntiles + tg) * P : nullptr);
         }
-        // the selection is in LDS, and the partials have been read before any
-        // wave writes the next step's (with one wave per tile, the reader is
-        // the only writer of its slot)
-        if ((P > 0 || imp_out) && wpt > 1) __syncthreads();
+        if (P > 0 && wpt > 1) __syncthreads();   // the selection is in LDS
 
         // ---- child correction, SCH chunks of 32 children at a time.
         // A position ph >= P*C (padding of the last chunks) takes the
@@ -482,9 +447,7 @@ void attention_kernel(
             asm volatile("" ::: "memory");
             load_q();
         }
-        float dz[QB];
-#pragma unroll
-        for (int b = 0; b < QB; ++b) dz[b] = 0.f;
+        float dz0 = 0.f, dz1 = 0.f;
         const float sl2c = sl2 * (1.0f / (float)CC);   // mean over CC children, scaled
         constexpr int SC = 32 * SCH;                    // children per super-chunk
 
@@ -553,29 +516,23 @@ void attention_kernel(
             }
             if (more) load_cw(c0 + SC, nxt);
             // child logits and their maximum
-            f32x4 SA[QB][SCH], SB[QB][SCH];
-            float cm[QB];
-#pragma unroll
-            for (int b = 0; b < QB; ++b) cm[b] = -INFINITY;
+            f32x4 SA0[SCH], SB0[SCH], SA1[SCH], SB1[SCH];
+            float c0m = -INFINITY, c1m = -INFINITY;
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
-                f32x4 a[QB], bb[QB];
+                f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, b0 = a0, a1 = a0, b1 = a0;
 #pragma unroll
-                for (int b = 0; b < QB; ++b) a[b] = bb[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int b = 0; b < QB; ++b) {
-                        a[b] = mma(cw.a[q][ks], qf[b][ks], a[b]);
-                        bb[b] = mma(cw.b[q][ks], qf[b][ks], bb[b]);
-                    }
-#pragma unroll
-                for (int b = 0; b < QB; ++b) {
-                    SA[b][q] = a[b];
-                    SB[b][q] = bb[b];
-                    cm[b] = max3f(cm[b], max3f(a[b][0], a[b][1], a[b][2]), max3f(a[b][3], bb[b][0], bb[b][1]));
-                    cm[b] = max3f(cm[b], bb[b][2], bb[b][3]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    a0 = mma(cw.a[q][ks], qa[ks], a0);
+                    b0 = mma(cw.b[q][ks], qa[ks], b0);
+                    a1 = mma(cw.a[q][ks], qb[ks], a1);
+                    b1 = mma(cw.b[q][ks], qb[ks], b1);
                 }
+                SA0[q] = a0; SB0[q] = b0; SA1[q] = a1; SB1[q] = b1;
+                c0m = max3f(c0m, max3f(a0[0], a0[1], a0[2]), max3f(a0[3], b0[0], b0[1]));
+                c0m = max3f(c0m, b0[2], b0[3]);
+                c1m = max3f(c1m, max3f(a1[0], a1[1], a1[2]), max3f(a1[3], b1[0], b1[1]));
+                c1m = max3f(c1m, b1[2], b1[3]);
             }
             // raise the shift to cover the child logits, rescale X and Z
             // The shift only has to keep the weights in range: child weights
@@ -583,66 +540,63 @@ void attention_kernel(
             // raised (and X, Z rescaled) only when a child logit exceeds it
             // by more than that, which takes extreme logit ranges.
             {
-                float n[QB];
-                bool up = false;
+                const float n0 = fmaxf(m0, sl2 * xgroup_max(c0m));
+                const float n1 = fmaxf(m1, sl2 * xgroup_max(c1m));
+                if (__ballot((n0 > m0 + 32.f) | (n1 > m1 + 32.f))) {
+                    const float a0 = __builtin_amdgcn_exp2f(m0 - n0), a1 = __builtin_amdgcn_exp2f(m1 - n1);
+                    m0 = n0; m1 = n1;
+                    Zf0 *= a0; dz0 *= a0; Zf1 *= a1; dz1 *= a1;
 #pragma unroll
-                for (int b = 0; b < QB; ++b) {
-                    n[b] = fmaxf(m[b], sl2 * xgroup_max(cm[b]));
-                    up |= n[b] > m[b] + 32.f;
-                }
-                if (__ballot(up)) {
-#pragma unroll
-                    for (int b = 0; b < QB; ++b) {
-                        const float a = __builtin_amdgcn_exp2f(m[b] - n[b]);
-                        m[b] = n[b];
-                        Zf[b] *= a;
-                        dz[b] *= a;
-#pragma unroll
-                        for (int db = 0; db < DB; ++db) X[b][db] *= a;
-                    }
+                    for (int db = 0; db < DB; ++db) { X0[db] *= a0; X1[db] *= a1; }
                 }
             }
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
                 // exp of the recovered parent logit of each child's parent
-                float eA[QB][2], eB[QB][2];   // [b][r >> 1]
+                float eA0[2], eB0[2], eA1[2], eB1[2];   // [r >> 1]
+                if constexpr (CC >= 8) {
+                    float u0 = (SA0[q][0] + SA0[q][1]) + (SA0[q][2] + SA0[q][3]) +
+                               ((SB0[q][0] + SB0[q][1]) + (SB0[q][2] + SB0[q][3]));
+                    float u1 = (SA1[q][0] + SA1[q][1]) + (SA1[q][2] + SA1[q][3]) +
+                               ((SB1[q][0] + SB1[q][1]) + (SB1[q][2] + SB1[q][3]));
+                    if constexpr (CC == 16) {
+                        u0 = pair16_sum(u0);
+                        u1 = pair16_sum(u1);
+                    }
+                    const float f0 = __builtin_amdgcn_exp2f(fmaf(u0, sl2c, -m0));
+                    const float f1 = __builtin_amdgcn_exp2f(fmaf(u1, sl2c, -m1));
+                    eA0[0] = eA0[1] = eB0[0] = eB0[1] = f0;
+                    eA1[0] = eA1[1] = eB1[0] = eB1[1] = f1;
+                } else if constexpr (CC == 4) {
+                    eA0[0] = eA0[1] = __builtin_amdgcn_exp2f(fmaf((SA0[q][0] + SA0[q][1]) + (SA0[q][2] + SA0[q][3]), sl2c, -m0));
+                    eB0[0] = eB0[1] = __builtin_amdgcn_exp2f(fmaf((SB0[q][0] + SB0[q][1]) + (SB0[q][2] + SB0[q][3]), sl2c, -m0));
+                    eA1[0] = eA1[1] = __builtin_amdgcn_exp2f(fmaf((SA1[q][0] + SA1[q][1]) + (SA1[q][2] + SA1[q][3]), sl2c, -m1));
+                    eB1[0] = eB1[1] = __builtin_amdgcn_exp2f(fmaf((SB1[q][0] + SB1[q][1]) + (SB1[q][2] + SB1[q][3]), sl2c, -m1));
+                } else {   // CC == 2
 #pragma unroll
-                for (int b = 0; b < QB; ++b) {
-                    if constexpr (CC >= 8) {
-                        float u = (SA[b][q][0] + SA[b][q][1]) + (SA[b][q][2] + SA[b][q][3]) +
-                                  ((SB[b][q][0] + SB[b][q][1]) + (SB[b][q][2] + SB[b][q][3]));
-                        if constexpr (CC == 16) u = pair16_sum(u);
-                        const float f = __builtin_amdgcn_exp2f(fmaf(u, sl2c, -m[b]));
-                        eA[b][0] = eA[b][1] = eB[b][0] = eB[b][1] = f;
-                    } else if constexpr (CC == 4) {
-                        eA[b][0] = eA[b][1] = __builtin_amdgcn_exp2f(
-                            fmaf((SA[b][q][0] + SA[b][q][1]) + (SA[b][q][2] + SA[b][q][3]), sl2c, -m[b]));
-                        eB[b][0] = eB[b][1] = __builtin_amdgcn_exp2f(
-                            fmaf((SB[b][q][0] + SB[b][q][1]) + (SB[b][q][2] + SB[b][q][3]), sl2c, -m[b]));
-                    } else {   // CC == 2
-#pragma unroll
-                        for (int k = 0; k < 2; ++k) {
-                            eA[b][k] = __builtin_amdgcn_exp2f(fmaf(SA[b][q][2 * k] + SA[b][q][2 * k + 1], sl2c, -m[b]));
-                            eB[b][k] = __builtin_amdgcn_exp2f(fmaf(SB[b][q][2 * k] + SB[b][q][2 * k + 1], sl2c, -m[b]));
-                        }
+                    for (int k = 0; k < 2; ++k) {
+                        eA0[k] = __builtin_amdgcn_exp2f(fmaf(SA0[q][2 * k] + SA0[q][2 * k + 1], sl2c, -m0));
+                        eB0[k] = __builtin_amdgcn_exp2f(fmaf(SB0[q][2 * k] + SB0[q][2 * k + 1], sl2c, -m0));
+                        eA1[k] = __builtin_amdgcn_exp2f(fmaf(SA1[q][2 * k] + SA1[q][2 * k + 1], sl2c, -m1));
+                        eB1[k] = __builtin_amdgcn_exp2f(fmaf(SB1[q][2 * k] + SB1[q][2 * k + 1], sl2c, -m1));
                     }
                 }
-                f32x4 dA[QB], dB[QB];
+                f32x4 dA0, dB0, dA1, dB1;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < 4; ++r) {
+                    dA0[r] = __builtin_amdgcn_exp2f(fmaf(SA0[q][r], sl2, -m0)) - eA0[r >> 1];
+                    dB0[r] = __builtin_amdgcn_exp2f(fmaf(SB0[q][r], sl2, -m0)) - eB0[r >> 1];
+                    dA1[r] = __builtin_amdgcn_exp2f(fmaf(SA1[q][r], sl2, -m1)) - eA1[r >> 1];
+                    dB1[r] = __builtin_amdgcn_exp2f(fmaf(SB1[q][r], sl2, -m1)) - eB1[r >> 1];
+                    dz0 = fmaf(dA0[r], nA[q][r], fmaf(dB0[r], nB[q][r], dz0));
+                    dz1 = fmaf(dA1[r], nA[q][r], fmaf(dB1[r], nB[q][r], dz1));
+                }
+                const Frag<T> b0 = pack_frag<T>(dA0, dB0), b1 = pack_frag<T>(dA1, dB1);
 #pragma unroll
-                    for (int b = 0; b < QB; ++b) {
-                        dA[b][r] = __builtin_amdgcn_exp2f(fmaf(SA[b][q][r], sl2, -m[b])) - eA[b][r >> 1];
-                        dB[b][r] = __builtin_amdgcn_exp2f(fmaf(SB[b][q][r], sl2, -m[b])) - eB[b][r >> 1];
-                        dz[b] = fmaf(dA[b][r], nA[q][r], fmaf(dB[b][r], nB[q][r], dz[b]));
-                    }
-                Frag<T> dp[QB];
-#pragma unroll
-                for (int b = 0; b < QB; ++b) dp[b] = pack_frag<T>(dA[b], dB[b]);
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int b = 0; b < QB; ++b) X[b][db] = mma(vc[q][db], dp[b], X[b][db]);
+                for (int db = 0; db < DB; ++db) {
+                    X0[db] = mma(vc[q][db], b0, X0[db]);
+                    X1[db] = mma(vc[q][db], b1, X1[db]);
+                }
             }
         };
         if (PC > 0) {
@@ -656,41 +610,30 @@ void attention_kernel(
         }
 
         // ---- Y = X / Z: lane (g, i) holds dims 16*db + 4g .. +3 of its query
-        float Zt[QB];
-#pragma unroll
-        for (int b = 0; b < QB; ++b) Zt[b] = Zf[b] + xgroup_sum(dz[b]);
-#pragma unroll
-        for (int b = 0; b < QB; ++b)
-            if (qv[b]) store_row4<T, DB>(Yh + (size_t)qi[b] * D + 4 * g, X[b], __builtin_amdgcn_rcpf(Zt[b]));
+        const float Z0 = Zf0 + xgroup_sum(dz0), Z1 = Zf1 + xgroup_sum(dz1);
+        if (v0) store_row4<T, DB>(Yh + (size_t)q0 * D + 4 * g, X0, __builtin_amdgcn_rcpf(Z0));
+        if (v1) store_row4<T, DB>(Yh + (size_t)q1 * D + 4 * g, X1, __builtin_amdgcn_rcpf(Z1));
     }
 }
 
 // ---------------------------------------------------------------------------
 
-// waves per work-group for a query tile: whole tiles, and at least four
-// waves (eight when the d = 128 value sums are held in LDS: the work-group
-// then fills its CU alone)
-template <typename T, int D, bool VT> static int attn_waves(int tile)
-{
-    constexpr int lo = VT && D == 128 ? 8 : 4;
-    const int w = tile / (16 * attn_qb<T, D>());
-    return w > lo ? w : lo;
-}
-
-template <typename T, int D, bool VT>
-static size_t attn_lds_bytes(int M0, int P, int tile)
-{
-    const int nw = attn_waves<T, D, VT>(tile);
-    return attn_lds<T, D, VT>(M0, P, nw, nw * 16 * attn_qb<T, D>() / tile).total;
-}
+// waves per work-group for a query tile: 4, or 8 for 256-query tiles and
+// whenever the d = 128 value sums are held in LDS (the work-group then fills
+// its CU alone)
+template <int D, bool VT> static int attn_waves(int tile) { return tile >= 256 || (VT && D == 128) ? 8 : 4; }
 
 int attention_child_chunk(int d, int M0, int C, int P, int tile, int dtype)
 {
     (void)C;
     if (tile != 32 && tile != 64 && tile != 128 && tile != 256) return 0;
     size_t lds;
-    if (dtype == 1) lds = d == 64 ? attn_lds_bytes<bf16, 64, true>(M0, P, tile) : attn_lds_bytes<bf16, 128, true>(M0, P, tile);
-    else lds = d == 64 ? attn_lds_bytes<float, 64, true>(M0, P, tile) : attn_lds_bytes<float, 128, false>(M0, P, tile);
+    if (dtype == 1)
+        lds = d == 64 ? attn_lds<bf16, 64, true>(M0, P, attn_waves<64, true>(tile)).total
+                      : attn_lds<bf16, 128, true>(M0, P, attn_waves<128, true>(tile)).total;
+    else
+        lds = d == 64 ? attn_lds<float, 64, true>(M0, P, attn_waves<64, true>(tile)).total
+                      : attn_lds<float, 128, false>(M0, P, attn_waves<128, false>(tile)).total;
     return lds <= 160 * 1024 ? 32 : 0;
 }
 
@@ -720,28 +663,25 @@ static hipError_t launch_attn_k(const void *Q, const void *parents, const void *
                                 const void *pack, int B, int H, int N, int M0, int P, int tile,
                                 float scale, void *Y, int32_t *sel, float *imp, hipStream_t stream)
 {
-    constexpr int QB = attn_qb<T, D>();
-    constexpr int STEP = NWV * 16 * QB;
     static bool attr = false;
     if (!attr) {
-        (void)hipFuncSetAttribute((const void *)attention_kernel<T, D, VT, NRB, CC, NWV, QB>,
+        (void)hipFuncSetAttribute((const void *)attention_kernel<T, D, VT, NRB, CC, NWV>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr = true;
     }
-    const size_t lds = attn_lds<T, D, VT>(M0, P, NWV, STEP / tile).total;
+    const size_t lds = attn_lds<T, D, VT>(M0, P, NWV).total;
     const int ntiles = (N + tile - 1) / tile;
-    const int nsteps = (N + STEP - 1) / STEP;
+    const int nsteps = (N + NWV * kQPW - 1) / (NWV * kQPW);
     const int BH = B * H;
-    // work-groups resident per CU (LDS and registers), each a slice of one
-    // head's steps
-    const int by_lds = lds * 2 <= 160 * 1024 ? 2 : 1;
-    const int by_regs = 4 * attn_waves_per_simd<T, D, QB>() / NWV;
-    const int per_cu = by_regs < by_lds ? (by_regs > 0 ? by_regs : 1) : by_lds;
-    // (rounded down, so that every work-group is resident from the start: one
-    // more slice per head would leave work-groups waiting for a second round)
+    // two work-groups per CU when LDS and registers allow (an 8-wave
+    // work-group takes both of a SIMD's two wave slots), each a slice of one
+    // head's steps; rounded down, so that every work-group is resident from
+    // the start (one more slice per head would leave work-groups waiting for
+    // a second round)
+    const int per_cu = NWV == 4 && lds * 2 <= 160 * 1024 ? 2 : 1;
     const int per_bh = max(1, min(nsteps, per_cu * device_cus() / BH));
     const int grid = (BH * per_bh + 7) & ~7;
-    hipLaunchKernelGGL((attention_kernel<T, D, VT, NRB, CC, NWV, QB>), dim3(grid), dim3(64 * NWV), lds, stream,
+    hipLaunchKernelGGL((attention_kernel<T, D, VT, NRB, CC, NWV>), dim3(grid), dim3(64 * NWV), lds, stream,
                        (const T *)Q, (const T *)parents, (const T *)children, (const unsigned char *)pack,
                        H, N, M0, P, ilog2(tile), fabsf(scale) * kLog2e, scale < 0.f ? 1 : 0, ntiles,
                        nsteps, per_bh, BH, (T *)Y, sel, imp);
@@ -753,7 +693,7 @@ static hipError_t launch_attn_w(const void *Q, const void *parents, const void *
                                 const void *pack, int B, int H, int N, int M0, int P, int tile,
                                 float scale, void *Y, int32_t *sel, float *imp, hipStream_t stream)
 {
-    if (attn_waves<T, D, VT>(tile) == 8)
+    if (attn_waves<D, VT>(tile) == 8)
         return launch_attn_k<T, D, VT, NRB, CC, 8>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
     if constexpr (!(VT && D == 128))
         return launch_attn_k<T, D, VT, NRB, CC, 4>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
@@ -779,7 +719,7 @@ static hipError_t launch_attn_t(const void *Q, const void *parents, const void *
                                 const void *pack, int B, int H, int N, int M0, int C, int P, int tile,
                                 float scale, void *Y, int32_t *sel, float *imp, hipStream_t stream)
 {
-    if (attn_lds_bytes<T, D, VT>(M0, P, tile) > 160 * 1024) return hipErrorInvalidConfiguration;
+    if (attn_lds<T, D, VT>(M0, P, attn_waves<D, VT>(tile)).total > 160 * 1024) return hipErrorInvalidConfiguration;
     switch (padded_parents(M0)) {
     case 32: return launch_attn_nrb<T, D, VT, 2>(Q, parents, children, pack, B, H, N, M0, C, P, tile, scale, Y, sel, imp, stream);
     case 64: return launch_attn_nrb<T, D, VT, 4>(Q, parents, children, pack, B, H, N, M0, C, P, tile, scale, Y, sel, imp, stream);
