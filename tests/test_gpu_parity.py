@@ -128,6 +128,12 @@ EDGE = [
     ("bf16", 64, 256, 8, 256, 128, 2100, False),
     ("bf16", 64, 40, 8, 6, 64, 3000, True),
     ("f32", 64, 16, 4, 4, 64, 1024, True),
+    # d = 128: 256-query tiles over 8-wave work-groups, C = 2, 30 parents
+    ("bf16", 128, 30, 2, 5, 256, 1500, False),
+    # d = 128 with C = 16 (refinement groups of two parents), fp32, and a
+    # ragged last group (129 parents)
+    ("f32", 128, 48, 16, 3, 32, 900, False),
+    ("bf16", 128, 129, 16, 20, 64, 777, True),
 ]
 
 
