@@ -134,6 +134,8 @@ EDGE = [
     # ragged last group (129 parents)
     ("f32", 128, 48, 16, 3, 32, 900, False),
     ("bf16", 128, 129, 16, 20, 64, 777, True),
+    # fp32 at d = 128 with 256-query tiles (8 waves, value sums from L2)
+    ("f32", 128, 200, 4, 8, 256, 1100, False),
 ]
 
 
@@ -141,6 +143,31 @@ EDGE = [
 def test_edge_shapes(avq, dtype, d, M0, C, P, T, N, force):
     inp = synth.generate("vit-b", B=1, H=2, N=N, d=d, M0=M0, C=C, P=P, T=T, dtype=dtype,
                          seed=77 + M0 + N)
+    check_all(avq, inp, force_child=force)
+
+
+def _random_shapes(n, seed=2024):
+    """n shapes drawn from the supported space (fp32 at d = 128 keeps M0 <=
+    128 so that its parents fit in LDS for every tile)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = str(rng.choice(["bf16", "f32"]))
+        d = int(rng.choice([64, 128]))
+        M0 = int(rng.integers(1, 129 if (dtype == "f32" and d == 128) else 257))
+        C = int(rng.choice([2, 4, 8, 16]))
+        P = int(rng.integers(0, M0 + 1))
+        T = int(rng.choice([32, 64, 128, 256]))
+        N = int(rng.integers(1, 2500))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        out.append((dtype, d, M0, C, P, T, N, B, H, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("dtype,d,M0,C,P,T,N,B,H,force", _random_shapes(12))
+def test_random_shapes(avq, dtype, d, M0, C, P, T, N, B, H, force):
+    inp = synth.generate("vit-b", B=B, H=H, N=N, d=d, M0=M0, C=C, P=P, T=T, dtype=dtype,
+                         seed=500 + N + M0)
     check_all(avq, inp, force_child=force)
 
 
