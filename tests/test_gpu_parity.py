@@ -204,6 +204,23 @@ def test_child_logits_far_above_the_shift(avq):
     check_all(avq, inp)
 
 
+@pytest.mark.parametrize("dtype,d,M0,C,N", [("bf16", 64, 256, 8, 6000), ("bf16", 128, 64, 16, 3000),
+                                            ("f32", 64, 40, 4, 2600)])
+def test_skewed_keys_split_groups(avq, dtype, d, M0, C, N):
+    # 70 % of the keys sit next to one child of parent 0, so one refinement
+    # group (one work-group of the refinement kernel) holds most of the list
+    inp = synth.generate("vit-b", B=1, H=2, N=N, d=d, M0=M0, C=C, P=5, T=64, dtype=dtype, seed=93 + N)
+    rng = np.random.default_rng(N)
+    K64, ch64 = inp.f64("K"), inp.f64("children")
+    hot = rng.random((1, inp.H, N)) < 0.7
+    near = ch64[:, 0, C // 2][None, :, None, :] + 0.01 * rng.standard_normal(K64.shape)
+    inp.K = synth.to_storage(np.where(hot[..., None], near, K64), dtype)
+    r = check_all(avq, inp)
+    group = 2 if (C == 16 and d == 128) else 4
+    heavy = r["count"][..., :group].sum(axis=-1)            # keys of the first group
+    assert heavy.min() > 0.6 * N
+
+
 # ------------------------------------------------------------------ invariants
 
 
