@@ -28,6 +28,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+# exponentials per second: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64 v_exp_f32
+# per 8 cycles per SIMD (measured issue cost) = 8 per cycle per SIMD
+EXP_PEAK_PER_S = 256 * 4 * 2.4e9 * 8
 MFMA_PEAK = {"bf16": 2500.0, "f32": 157.3}   # dense TFLOP/s (fp32 on the fp32 MFMA path)
 METRIC = "AVQ attention fwd tokens/s/head at N=64k; % HBM BW and % MFMA peak"
 
@@ -45,7 +48,9 @@ def algorithmic(inp, P):
     s1_flops = BH * N * 2 * d * (M0 + C)
     s2_bytes = BH * (N * 2 * d * e + S * (4 * d + 4 + d * e))
     s2_flops = BH * N * 4 * d * (M0 + P * C)
-    return dict(s1_bytes=s1_bytes, s1_flops=s1_flops, s2_bytes=s2_bytes, s2_flops=s2_flops)
+    s2_exps = BH * N * (M0 + P * (C + 1))
+    return dict(s1_bytes=s1_bytes, s1_flops=s1_flops, s2_bytes=s2_bytes, s2_flops=s2_flops,
+                s2_exps=s2_exps)
 
 
 def measured_traffic(kernel, workload):
@@ -250,7 +255,9 @@ def main():
                               "alg_bytes": alg["s2_bytes"], "TFLOPs": round(s2_tfs, 2),
                               "GBps": round(s2_gbs, 1), "bound": s2_bound,
                               "frac_mfma": round(s2_tfs / peak_mf, 4),
-                              "frac_hbm": round(s2_gbs / HBM_PEAK_GBS, 4)},
+                              "frac_hbm": round(s2_gbs / HBM_PEAK_GBS, 4),
+                              "alg_exps": alg["s2_exps"],
+                              "exp_bound_ms": round(alg["s2_exps"] / EXP_PEAK_PER_S * 1e3, 5)},
         },
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 5),
         "ms_per_step_with_stage_events": round(ms_step_instrumented, 5),
