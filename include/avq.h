@@ -164,8 +164,9 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents,
  *              every tile in ascending index order
  *   importance_out [B][H][ceil(N/tile)][M0] fp32, optional: w_j(I)
  *   Requires at least one key per (b, h) (every count row sums to N >= 1).
- *   Returns AVQ_ERR_UNSUPPORTED if the codebook does not fit the kernel's
- *   on-chip budget (large fp32 trees).
+ *   Returns AVQ_ERR_UNSUPPORTED if the codebook and tile do not fit the
+ *   kernel's 160 KB of LDS: only fp32 with M0 near 256, 256-query tiles and
+ *   P above ~160 (d = 64) or ~224 (d = 128).
  */
 int avq_attention_fwd(const void *Q, const void *parents, const void *children,
                       const void *pack, int B, int H, int N, int d, int M0, int C,
