@@ -102,6 +102,11 @@ def test_invalid_arguments_are_rejected_before_launch(lib):
     assert call(M0=300, P=4) == -2
     assert call(tile=48) == -2
     assert b"tile" in lib.avq_last_error()
+    # fp32 codebooks of 256 parents with 256-query tiles and a large P exceed
+    # the attention kernel's 160 KB of LDS
+    assert call(dt=0, M0=256, tile=256, P=200) == -2
+    assert call(dt=0, d=128, M0=256, tile=256, P=240) == -2
+    assert b"LDS" in lib.avq_last_error()
     assert call(N=(1 << 20) + 1) == -2
 
     aa = lib.avq_assign_aggregate
