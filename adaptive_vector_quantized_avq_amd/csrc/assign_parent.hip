@@ -270,12 +270,7 @@ static hipError_t launch_assign(const void *K, const void *parents, const float 
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     const size_t lds = (size_t)16 * NRB * (D + 8) * sizeof(T) + (size_t)16 * NRB * 4 +
                        kAssignChunk + 257 * 4;
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute((const void *)assign_parent_kernel<T, D, NRB>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr = true;
-    }
+    allow_full_lds<assign_parent_kernel<T, D, NRB>>();
     hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(kAssignThreads), lds, stream,
                        (const T *)K, (const T *)parents, sqnorm, H, N, M0, C, nchunks, ws.sorted,
                        ws.seg);

@@ -663,12 +663,7 @@ static hipError_t launch_attn_k(const void *Q, const void *parents, const void *
                                 const void *pack, int B, int H, int N, int M0, int P, int tile,
                                 float scale, void *Y, int32_t *sel, float *imp, hipStream_t stream)
 {
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute((const void *)attention_kernel<T, D, VT, NRB, CC, NWV>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr = true;
-    }
+    allow_full_lds<attention_kernel<T, D, VT, NRB, CC, NWV>>();
     const size_t lds = attn_lds<T, D, VT>(M0, P, NWV).total;
     const int ntiles = (N + tile - 1) / tile;
     const int nsteps = (N + NWV * kQPW - 1) / (NWV * kQPW);

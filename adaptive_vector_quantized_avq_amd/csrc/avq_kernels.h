@@ -7,9 +7,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "avq_device.h"
 
 namespace avq {
+
+// Raises kernel KERNEL's dynamic-LDS limit to a CU's 160 KB, once per device
+// (the attribute belongs to the function on the current device).
+template <auto KERNEL> inline void allow_full_lds()
+{
+    static std::atomic<unsigned long long> done{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    const unsigned long long bit = 1ull << dev;
+    if (!(done.load(std::memory_order_relaxed) & bit)) {
+        (void)hipFuncSetAttribute((const void *)KERNEL, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  160 * 1024);
+        done.fetch_or(bit, std::memory_order_relaxed);
+    }
+}
 
 // keys per chunk of the parent-assignment kernel; a chunk's keys are
 // bucketed by parent in the workspace

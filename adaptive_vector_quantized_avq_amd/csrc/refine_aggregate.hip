@@ -475,12 +475,7 @@ static hipError_t launch_refine(const void *K, const void *V, const void *parent
 {
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     const size_t lds = RefineCfg<T, D, CC>::lds(nchunks);
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute((const void *)refine_aggregate_kernel<T, D, CC>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr = true;
-    }
+    allow_full_lds<refine_aggregate_kernel<T, D, CC>>();
     const int ngroups = (M0 + RefineCfg<T, D, CC>::G - 1) / RefineCfg<T, D, CC>::G;
     hipLaunchKernelGGL((refine_aggregate_kernel<T, D, CC>), dim3(ngroups, B * H), dim3(kRefineThreads),
                        lds, stream, (const T *)K, (const T *)V, (const T *)parents,
