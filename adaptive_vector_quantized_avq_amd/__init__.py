@@ -89,6 +89,12 @@ def _stream(dev: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _on(dev: torch.device):
+    # the library launches on the given stream but reads per-device state
+    # (CU count, kernel attributes) from the current device
+    return torch.cuda.device(dev)
+
+
 def _dt(t: torch.Tensor) -> int:
     if t.dtype not in _DTYPES:
         raise AvqError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
@@ -114,8 +120,9 @@ def build_tree(children: torch.Tensor):
     H, M0, C, d = children.shape
     parents = torch.empty((H, M0, d), dtype=children.dtype, device=children.device)
     sqnorm = torch.empty((H, M0 * (1 + C)), dtype=torch.float32, device=children.device)
-    _check(load_library().avq_build_tree(_ptr(children), H, M0, C, d, _dt(children), _ptr(parents),
-                                         _ptr(sqnorm), _stream(children.device)))
+    with _on(children.device):
+        _check(load_library().avq_build_tree(_ptr(children), H, M0, C, d, _dt(children), _ptr(parents),
+                                             _ptr(sqnorm), _stream(children.device)))
     return parents, sqnorm
 
 
@@ -156,11 +163,19 @@ def assign_aggregate(K, V, parents, children, sqnorm, force_child: bool = False,
                            device=dev)
     else:
         vsum, count, pack = out
+        _need(vsum, "vsum", 4, torch.float32, dev)
+        _need(count, "count", 3, torch.int32, dev)
+        _need(pack, "pack", 1, torch.uint8, dev)
+        if vsum.shape != (B, H, S, d) or count.shape != (B, H, S) or \
+                pack.numel() < int(lib.avq_operand_pack_size(B, H, M0, C, d, _dt(K))):
+            raise AvqError("output buffers do not match the shape")
+    _need(workspace, "workspace", 1, torch.uint8, dev)
     leaf = torch.empty((B, H, N), dtype=torch.int32, device=dev) if want_leaf else None
-    _check(lib.avq_assign_aggregate(
-        _ptr(K), _ptr(V), _ptr(parents), _ptr(children), _ptr(sqnorm), B, H, N, d, M0, C, _dt(K),
-        AVQ_FLAG_FORCE_CHILD if force_child else 0, _ptr(vsum), _ptr(count), _ptr(leaf), _ptr(pack),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    with _on(dev):
+        _check(lib.avq_assign_aggregate(
+            _ptr(K), _ptr(V), _ptr(parents), _ptr(children), _ptr(sqnorm), B, H, N, d, M0, C, _dt(K),
+            AVQ_FLAG_FORCE_CHILD if force_child else 0, _ptr(vsum), _ptr(count), _ptr(leaf), _ptr(pack),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
     return vsum, count, leaf, pack
 
 
@@ -183,11 +198,15 @@ def attention_fwd(Q, parents, children, pack, P: int, tile: int, scale: float,
         raise AvqError("operand pack too small for this shape")
     nt = -(-N // tile) if tile > 0 else 0
     Y = torch.empty_like(Q) if out is None else out
+    _need(Y, "out", 4, dt, dev)
+    if Y.shape != Q.shape:
+        raise AvqError("out must have Q's shape")
     sel = torch.empty((B, H, nt, P), dtype=torch.int32, device=dev) if want_sel else None
     imp = torch.empty((B, H, nt, M0), dtype=torch.float32, device=dev) if want_importance else None
-    _check(load_library().avq_attention_fwd(
-        _ptr(Q), _ptr(parents), _ptr(children), _ptr(pack), B, H, N, d, M0, C, P, tile,
-        float(scale), _dt(Q), _ptr(Y), _ptr(sel), _ptr(imp), _stream(dev)))
+    with _on(dev):
+        _check(load_library().avq_attention_fwd(
+            _ptr(Q), _ptr(parents), _ptr(children), _ptr(pack), B, H, N, d, M0, C, P, tile,
+            float(scale), _dt(Q), _ptr(Y), _ptr(sel), _ptr(imp), _stream(dev)))
     return Y, sel, imp
 
 
@@ -200,8 +219,12 @@ def exact_attention_fwd(Q, K, V, scale: float, out: Optional[torch.Tensor] = Non
         raise AvqError("Q, K, V must have the same shape")
     B, H, N, d = Q.shape
     Y = torch.empty_like(Q) if out is None else out
-    _check(load_library().avq_exact_attention_fwd(_ptr(Q), _ptr(K), _ptr(V), B, H, N, d, float(scale),
-                                                  _dt(Q), _ptr(Y), _stream(Q.device)))
+    _need(Y, "out", 4, Q.dtype, Q.device)
+    if Y.shape != Q.shape:
+        raise AvqError("out must have Q's shape")
+    with _on(Q.device):
+        _check(load_library().avq_exact_attention_fwd(_ptr(Q), _ptr(K), _ptr(V), B, H, N, d, float(scale),
+                                                      _dt(Q), _ptr(Y), _stream(Q.device)))
     return Y
 
 

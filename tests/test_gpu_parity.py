@@ -285,4 +285,14 @@ def test_invalid_arguments_raise(avq):
     with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
         bad = torch.zeros((1, 8, 4, 96), dtype=torch.bfloat16, device=DEV)
         avq.build_tree(bad)   # d = 96
+    # output buffers of the wrong shape or type are refused before any launch
+    with pytest.raises(avq.AvqError, match="Q's shape"):
+        avq.attention_fwd(Q, parents, ch, pack, 2, 128, inp.scale, out=Q[:, :, :128].contiguous())
+    with pytest.raises(avq.AvqError, match="dtype"):
+        avq.attention_fwd(Q, parents, ch, pack, 2, 128, inp.scale, out=Q.float())
+    vsum, count, _, pk = avq.assign_aggregate(K, V, parents, ch, sq)
+    with pytest.raises(avq.AvqError, match="do not match"):
+        avq.assign_aggregate(K, V, parents, ch, sq, out=(vsum[:, :, :-1].contiguous(), count, pk))
+    with pytest.raises(avq.AvqError, match="do not match"):
+        avq.assign_aggregate(K, V, parents, ch, sq, out=(vsum, count, pk[:-1]))
     torch.cuda.synchronize()
