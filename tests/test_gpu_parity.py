@@ -267,6 +267,21 @@ def test_constant_values_give_constant_output(avq):
         assert np.abs(tensor_to_f64(Y, "bf16") - 0.75).max() <= 4e-3
 
 
+def test_forward_equals_the_stages(avq):
+    # the one-call helper runs the same three entry points: identical bits
+    inp = synth.generate("vit-b", B=1, H=2, N=900, M0=24, C=8, P=3, T=64, seed=12)
+    _say(f"forward() vs stages: {inp.name} N={inp.N} M0={inp.M0}")
+    ch = to_dev(inp.children, inp.dtype)
+    K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
+    Y1 = avq.forward(Q, K, V, ch, inp.P, inp.T, inp.scale)
+    parents, sq = avq.build_tree(ch)
+    _, _, _, pack = avq.assign_aggregate(K, V, parents, ch, sq)
+    Y2, _, _ = avq.attention_fwd(Q, parents, ch, pack, inp.P, inp.T, inp.scale)
+    Y3 = avq.forward(Q, K, V, ch, inp.P, inp.T, inp.scale, tree=(parents, sq))
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(Y1, Y3)
+
+
 def test_invalid_arguments_raise(avq):
     _say("invalid arguments")
     inp = synth.generate("vit-b", B=1, H=1, N=256, M0=8)
