@@ -88,6 +88,7 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
     float *pn = reinterpret_cast<float *>(smem + (size_t)M0p * LDP * sizeof(T));
     unsigned char *pst = reinterpret_cast<unsigned char *>(pn + M0p);   // [kAssignChunk]
     int *hist = reinterpret_cast<int *>(pst + kAssignChunk);           // [257]
+    int *wcnt = hist + 257;                                            // [NWV][256]
 
     const int chunk = blockIdx.x, bh = blockIdx.y, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
     }
     if (tid < M0p) pn[tid] = tid < M0 ? snorm : FLT_MAX;   // padding rows never win
     for (int r = tid; r < 257; r += NT) hist[r] = 0;
+    for (int r = tid; r < NWV * 256; r += NT) wcnt[r] = 0;
     __syncthreads();
 
     // codeword fragments and norms of row block rb
@@ -221,9 +223,48 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
     }
     __syncthreads();
 
-    // counting sort of the chunk's keys by parent
+    // Stable counting sort of the chunk's keys by parent, so that a bucket
+    // lists its keys in key order and the sums the second kernel forms over
+    // it come out the same in every run.  Wave w owns keys [w*KPW, (w+1)*KPW);
+    // a key's position is its parent's bucket start, plus that parent's keys
+    // in earlier waves, plus those earlier in its own wave (same-parent lanes
+    // are matched with one ballot per bit of the parent index).
     const int nk = min(kAssignChunk, N - key0);
-    for (int x = tid; x < nk; x += NT) atomicAdd(&hist[pst[x]], 1);
+    constexpr int KPW = kAssignChunk / NWV;
+    static_assert(KPW % 64 == 0, "a wave's keys must be whole rounds of 64");
+    auto same_parent = [&](bool v, int p) {   // lanes holding a key of parent p
+        unsigned long long m = __ballot(v);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const bool set = (p >> bit) & 1;
+            const unsigned long long b = __ballot(set);
+            m &= set ? b : ~b;
+        }
+        return m;
+    };
+    constexpr int NRD = KPW / 64;
+    int *mycnt = wcnt + wave * 256;
+    int kp[NRD];
+    unsigned long long km[NRD];
+#pragma unroll
+    for (int r = 0; r < NRD; ++r) {   // this wave's count of every parent
+        const int x = wave * KPW + 64 * r + lane;
+        const bool v = x < nk;
+        kp[r] = v ? pst[x] : 0;
+        km[r] = same_parent(v, kp[r]);
+        if (v && mbcnt(km[r]) == 0) mycnt[kp[r]] += __popcll(km[r]);   // one lane per parent
+    }
+    __syncthreads();
+    for (int p = tid; p < 256; p += NT) {   // earlier waves' counts, and totals
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+            const int c = wcnt[w * 256 + p];
+            wcnt[w * 256 + p] = run;
+            run += c;
+        }
+        hist[p] = run;
+    }
     __syncthreads();
     if (wave == 0) {
         int v[4], s = 0;
@@ -256,10 +297,18 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
         seg[((int64_t)bh * ngroups + gr) * nchunks + chunk] = int2{a, b - a};
     }
     __syncthreads();
-    for (int x = tid; x < nk; x += NT) {
-        const int p = pst[x];
-        const int pos = atomicAdd(&hist[p], 1);
-        sorted[head + key0 + pos] = (int32_t)((unsigned)(key0 + x) | ((unsigned)p << 24));
+#pragma unroll
+    for (int r = 0; r < NRD; ++r) {
+        const int x = wave * KPW + 64 * r + lane;
+        const int p = kp[r];
+        const int before = mbcnt(km[r]);
+        const int pos = hist[p] + mycnt[p] + before;
+        // (every lane has read mycnt[p] before one lane per parent advances it:
+        // a wave's LDS accesses complete in order)
+        if (x < nk) {
+            if (before == 0) mycnt[p] += __popcll(km[r]);
+            sorted[head + key0 + pos] = (int32_t)((unsigned)(key0 + x) | ((unsigned)p << 24));
+        }
     }
 }
 
@@ -269,7 +318,7 @@ static hipError_t launch_assign(const void *K, const void *parents, const float 
 {
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     const size_t lds = (size_t)16 * NRB * (D + 8) * sizeof(T) + (size_t)16 * NRB * 4 +
-                       kAssignChunk + 257 * 4;
+                       kAssignChunk + 257 * 4 + (kAssignThreads / 64) * 256 * 4;
     allow_full_lds<assign_parent_kernel<T, D, NRB>>();
     hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(kAssignThreads), lds, stream,
                        (const T *)K, (const T *)parents, sqnorm, H, N, M0, C, nchunks, ws.sorted,
