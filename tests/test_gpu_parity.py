@@ -158,13 +158,15 @@ def _random_shapes(n, seed=2024):
         C = int(rng.choice([2, 4, 8, 16]))
         P = int(rng.integers(0, M0 + 1))
         T = int(rng.choice([32, 64, 128, 256]))
+        if dtype == "f32" and T == 256 and M0 > 128:
+            P = min(P, 150)   # past that, the shape does not fit in LDS
         N = int(rng.integers(1, 2500))
         B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
         out.append((dtype, d, M0, C, P, T, N, B, H, bool(rng.integers(0, 2))))
     return out
 
 
-@pytest.mark.parametrize("dtype,d,M0,C,P,T,N,B,H,force", _random_shapes(12))
+@pytest.mark.parametrize("dtype,d,M0,C,P,T,N,B,H,force", _random_shapes(40))
 def test_random_shapes(avq, dtype, d, M0, C, P, T, N, B, H, force):
     inp = synth.generate("vit-b", B=B, H=H, N=N, d=d, M0=M0, C=C, P=P, T=T, dtype=dtype,
                          seed=500 + N + M0)
