@@ -112,6 +112,15 @@ def test_workload_full_size_sampled_tiles(avq, name):
     check_all(avq, inp, tile_ranges=[(0, 1), (nt // 2, nt // 2 + 1), (nt - 1, nt)])
 
 
+def test_maximum_sequence_length(avq):
+    """N = 2^20, the largest supported: 1024 assignment chunks per head (the
+    refinement kernel's chunk table at its largest).  Stage 1 on every key,
+    stage 2 on three tiles."""
+    inp = synth.generate("long-64k", H=1, N=1 << 20)
+    nt = inp.ntiles
+    check_all(avq, inp, tile_ranges=[(0, 1), (nt // 2, nt // 2 + 1), (nt - 1, nt)])
+
+
 # ------------------------------------------------------------------ edge shapes
 
 EDGE = [
