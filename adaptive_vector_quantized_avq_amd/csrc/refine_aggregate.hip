@@ -58,8 +58,16 @@ template <typename T, int D, int CC> struct RefineCfg {
     static constexpr size_t rn_bytes = (size_t)G * BR * 4;
     static constexpr size_t vt_bytes = (size_t)NW * (D * LDK * sizeof(T) + KEYS);
     static constexpr size_t acc1_bytes = (size_t)NSB * 16 * (LDA + 1) * 4;
-    // partial-sum slices summed in parallel (one per wave) when they fit
-    static constexpr int NSL = NW * acc1_bytes + (size_t)G * BR * (LDP * sizeof(T) + 4) <= 96 * 1024 ? NW : 1;
+    // partial-sum slices in LDS (they share the region of the V tiles): one
+    // per wave, summed in parallel, when that costs no LDS beyond the V tiles
+    // or still leaves room for two work-groups per CU; else two (pairs of
+    // waves take turns); else one (the waves take turns)
+    static constexpr bool slices_fit(int n)
+    {
+        return (size_t)n * acc1_bytes <= vt_bytes ||
+               cw_bytes + rn_bytes + (size_t)n * acc1_bytes <= 76 * 1024;
+    }
+    static constexpr int NSL = slices_fit(NW) ? NW : slices_fit(2) ? 2 : 1;
     static constexpr size_t acc_bytes = NSL * acc1_bytes;
     static constexpr size_t union_bytes = vt_bytes > acc_bytes ? vt_bytes : acc_bytes;
     static size_t lds(int nchunks)
@@ -362,49 +370,45 @@ void refine_aggregate_kernel(
     float *acc = reinterpret_cast<float *>(un);     // [NSL][NSB*16][LDA], slice 0 = total
     constexpr int NSL = Cfg::NSL;
     float *cntf = acc + NSL * NSB * 16 * LDA;       // [NSL][NSB*16]
-    if constexpr (NSL == NW) {
+    // round r: waves r*NSL .. r*NSL+NSL-1 write (r = 0) or add (r > 0) their
+    // sums into slices 0..NSL-1; then the slices are summed into slice 0
+    static_assert(NW % NSL == 0, "slices must divide the waves");
+    for (int rnd = 0; rnd < NW / NSL; ++rnd) {
+        if (wave / NSL == rnd) {
+            const int sl = wave % NSL;
 #pragma unroll
-        for (int sb = 0; sb < NSB; ++sb)
+            for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * sb + 4 * g + r;
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * sb + 4 * g + r;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[(wave * NSB * 16 + row) * LDA + 16 * db + i16] = sums[sb][db][r];
-                if (i16 == 0) cntf[wave * NSB * 16 + row] = cnts[sb][r];
-            }
+                    for (int db = 0; db < NDB; ++db) {
+                        float *pa = acc + (sl * NSB * 16 + row) * LDA + 16 * db + i16;
+                        *pa = (rnd == 0 ? 0.f : *pa) + sums[sb][db][r];
+                    }
+                    if (i16 == 0) {
+                        float *pc = cntf + sl * NSB * 16 + row;
+                        *pc = (rnd == 0 ? 0.f : *pc) + cnts[sb][r];
+                    }
+                }
+        }
         __syncthreads();
+    }
+    if constexpr (NSL > 1) {
         for (int e = tid; e < NSB * 16 * D; e += NT) {
             const int row = e / D, t = e % D;
             float s = acc[row * LDA + t];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) s += acc[(w * NSB * 16 + row) * LDA + t];
+            for (int w = 1; w < NSL; ++w) s += acc[(w * NSB * 16 + row) * LDA + t];
             acc[row * LDA + t] = s;
         }
         for (int e = tid; e < NSB * 16; e += NT) {
             float s = cntf[e];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) s += cntf[w * NSB * 16 + e];
+            for (int w = 1; w < NSL; ++w) s += cntf[w * NSB * 16 + e];
             cntf[e] = s;
         }
         __syncthreads();
-    } else {
-        for (int w = 0; w < NW; ++w) {
-            if (wave == w) {
-#pragma unroll
-                for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = 16 * sb + 4 * g + r;
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-                            float *pa = acc + row * LDA + 16 * db + i16;
-                            *pa = (w == 0 ? 0.f : *pa) + sums[sb][db][r];
-                        }
-                        if (i16 == 0) cntf[row] = (w == 0 ? 0.f : cntf[row]) + cnts[sb][r];
-                    }
-            }
-            __syncthreads();
-        }
     }
 
     // ---- outputs: child slots as accumulated; parent = stayed + children
