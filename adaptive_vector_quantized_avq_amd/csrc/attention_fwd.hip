@@ -93,8 +93,13 @@ __device__ void select_top_p_regs(const float (&wv)[4], int M0, int P, int *selL
     if (P < M0) {
         for (int bit = 30; bit >= 0; --bit) {   // w >= 0: the sign bit is clear
             const unsigned cand = tau | (1u << bit);
-            const int cnt = __popcll(__ballot(u[0] >= cand)) + __popcll(__ballot(u[1] >= cand)) +
-                            __popcll(__ballot(u[2] >= cand)) + __popcll(__ballot(u[3] >= cand));
+            // (the four ballots are formed before any is counted, so that
+            // they occupy separate scalar registers and issue back to back)
+            const unsigned long long b0 = __builtin_amdgcn_ballot_w64(u[0] >= cand);
+            const unsigned long long b1 = __builtin_amdgcn_ballot_w64(u[1] >= cand);
+            const unsigned long long b2 = __builtin_amdgcn_ballot_w64(u[2] >= cand);
+            const unsigned long long b3 = __builtin_amdgcn_ballot_w64(u[3] >= cand);
+            const int cnt = (__popcll(b0) + __popcll(b1)) + (__popcll(b2) + __popcll(b3));
             if (cnt == P) {        // exactly P values >= cand: they are the top P
                 tau = cand - 1u;
                 break;
