@@ -12,10 +12,10 @@
 // partials, so two work-groups share a CU and hide each other's barrier and
 // load stalls (at d = 128 the value sums no longer fit beside a second
 // work-group's parents: bf16 keeps them in LDS with one 8-wave work-group
-// per CU, fp32 reads them from L2).  Work-groups are assigned to (head, query slice) so that
-// consecutive work-group ids, which the dispatcher spreads over the 8 XCDs,
-// give every XCD a contiguous range of heads: a head's children and value
-// sums then live in one XCD's L2.
+// per CU, fp32 reads them from L2).  Work-groups are assigned to (head,
+// query slice) so that consecutive work-group ids, which the dispatcher
+// spreads over the 8 XCDs, give every XCD a contiguous range of heads: a
+// head's children and value sums then live in one XCD's L2.
 //
 // Logits are computed transposed, S^T = C . Q^T (codewords as MFMA rows,
 // queries as columns): each lane owns one query of each block, so the row
