@@ -90,6 +90,7 @@ __device__ void select_top_p_regs(const float (&wv)[4], int M0, int P, int *selL
 #pragma unroll
     for (int i = 0; i < 4; ++i) u[i] = lane + 64 * i < M0 ? __float_as_uint(wv[i]) : 0u;
     unsigned tau = 0u;
+    bool exact = false;   // exactly P values lie above tau
     if (P < M0) {
         for (int bit = 30; bit >= 0; --bit) {   // w >= 0: the sign bit is clear
             const unsigned cand = tau | (1u << bit);
@@ -102,29 +103,45 @@ __device__ void select_top_p_regs(const float (&wv)[4], int M0, int P, int *selL
             const int cnt = (__popcll(b0) + __popcll(b1)) + (__popcll(b2) + __popcll(b3));
             if (cnt == P) {        // exactly P values >= cand: they are the top P
                 tau = cand - 1u;
+                exact = true;
                 break;
             }
             tau = cnt > P ? cand : tau;
         }
     }
-    int gt = 0;
+    int pos_base = 0;
+    if (exact) {   // the selection is the values above tau, no tie to break
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gt += __popcll(__ballot(u[i] > tau));
-    const int need = P - gt;
-    int eq_before = 0, pos_base = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const bool in = lane + 64 * i < M0;
-        const unsigned long long eqm = __ballot(in & (u[i] == tau));
-        const bool s = (u[i] > tau) | (in & (u[i] == tau) & (eq_before + mbcnt(eqm) < need));
-        eq_before += __popcll(eqm);
-        const unsigned long long sm = __ballot(s);
-        if (s) {
-            const int pos = pos_base + mbcnt(sm);
-            selL[pos] = lane + 64 * i;
-            if (sel_out) sel_out[pos] = lane + 64 * i;
+        for (int i = 0; i < 4; ++i) {
+            const bool s = u[i] > tau;
+            const unsigned long long sm = __ballot(s);
+            if (s) {
+                const int pos = pos_base + mbcnt(sm);
+                selL[pos] = lane + 64 * i;
+                if (sel_out) sel_out[pos] = lane + 64 * i;
+            }
+            pos_base += __popcll(sm);
         }
-        pos_base += __popcll(sm);
+    } else {       // values above tau, then the lowest indices equal to tau
+        int gt = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gt += __popcll(__ballot(u[i] > tau));
+        const int need = P - gt;
+        int eq_before = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool in = lane + 64 * i < M0;
+            const unsigned long long eqm = __ballot(in & (u[i] == tau));
+            const bool s = (u[i] > tau) | (in & (u[i] == tau) & (eq_before + mbcnt(eqm) < need));
+            eq_before += __popcll(eqm);
+            const unsigned long long sm = __ballot(s);
+            if (s) {
+                const int pos = pos_base + mbcnt(sm);
+                selL[pos] = lane + 64 * i;
+                if (sel_out) sel_out[pos] = lane + 64 * i;
+            }
+            pos_base += __popcll(sm);
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
