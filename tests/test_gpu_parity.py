@@ -145,6 +145,10 @@ EDGE = [
     ("bf16", 128, 129, 16, 20, 64, 777, True),
     # fp32 at d = 128 with 256-query tiles (8 waves, value sums from L2)
     ("f32", 128, 200, 4, 8, 256, 1100, False),
+    # fewer non-empty parents than P (5 keys, 40 parents, P = 12): the top-P
+    # threshold is 0 and the empty parents tie there, lowest indices first
+    ("bf16", 64, 40, 4, 12, 64, 5, False),
+    ("f32", 64, 40, 8, 12, 32, 3, False),
 ]
 
 
