@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "AvqError", "library_path", "load_library", "abi_version",
     "build_tree", "assign_aggregate", "attention_fwd", "exact_attention_fwd",
-    "assign_aggregate_workspace_size", "operand_pack_size", "forward",
+    "assign_aggregate_workspace_size", "attention_workspace_size", "forward",
     "AVQ_FLAG_FORCE_CHILD",
 ]
 
@@ -56,15 +56,14 @@ def load_library():
     lib.avq_build_tree.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.avq_assign_aggregate_workspace_size.restype = sz
     lib.avq_assign_aggregate_workspace_size.argtypes = [i32] * 6
-    lib.avq_assign_aggregate.restype = i32
-    lib.avq_operand_pack_size.restype = sz
-    lib.avq_operand_pack_size.argtypes = [i32] * 6
+    lib.avq_attention_workspace_size.restype = sz
+    lib.avq_attention_workspace_size.argtypes = [i32] * 6
     lib.avq_assign_aggregate.restype = i32
     lib.avq_assign_aggregate.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, u32,
-                                         vp, vp, vp, vp, vp, sz, vp]
+                                         vp, vp, vp, vp, sz, vp]
     lib.avq_attention_fwd.restype = i32
-    lib.avq_attention_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                      f32, i32, vp, vp, vp, vp]
+    lib.avq_attention_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                      f32, i32, vp, vp, vp, vp, sz, vp]
     lib.avq_exact_attention_fwd.restype = i32
     lib.avq_exact_attention_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
     _lib = lib
@@ -130,16 +129,24 @@ def assign_aggregate_workspace_size(B, H, N, M0, C, d) -> int:
     return int(load_library().avq_assign_aggregate_workspace_size(B, H, N, M0, C, d))
 
 
-def operand_pack_size(B, H, M0, C, d, dtype) -> int:
-    return int(load_library().avq_operand_pack_size(B, H, M0, C, d, _DTYPES[dtype]))
+def attention_workspace_size(B, H, M0, C, d, dtype) -> int:
+    return int(load_library().avq_attention_workspace_size(B, H, M0, C, d, _DTYPES[dtype]))
+
+
+def _workspace(ws, need: int, dev, name: str):
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(ws, name, 1, torch.uint8, dev)
+    if ws.numel() < need:
+        raise AvqError(f"{name} too small: {ws.numel()} < {need} bytes")
+    return ws
 
 
 def assign_aggregate(K, V, parents, children, sqnorm, force_child: bool = False,
                      want_leaf: bool = False, workspace: Optional[torch.Tensor] = None,
                      out: Optional[tuple] = None):
     """Stage 1.  K, V [B][H][N][d] -> (vsum [B][H][S_tot][d] fp32,
-    count [B][H][S_tot] int32, leaf [B][H][N] int32 or None, pack uint8: the
-    same aggregates laid out as stage-2 operands)."""
+    count [B][H][S_tot] int32, leaf [B][H][N] int32 or None)."""
     _need(K, "K", 4)
     dev, dt = K.device, K.dtype
     _need(V, "V", 4, dt, dev)
@@ -153,49 +160,48 @@ def assign_aggregate(K, V, parents, children, sqnorm, force_child: bool = False,
         raise AvqError("inconsistent shapes")
     S = M0 * (1 + C)
     lib = load_library()
-    need = int(lib.avq_assign_aggregate_workspace_size(B, H, N, M0, C, d))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, int(lib.avq_assign_aggregate_workspace_size(B, H, N, M0, C, d)),
+                           dev, "workspace")
     if out is None:
         vsum = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
         count = torch.empty((B, H, S), dtype=torch.int32, device=dev)
-        pack = torch.empty(int(lib.avq_operand_pack_size(B, H, M0, C, d, _dt(K))), dtype=torch.uint8,
-                           device=dev)
     else:
-        vsum, count, pack = out
+        vsum, count = out
         _need(vsum, "vsum", 4, torch.float32, dev)
         _need(count, "count", 3, torch.int32, dev)
-        _need(pack, "pack", 1, torch.uint8, dev)
-        if vsum.shape != (B, H, S, d) or count.shape != (B, H, S) or \
-                pack.numel() < int(lib.avq_operand_pack_size(B, H, M0, C, d, _dt(K))):
+        if vsum.shape != (B, H, S, d) or count.shape != (B, H, S):
             raise AvqError("output buffers do not match the shape")
-    _need(workspace, "workspace", 1, torch.uint8, dev)
     leaf = torch.empty((B, H, N), dtype=torch.int32, device=dev) if want_leaf else None
     with _on(dev):
         _check(lib.avq_assign_aggregate(
             _ptr(K), _ptr(V), _ptr(parents), _ptr(children), _ptr(sqnorm), B, H, N, d, M0, C, _dt(K),
-            AVQ_FLAG_FORCE_CHILD if force_child else 0, _ptr(vsum), _ptr(count), _ptr(leaf), _ptr(pack),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
-    return vsum, count, leaf, pack
+            AVQ_FLAG_FORCE_CHILD if force_child else 0, _ptr(vsum), _ptr(count), _ptr(leaf),
+            _ptr(workspace), workspace.numel(), _stream(dev)))
+    return vsum, count, leaf
 
 
-def attention_fwd(Q, parents, children, pack, P: int, tile: int, scale: float,
+def attention_fwd(Q, parents, children, vsum, count, P: int, tile: int, scale: float,
                   want_sel: bool = False, want_importance: bool = False,
-                  out: Optional[torch.Tensor] = None):
-    """Stage 2.  Q [B][H][N][d] and the operand pack of stage 1 ->
-    (Y [B][H][N][d], sel [B][H][ntiles][P] or None,
-    importance [B][H][ntiles][M0] or None)."""
+                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Stage 2.  Q [B][H][N][d] and the aggregates vsum [B][H][S_tot][d] fp32,
+    count [B][H][S_tot] int32 -> (Y [B][H][N][d], sel [B][H][ntiles][P] or
+    None, importance [B][H][ntiles][M0] or None)."""
     _need(Q, "Q", 4)
     dev, dt = Q.device, Q.dtype
     _need(children, "children", 4, dt, dev)
     _need(parents, "parents", 3, dt, dev)
-    _need(pack, "pack", 1, torch.uint8, dev)
+    _need(vsum, "vsum", 4, torch.float32, dev)
+    _need(count, "count", 3, torch.int32, dev)
     B, H, N, d = Q.shape
     M0, C = children.shape[1], children.shape[2]
+    S = M0 * (1 + C)
     if parents.shape != (H, M0, d) or children.shape[0] != H or children.shape[3] != d:
         raise AvqError("inconsistent shapes")
-    if pack.numel() < int(load_library().avq_operand_pack_size(B, H, M0, C, d, _dt(Q))):
-        raise AvqError("operand pack too small for this shape")
+    if vsum.shape != (B, H, S, d) or count.shape != (B, H, S):
+        raise AvqError("vsum / count do not match the shape")
+    lib = load_library()
+    workspace = _workspace(workspace, int(lib.avq_attention_workspace_size(B, H, M0, C, d, _dt(Q))),
+                           dev, "workspace")
     nt = -(-N // tile) if tile > 0 else 0
     Y = torch.empty_like(Q) if out is None else out
     _need(Y, "out", 4, dt, dev)
@@ -204,9 +210,10 @@ def attention_fwd(Q, parents, children, pack, P: int, tile: int, scale: float,
     sel = torch.empty((B, H, nt, P), dtype=torch.int32, device=dev) if want_sel else None
     imp = torch.empty((B, H, nt, M0), dtype=torch.float32, device=dev) if want_importance else None
     with _on(dev):
-        _check(load_library().avq_attention_fwd(
-            _ptr(Q), _ptr(parents), _ptr(children), _ptr(pack), B, H, N, d, M0, C, P, tile,
-            float(scale), _dt(Q), _ptr(Y), _ptr(sel), _ptr(imp), _stream(dev)))
+        _check(lib.avq_attention_fwd(
+            _ptr(Q), _ptr(parents), _ptr(children), _ptr(vsum), _ptr(count), B, H, N, d, M0, C, P,
+            tile, float(scale), _dt(Q), _ptr(Y), _ptr(sel), _ptr(imp), _ptr(workspace),
+            workspace.numel(), _stream(dev)))
     return Y, sel, imp
 
 
@@ -232,6 +239,6 @@ def forward(Q, K, V, children, P: int, tile: int, scale: float, tree=None, force
     """Whole AVQ-Attention forward: build (or reuse) the tree, stage 1,
     stage 2.  Returns Y."""
     parents, sqnorm = tree if tree is not None else build_tree(children)
-    _, _, _, pack = assign_aggregate(K, V, parents, children, sqnorm, force_child=force_child)
-    Y, _, _ = attention_fwd(Q, parents, children, pack, P, tile, scale)
+    vsum, count, _ = assign_aggregate(K, V, parents, children, sqnorm, force_child=force_child)
+    Y, _, _ = attention_fwd(Q, parents, children, vsum, count, P, tile, scale)
     return Y

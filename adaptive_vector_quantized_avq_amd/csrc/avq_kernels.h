@@ -46,9 +46,10 @@ struct AssignWorkspace {
     size_t bytes;
 };
 
-// Aggregates rearranged as stage-2 MFMA operands (written by stage 1 next to
-// the fp32 value sums).  Per (b, h), byte offsets into one block of
-// `bytes` bytes, element type T (the input dtype):
+// Aggregates rearranged as stage-2 MFMA operands (written into the stage-2
+// workspace from the caller's fp32 value sums and int32 counts by
+// pack_aggregates.hip).  Per (b, h), byte offsets into one block of `bytes`
+// bytes, element type T (the input dtype):
 //   pvt [D][M0p]  T      parent value sums, transposed; column of parent j
 //                        at (j & ~31) + perm32(j & 31), zero for j >= M0
 //   pn  [M0p]     float  parent counts (zero for j >= M0)
@@ -94,8 +95,12 @@ hipError_t launch_assign_parent(const void *K, const void *parents, const float 
 hipError_t launch_assign_aggregate(const void *K, const void *V, const void *parents,
                                    const void *children, const float *sqnorm, int B, int H, int N,
                                    int d, int M0, int C, int dtype, unsigned flags, float *vsum,
-                                   int32_t *count, int32_t *leaf, void *pack,
-                                   const AssignWorkspace &ws, hipStream_t stream);
+                                   int32_t *count, int32_t *leaf, const AssignWorkspace &ws,
+                                   hipStream_t stream);
+
+// stage-2 operand pack (PackLayout, B*H blocks) from fp32 sums and int32 counts
+hipError_t launch_pack_aggregates(const float *vsum, const int32_t *count, int B, int H, int d, int M0, int C,
+                                  int dtype, void *pack, hipStream_t stream);
 
 // returns hipErrorInvalidConfiguration when the shape does not fit the
 // kernel's on-chip budget

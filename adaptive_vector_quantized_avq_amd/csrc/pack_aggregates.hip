@@ -1,0 +1,146 @@
+// Stage 2 input preparation: the caller's fp32 value sums and int32 counts
+// ("AVQ-Attention", Sec. 4.3: the numerator sums Vbar and the denominator
+// counts n of every codeword) rearranged as the attention kernel's
+// matrix-core operands (PackLayout in avq_kernels.h), in the call's
+// workspace.  Pure data movement plus one rounding of each value sum to the
+// input dtype; it runs at the start of every avq_attention_fwd call, so
+// stage 2 reads only what the caller hands it.
+//
+// One item per thread, so that every thread issues its loads at once and
+// the kernel costs a single memory round trip.  Items of one (b, h), in
+// order:
+//   pvt  item (t, q8): 8 consecutive operand columns 8*q8.. of dimension t;
+//        column 32*b + perm32(rho) holds parent 32*b + rho (zero past M0).
+//        Threads with consecutive t read consecutive sums (coalesced);
+//   cvt  item (p, t, group of 8 children): the children's sums of dimension
+//        t, children innermost; entry M0 is all zero;
+//   pn   parent counts as fp32 (zero past M0);
+//   cn   child counts as fp32; entry M0 is all zero.
+// The grid is 1-D, with the (b, h) units spread over the XCDs in contiguous
+// ranges the way the attention kernel spreads them, so that a head's operands
+// are written from the XCD whose L2 then reads them.
+#include "avq_kernels.h"
+
+namespace avq {
+
+constexpr int kPackThreads = 256;
+
+template <typename T> __device__ __forceinline__ void store8(T *dst, const float (&v)[8]);
+template <> __device__ __forceinline__ void store8<bf16>(bf16 *dst, const float (&v)[8])
+{
+    bf16x8 o;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = (bf16)v[k];
+    *reinterpret_cast<bf16x8 *>(dst) = o;
+}
+template <> __device__ __forceinline__ void store8<float>(float *dst, const float (&v)[8])
+{
+    *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+template <int D, int CC> __host__ __device__ inline int pack_items(int M0)
+{
+    const int NG = CC >= 8 ? CC / 8 : 1;
+    return D * (padded_parents(M0) / 8) + (CC > 0 ? (M0 + 1) * D * NG : 0) + padded_parents(M0) +
+           (M0 + 1) * CC;
+}
+
+template <typename T, int D, int CC>
+__global__ __launch_bounds__(kPackThreads) void pack_aggregates_kernel(
+    const float *__restrict__ vsum, const int32_t *__restrict__ count, int M0, int nbh, int parts,
+    unsigned char *__restrict__ pack)
+{
+    const int G8 = gridDim.x >> 3;
+    const int unit = (blockIdx.x & 7) * G8 + (blockIdx.x >> 3);
+    const int bh = unit / parts, part = unit - bh * parts;
+    if (bh >= nbh) return;
+    const int M0p = padded_parents(M0);
+    const int S = M0 * (1 + CC);
+    const PackLayout PL = pack_layout(M0, CC, D, (int)sizeof(T));
+    unsigned char *pk = pack + (size_t)bh * PL.bytes;
+    const float *vs = vsum + (size_t)bh * S * D;
+    const int32_t *cs = count + (size_t)bh * S;
+    int a = part * kPackThreads + threadIdx.x;
+
+    // parent value sums, transposed, columns permuted within 32-blocks
+    const int n_pvt = D * (M0p / 8);
+    if (a < n_pvt) {
+        const int t = a % D, q8 = a / D;
+        const int base = 32 * (q8 >> 2), q = q8 & 3;
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int j = base + (k < 4 ? 4 * q + k : 16 + 4 * q + (k - 4));
+            v[k] = j < M0 ? vs[(size_t)j * D + t] : 0.f;
+        }
+        store8<T>(reinterpret_cast<T *>(pk + PL.pvt) + (size_t)t * M0p + 8 * q8, v);
+        return;
+    }
+    a -= n_pvt;
+    if constexpr (CC > 0) {
+        constexpr int CG = CC >= 8 ? 8 : CC;   // children per item
+        constexpr int NG = CC / CG;
+        const int n_cvt = (M0 + 1) * D * NG;
+        if (a < n_cvt) {
+            const int t = a % D, r = a / D, cg = r % NG, p = r / NG;
+            T *dst = reinterpret_cast<T *>(pk + PL.cvt) + ((size_t)p * D + t) * CC + CG * cg;
+            if constexpr (CG == 8) {
+                float v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    v[k] = p < M0 ? vs[((size_t)M0 + (size_t)p * CC + 8 * cg + k) * D + t] : 0.f;
+                store8<T>(dst, v);
+            } else {
+#pragma unroll
+                for (int k = 0; k < CG; ++k)
+                    dst[k] = from_float<T>(p < M0 ? vs[((size_t)M0 + (size_t)p * CC + k) * D + t] : 0.f);
+            }
+            return;
+        }
+        a -= n_cvt;
+    }
+    if (a < M0p) {
+        reinterpret_cast<float *>(pk + PL.pn)[a] = a < M0 ? (float)cs[a] : 0.f;
+        return;
+    }
+    a -= M0p;
+    if (a < (M0 + 1) * CC)
+        reinterpret_cast<float *>(pk + PL.cn)[a] = a < M0 * CC ? (float)cs[M0 + a] : 0.f;
+}
+
+template <typename T, int D, int CC>
+static hipError_t launch_pack_k(const float *vsum, const int32_t *count, int BH, int M0, void *pack,
+                                hipStream_t stream)
+{
+    const int parts = (pack_items<D, CC>(M0) + kPackThreads - 1) / kPackThreads;
+    const int grid = (BH * parts + 7) & ~7;
+    hipLaunchKernelGGL((pack_aggregates_kernel<T, D, CC>), dim3(grid), dim3(kPackThreads), 0, stream, vsum,
+                       count, M0, BH, parts, (unsigned char *)pack);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_pack_t(const float *vsum, const int32_t *count, int BH, int M0, int C, void *pack,
+                                hipStream_t stream)
+{
+    switch (C) {
+    case 0: return launch_pack_k<T, D, 0>(vsum, count, BH, M0, pack, stream);
+    case 2: return launch_pack_k<T, D, 2>(vsum, count, BH, M0, pack, stream);
+    case 4: return launch_pack_k<T, D, 4>(vsum, count, BH, M0, pack, stream);
+    case 8: return launch_pack_k<T, D, 8>(vsum, count, BH, M0, pack, stream);
+    default: return launch_pack_k<T, D, 16>(vsum, count, BH, M0, pack, stream);
+    }
+}
+
+hipError_t launch_pack_aggregates(const float *vsum, const int32_t *count, int B, int H, int d, int M0, int C,
+                                  int dtype, void *pack, hipStream_t stream)
+{
+    if (dtype == 1)
+        return d == 64 ? launch_pack_t<bf16, 64>(vsum, count, B * H, M0, C, pack, stream)
+                       : launch_pack_t<bf16, 128>(vsum, count, B * H, M0, C, pack, stream);
+    return d == 64 ? launch_pack_t<float, 64>(vsum, count, B * H, M0, C, pack, stream)
+                   : launch_pack_t<float, 128>(vsum, count, B * H, M0, C, pack, stream);
+}
+
+}  // namespace avq

@@ -5,8 +5,7 @@
 // than the parent.  Value sums and counts are accumulated at both levels: a
 // parent slot covers its whole cell, a child slot the keys that moved to it.
 // One work-group owns a group of parents and writes every output slot of
-// those parents exactly once (no global atomics, no pre-zeroing); it also
-// writes the same aggregates as the stage-2 operand pack.
+// those parents exactly once (no global atomics, no pre-zeroing).
 #include "avq_kernels.h"
 
 namespace avq {
@@ -134,7 +133,7 @@ void refine_aggregate_kernel(
     const T *__restrict__ children, const float *__restrict__ sqnorm, int H, int N, int M0,
     int nchunks, int force_child, const int32_t *__restrict__ sorted,
     const int2 *__restrict__ seg, float *__restrict__ vsum, int32_t *__restrict__ count,
-    int32_t *__restrict__ leaf, unsigned char *__restrict__ pack)
+    int32_t *__restrict__ leaf)
 {
     using Cfg = RefineCfg<T, D, CC>;
     constexpr int G = Cfg::G, NW = Cfg::NW, BR = Cfg::BR, BRB = Cfg::BRB, NRB = Cfg::NRB;
@@ -432,50 +431,13 @@ void refine_aggregate_kernel(
         for (int c = 0; c <= CC; ++c) s += cntf[lp * (CC + 1) + c];
         cs[p0 + lp] = (int)s;
     }
-
-    // ---- the same aggregates as stage-2 operands (layout in PackLayout)
-    const PackLayout PL = pack_layout(M0, CC, D, (int)sizeof(T));
-    const int M0p = padded_parents(M0);
-    unsigned char *pk = pack + (size_t)bh * PL.bytes;
-    T *pvt = reinterpret_cast<T *>(pk + PL.pvt);
-    float *pnp = reinterpret_cast<float *>(pk + PL.pn);
-    T *cvt = reinterpret_cast<T *>(pk + PL.cvt);
-    float *cnp = reinterpret_cast<float *>(pk + PL.cn);
-    for (int e = tid; e < G * D; e += NT) {
-        const int lp = e % G, t = e / G, j = p0 + lp;
-        if (lp >= Gv) continue;
-        float s = acc[(lp * (CC + 1) + CC) * LDA + t];
-#pragma unroll
-        for (int c = 0; c < CC; ++c) s += acc[(lp * (CC + 1) + c) * LDA + t];
-        store_elem(pvt + (size_t)t * M0p + (j & ~31) + perm32(j & 31), s);
-    }
-    for (int lp = tid; lp < Gv; lp += NT) {
-        float s = 0.f;
-#pragma unroll
-        for (int c = 0; c <= CC; ++c) s += cntf[lp * (CC + 1) + c];
-        pnp[p0 + lp] = s;
-    }
-    for (int e = tid; e < Gv * D * CC; e += NT) {
-        const int lp = e / (D * CC), rem = e % (D * CC), t = rem / CC, c = rem % CC;
-        store_elem(cvt + ((size_t)(p0 + lp) * D + t) * CC + c, acc[(lp * (CC + 1) + c) * LDA + t]);
-    }
-    for (int e = tid; e < Gv * CC; e += NT) cnp[(size_t)p0 * CC + e] = cntf[(e / CC) * (CC + 1) + e % CC];
-    if (p0 + Gv == M0) {   // padding columns of the parent operands, zero child entry M0
-        for (int e = tid; e < (M0p - M0) * D; e += NT) {
-            const int j = M0 + e / D, t = e % D;
-            store_elem(pvt + (size_t)t * M0p + (j & ~31) + perm32(j & 31), 0.f);
-        }
-        for (int j = M0 + tid; j < M0p; j += NT) pnp[j] = 0.f;
-        for (int e = tid; e < D * CC; e += NT) store_elem(cvt + (size_t)M0 * D * CC + e, 0.f);
-        for (int e = tid; e < CC; e += NT) cnp[(size_t)M0 * CC + e] = 0.f;
-    }
 }
 
 template <typename T, int D, int CC>
 static hipError_t launch_refine(const void *K, const void *V, const void *parents,
                                 const void *children, const float *sqnorm, int B, int H, int N,
                                 int M0, unsigned flags, float *vsum, int32_t *count, int32_t *leaf,
-                                void *pack, const AssignWorkspace &ws, hipStream_t stream)
+                                const AssignWorkspace &ws, hipStream_t stream)
 {
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     const size_t lds = RefineCfg<T, D, CC>::lds(nchunks);
@@ -484,18 +446,18 @@ static hipError_t launch_refine(const void *K, const void *V, const void *parent
     hipLaunchKernelGGL((refine_aggregate_kernel<T, D, CC>), dim3(ngroups, B * H), dim3(kRefineThreads),
                        lds, stream, (const T *)K, (const T *)V, (const T *)parents,
                        (const T *)children, sqnorm, H, N, M0, nchunks, (flags & 1u) ? 1 : 0,
-                       ws.sorted, ws.seg, vsum, count, leaf, (unsigned char *)pack);
+                       ws.sorted, ws.seg, vsum, count, leaf);
     return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_refine_t(const void *K, const void *V, const void *parents, const void *children,
                                   const float *sqnorm, int B, int H, int N, int M0, int C, unsigned flags,
-                                  float *vsum, int32_t *count, int32_t *leaf, void *pack,
+                                  float *vsum, int32_t *count, int32_t *leaf,
                                   const AssignWorkspace &ws, hipStream_t stream)
 {
 #define AVQ_REFINE(CCV) \
-    launch_refine<T, D, CCV>(K, V, parents, children, sqnorm, B, H, N, M0, flags, vsum, count, leaf, pack, ws, stream)
+    launch_refine<T, D, CCV>(K, V, parents, children, sqnorm, B, H, N, M0, flags, vsum, count, leaf, ws, stream)
     switch (C) {
     case 2: return AVQ_REFINE(2);
     case 4: return AVQ_REFINE(4);
@@ -508,19 +470,19 @@ static hipError_t launch_refine_t(const void *K, const void *V, const void *pare
 hipError_t launch_assign_aggregate(const void *K, const void *V, const void *parents,
                                    const void *children, const float *sqnorm, int B, int H, int N,
                                    int d, int M0, int C, int dtype, unsigned flags, float *vsum,
-                                   int32_t *count, int32_t *leaf, void *pack,
-                                   const AssignWorkspace &ws, hipStream_t stream)
+                                   int32_t *count, int32_t *leaf, const AssignWorkspace &ws,
+                                   hipStream_t stream)
 {
     hipError_t err = launch_assign_parent(K, parents, sqnorm, B, H, N, d, M0, C, dtype, ws, stream);
     if (err != hipSuccess) return err;
     if (dtype == 1) {
         if (d == 64)
-            return launch_refine_t<bf16, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
-        return launch_refine_t<bf16, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
+            return launch_refine_t<bf16, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
+        return launch_refine_t<bf16, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
     }
     if (d == 64)
-        return launch_refine_t<float, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
-    return launch_refine_t<float, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, pack, ws, stream);
+        return launch_refine_t<float, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
+    return launch_refine_t<float, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
 }
 
 }  // namespace avq

@@ -159,20 +159,20 @@ def main():
     B, H, N, d, S = inp.B, inp.H, inp.N, inp.d, inp.S_tot
     vsum = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
     count = torch.empty((B, H, S), dtype=torch.int32, device=dev)
-    pack = torch.empty(avq.operand_pack_size(B, H, inp.M0, inp.C, d, sets[0][0].dtype),
-                       dtype=torch.uint8, device=dev)
-    ws = torch.empty(avq.assign_aggregate_workspace_size(B, H, N, inp.M0, inp.C, d),
-                     dtype=torch.uint8, device=dev)
+    ws1 = torch.empty(avq.assign_aggregate_workspace_size(B, H, N, inp.M0, inp.C, d),
+                      dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(avq.attention_workspace_size(B, H, inp.M0, inp.C, d, sets[0][0].dtype),
+                      dtype=torch.uint8, device=dev)
     Y = torch.empty_like(sets[0][0])
 
     def step(i, ev=None):
         Q, K, V = sets[i % len(sets)]
         if ev is not None:
             ev[0].record()
-        avq.assign_aggregate(K, V, parents, ch, sq, workspace=ws, out=(vsum, count, pack))
+        avq.assign_aggregate(K, V, parents, ch, sq, workspace=ws1, out=(vsum, count))
         if ev is not None:
             ev[1].record()
-        avq.attention_fwd(Q, parents, ch, pack, P, inp.T, inp.scale, out=Y)
+        avq.attention_fwd(Q, parents, ch, vsum, count, P, inp.T, inp.scale, workspace=ws2, out=Y)
         if ev is not None:
             ev[2].record()
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define AVQ_ABI_VERSION 1
+#define AVQ_ABI_VERSION 2
 
 enum avq_status {
     AVQ_OK = 0,
@@ -87,16 +87,10 @@ int avq_build_tree(const void *children, int H, int M0, int C, int d, int dtype,
 
 /*
  * avq_assign_aggregate_workspace_size -- bytes of device workspace that
- * avq_assign_aggregate needs for this shape (0 if the shape is invalid).
+ * avq_assign_aggregate needs for this shape (0 if the shape is invalid or
+ * unsupported).
  */
 size_t avq_assign_aggregate_workspace_size(int B, int H, int N, int M0, int C, int d);
-
-/*
- * avq_operand_pack_size -- bytes of the operand pack written by
- * avq_assign_aggregate and read by avq_attention_fwd (0 if the shape is
- * invalid).
- */
-size_t avq_operand_pack_size(int B, int H, int M0, int C, int d, int dtype);
 
 /*
  * avq_assign_aggregate -- stage 1, full-tree assignment and aggregation.
@@ -116,22 +110,32 @@ size_t avq_operand_pack_size(int B, int H, int M0, int C, int d, int dtype);
  *   count_out  [B][H][S_tot]  int32   output key counts (every slot written)
  *   leaf_out   [B][H][N]      int32   optional (NULL = not written): slot of
  *                                     each key's leaf (p*, or M0+p*C+c*)
- *   pack_out   avq_operand_pack_size(...) bytes, 256-byte aligned: the same
- *              value sums (rounded to dtype) and counts (as fp32) laid out
- *              as the MFMA operands of avq_attention_fwd; its layout is
- *              private to the library and only that call reads it.
  *   workspace  device buffer of at least
  *              avq_assign_aggregate_workspace_size(...) bytes, 256-byte
  *              aligned, used only during this call's kernels (it must not
- *              be shared with a concurrent call).
- *   The order in which fp32 value sums are accumulated is not specified.
+ *              be shared with a concurrent call).  The caller owns it.
+ *   The fp32 value sums are accumulated in an order that depends only on
+ *   the inputs: repeated calls give identical bits.
+ *   Sums and counts are additive over keys: running this call on disjoint
+ *   key subsets of the same heads and adding the outputs gives the
+ *   aggregates of the union (up to fp32 summation order), which is what a
+ *   sequence split over several devices would all-reduce.
  */
 int avq_assign_aggregate(const void *K, const void *V, const void *parents,
                          const void *children, const float *sqnorm,
                          int B, int H, int N, int d, int M0, int C, int dtype,
                          unsigned flags, float *vsum_out, int32_t *count_out,
-                         int32_t *leaf_out, void *pack_out, void *workspace,
-                         size_t workspace_bytes, void *stream);
+                         int32_t *leaf_out, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * avq_attention_workspace_size -- bytes of device workspace that
+ * avq_attention_fwd needs for this shape (0 if the shape is invalid or
+ * unsupported).  The workspace receives the aggregates rearranged as the
+ * attention kernel's matrix-core operands (value sums rounded to dtype,
+ * counts as fp32); its layout is private to the library.
+ */
+size_t avq_attention_workspace_size(int B, int H, int M0, int C, int d, int dtype);
 
 /*
  * avq_attention_fwd -- stage 2, query-tile adaptive attention.
@@ -154,8 +158,14 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents,
  *   Q          [B][H][N][d]   dtype
  *   parents    [H][M0][d]     dtype   from avq_build_tree
  *   children   [H][M0][C][d]  dtype
- *   pack       operand pack written by avq_assign_aggregate for these
- *              B, H, M0, C, d, dtype: the value sums Vbar and counts n
+ *   vsum       [B][H][S_tot][d] fp32  value sums Vbar (slot layout of
+ *                                     avq_assign_aggregate)
+ *   count      [B][H][S_tot]  int32   key counts n (every count row must sum
+ *                                     to at least one key; a parent's count
+ *                                     must include its children's)
+ *   The aggregates may come from avq_assign_aggregate or from anywhere else
+ *   (e.g. the sum of several partial runs); they are read, never written.
+ *   The value sums enter the matrix-core products rounded to dtype.
  *   P          0 <= P <= M0 parents refined per tile
  *   tile       queries per tile
  *   scale      finite softmax scale applied to every logit
@@ -163,15 +173,18 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents,
  *   sel_out    [B][H][ceil(N/tile)][P] int32, optional: selected parents of
  *              every tile in ascending index order
  *   importance_out [B][H][ceil(N/tile)][M0] fp32, optional: w_j(I)
- *   Requires at least one key per (b, h) (every count row sums to N >= 1).
+ *   workspace  device buffer of at least avq_attention_workspace_size(...)
+ *              bytes, 256-byte aligned, used only during this call's
+ *              kernels (not shared with a concurrent call); caller-owned.
  *   Returns AVQ_ERR_UNSUPPORTED if the codebook and tile do not fit the
  *   kernel's 160 KB of LDS: only fp32 with M0 near 256, 256-query tiles and
  *   P above ~160 (d = 64) or ~224 (d = 128).
  */
 int avq_attention_fwd(const void *Q, const void *parents, const void *children,
-                      const void *pack, int B, int H, int N, int d, int M0, int C,
-                      int P, int tile, float scale, int dtype, void *Y_out,
-                      int32_t *sel_out, float *importance_out, void *stream);
+                      const float *vsum, const int32_t *count, int B, int H, int N,
+                      int d, int M0, int C, int P, int tile, float scale, int dtype,
+                      void *Y_out, int32_t *sel_out, float *importance_out,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * avq_exact_attention_fwd -- exact softmax attention, non-causal

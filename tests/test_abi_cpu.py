@@ -39,15 +39,15 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.avq_abi_version() == 1
+    assert lib.avq_abi_version() == 2
     assert lib.avq_status_string(0) == b"AVQ_OK"
     assert lib.avq_status_string(-1) == b"AVQ_ERR_INVALID_ARG"
     assert lib.avq_status_string(-2) == b"AVQ_ERR_UNSUPPORTED"
     assert lib.avq_status_string(-3) == b"AVQ_ERR_HIP"
 
 
-def test_operand_pack_size(lib):
-    f = lib.avq_operand_pack_size
+def test_attention_workspace_size(lib):
+    f = lib.avq_attention_workspace_size
     # per (b,h): parent sums [d][256] + counts [256] + child sums [257][d][8] +
     # counts [257][8] (one all-zero entry), each section 256-byte aligned
     al = lambda x: (x + 255) // 256 * 256
@@ -79,16 +79,22 @@ def test_invalid_arguments_are_rejected_before_launch(lib):
     import adaptive_vector_quantized_avq_amd  # noqa: F401  (sets argtypes)
     p = _fake()
     af = lib.avq_attention_fwd
-    args = dict(Q=p, par=p, ch=p, pk=p, B=1, H=1, N=128, d=64, M0=16, C=4, P=4, tile=64,
-                scale=0.125, dt=1)
+    args = dict(Q=p, par=p, ch=p, vs=p, cn=p, B=1, H=1, N=128, d=64, M0=16, C=4, P=4, tile=64,
+                scale=0.125, dt=1, ws=p, wsb=1 << 20)
 
     def call(**kw):
         a = dict(args, **kw)
-        return af(a["Q"], a["par"], a["ch"], a["pk"], a["B"], a["H"], a["N"], a["d"],
-                  a["M0"], a["C"], a["P"], a["tile"], a["scale"], a["dt"], p, None, None, None)
+        return af(a["Q"], a["par"], a["ch"], a["vs"], a["cn"], a["B"], a["H"], a["N"], a["d"],
+                  a["M0"], a["C"], a["P"], a["tile"], a["scale"], a["dt"], p, None, None,
+                  a["ws"], a["wsb"], None)
 
     assert call(Q=None) == -1
-    assert call(pk=None) == -1
+    assert call(vs=None) == -1
+    assert call(cn=None) == -1
+    assert call(ws=None) == -1
+    assert call(wsb=64) == -1
+    assert b"workspace" in lib.avq_last_error()
+    assert call(ws=ctypes.c_void_p(0x1010)) == -1
     assert call(tile=16) == -2
     assert call(P=17) == -1
     assert call(P=-1) == -1
@@ -111,18 +117,18 @@ def test_invalid_arguments_are_rejected_before_launch(lib):
 
     aa = lib.avq_assign_aggregate
     # a valid call template; each case below breaks exactly one argument
-    base = [p, p, p, p, p, 1, 1, 128, 64, 16, 4, 1, 0, p, p, None, p, p, 1 << 20, None]
+    base = [p, p, p, p, p, 1, 1, 128, 64, 16, 4, 1, 0, p, p, None, p, 1 << 20, None]
     bad_flags = list(base)
     bad_flags[12] = 2
     assert aa(*bad_flags) == -1
-    no_pack = list(base)
-    no_pack[16] = None
-    assert aa(*no_pack) == -1
+    no_ws = list(base)
+    no_ws[16] = None
+    assert aa(*no_ws) == -1
     small_ws = list(base)
-    small_ws[18] = 16
+    small_ws[17] = 16
     assert aa(*small_ws) == -1
     misaligned = list(base)
-    misaligned[17] = ctypes.c_void_p(0x1004)
+    misaligned[16] = ctypes.c_void_p(0x1004)
     assert aa(*misaligned) == -1
     assert lib.avq_build_tree(None, 1, 4, 4, 64, 1, p, p, None) == -1
     assert lib.avq_build_tree(p, 1, 4, 4, 64, 5, p, p, None) == -1

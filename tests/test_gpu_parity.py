@@ -45,9 +45,9 @@ def run_gpu(avq, inp, P, T, force_child=False):
     ch = to_dev(inp.children, inp.dtype)
     K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
     parents, sq = avq.build_tree(ch)
-    vsum, count, leaf, pack = avq.assign_aggregate(K, V, parents, ch, sq, force_child=force_child,
-                                                   want_leaf=True)
-    Y, sel, imp = avq.attention_fwd(Q, parents, ch, pack, P, T, inp.scale,
+    vsum, count, leaf = avq.assign_aggregate(K, V, parents, ch, sq, force_child=force_child,
+                                             want_leaf=True)
+    Y, sel, imp = avq.attention_fwd(Q, parents, ch, vsum, count, P, T, inp.scale,
                                     want_sel=True, want_importance=True)
     torch.cuda.synchronize()
     return dict(parents=tensor_to_f64(parents, inp.dtype), sqnorm=sq.cpu().numpy(),
@@ -56,9 +56,24 @@ def run_gpu(avq, inp, P, T, force_child=False):
                 sel=sel.cpu().numpy(), imp=imp.cpu().numpy().astype(np.float64))
 
 
-def check_all(avq, inp, P=None, T=None, force_child=False, tile_ranges=None):
+def check_stage2(inp, par64, vsum, count, g, P, T):
+    """Stage 2 of the GPU run `g` against the oracle on every query tile,
+    using the oracle's own aggregates; returns (max |dY|, ambiguous tiles)."""
+    Q64, ch64 = inp.f64("Q"), inp.f64("children")
+    Yn, w, sel = oracle.attention(Q64, par64, ch64, vsum, count, P, T, inp.scale)
+    namb = check_selection(w, sel, g["sel"], P)
+    np.testing.assert_allclose(g["imp"], w, rtol=2e-4, atol=1e-7 * T)
+    same = (np.sort(g["sel"], axis=-1) == np.sort(sel, axis=-1)).all()
+    # where every tile selected the same set, the oracle's own run is the
+    # reference; otherwise it is re-run with the GPU's selections
+    Yf = Yn if same else oracle.attention(Q64, par64, ch64, vsum, count, P, T, inp.scale,
+                                          forced_sel=g["sel"])[0]
+    return float(np.abs(g["Y"] - Yf).max()), namb
+
+
+def check_all(avq, inp, P=None, T=None, force_child=False):
     """Run the whole forward on the GPU once, check stage 1 on every key and
-    stage 2 on the given query-tile ranges (default: every tile)."""
+    stage 2 on every query tile."""
     P = inp.P if P is None else P
     T = inp.T if T is None else T
     _say(f"{inp.name} dtype={inp.dtype} B={inp.B} H={inp.H} N={inp.N} d={inp.d} M0={inp.M0} "
@@ -69,18 +84,7 @@ def check_all(avq, inp, P=None, T=None, force_child=False, tile_ranges=None):
     np.testing.assert_array_equal(g["parents"], par64)
     np.testing.assert_array_equal(g["sqnorm"], sq64.astype(np.float32))
     a, vsum, count = check_stage1(inp, par64, g["leaf"], g["vsum"], g["count"], force_child)
-    Q64 = inp.f64("Q")
-    nt = -(-inp.N // T)
-    errs, namb = [], 0
-    for (t0, t1) in (tile_ranges or [(0, nt)]):
-        _, w, sel = oracle.attention(Q64, par64, ch64, vsum, count, P, T, inp.scale, tiles=(t0, t1))
-        namb += check_selection(w[:, :, t0:t1], sel[:, :, t0:t1], g["sel"][:, :, t0:t1], P)
-        np.testing.assert_allclose(g["imp"][:, :, t0:t1], w[:, :, t0:t1], rtol=2e-4, atol=1e-7 * T)
-        Yf, _, _ = oracle.attention(Q64, par64, ch64, vsum, count, P, T, inp.scale,
-                                    forced_sel=g["sel"], tiles=(t0, t1))
-        rows = slice(t0 * T, min(inp.N, t1 * T))
-        errs.append(float(np.abs(g["Y"][:, :, rows] - Yf[:, :, rows]).max()))
-    err = max(errs)
+    err, namb = check_stage2(inp, par64, vsum, count, g, P, T)
     _say(f"  max|dY|={err:.3e} ambiguous keys={a['n_ambiguous']} tiles={namb} "
          f"residual keys={int(count[..., :inp.M0].sum() - count[..., inp.M0:].sum())}")
     assert err <= Y_TOL[inp.dtype], err
@@ -104,21 +108,53 @@ def test_seg_zipf_P_sweep(avq, P):
 
 
 @pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
-def test_workload_full_size_sampled_tiles(avq, name):
-    """Full size of every workload; stage 1 checked on every key, stage 2
-    on the first, a middle and the last query tile of every (b, h)."""
-    inp = synth.generate(name)
-    nt = inp.ntiles
-    check_all(avq, inp, tile_ranges=[(0, 1), (nt // 2, nt // 2 + 1), (nt - 1, nt)])
+def test_workload_full_size(avq, name):
+    """Full size of every workload: stage 1 on every key, stage 2 on every
+    query tile of every (b, h)."""
+    check_all(avq, synth.generate(name))
+
+
+@pytest.mark.parametrize("P", [0, 4, 128])
+def test_seg_zipf_P_sweep_full_size(avq, P):
+    """The seg-zipf P sweep at its own shape (B=2, H=16, N=16384, M0=128);
+    P = 16 is the workload's default, run above."""
+    check_all(avq, synth.generate("seg-zipf"), P=P)
 
 
 def test_maximum_sequence_length(avq):
     """N = 2^20, the largest supported: 1024 assignment chunks per head (the
-    refinement kernel's chunk table at its largest).  Stage 1 on every key,
-    stage 2 on three tiles."""
-    inp = synth.generate("long-64k", H=1, N=1 << 20)
-    nt = inp.ntiles
-    check_all(avq, inp, tile_ranges=[(0, 1), (nt // 2, nt // 2 + 1), (nt - 1, nt)])
+    refinement kernel's chunk table at its largest).  Every key and every
+    query tile."""
+    check_all(avq, synth.generate("long-64k", H=1, N=1 << 20))
+
+
+def test_stage2_on_summed_partial_aggregates(avq):
+    """Stage 2 on aggregates the caller formed: stage 1 runs on two disjoint
+    halves of every head's keys, the test adds the two value sums and the
+    two counts, and stage 2 reads the sums.  The result must match the
+    oracle over the whole key set, as a sequence split over two devices
+    followed by a sum all-reduce would."""
+    inp = synth.generate("long-64k", B=1, H=2, N=9000)
+    _say(f"summed partial aggregates: {inp.name} H={inp.H} N={inp.N}")
+    ch = to_dev(inp.children, inp.dtype)
+    K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
+    parents, sq = avq.build_tree(ch)
+    cut = 4321
+    parts = [avq.assign_aggregate(K[:, :, a:b].contiguous(), V[:, :, a:b].contiguous(), parents, ch, sq,
+                                  want_leaf=True) for a, b in ((0, cut), (cut, inp.N))]
+    vsum = parts[0][0] + parts[1][0]
+    count = parts[0][1] + parts[1][1]
+    leaf = torch.cat([parts[0][2], parts[1][2]], dim=2)
+    Y, sel, imp = avq.attention_fwd(Q, parents, ch, vsum, count, inp.P, inp.T, inp.scale,
+                                    want_sel=True, want_importance=True)
+    torch.cuda.synchronize()
+    g = dict(Y=tensor_to_f64(Y, inp.dtype), sel=sel.cpu().numpy(), imp=imp.cpu().numpy().astype(np.float64))
+    par64, _ = oracle.build_tree(inp.f64("children"), inp.dtype)
+    a, vs64, cn64 = check_stage1(inp, par64, leaf.cpu().numpy(), vsum.cpu().numpy().astype(np.float64),
+                                 count.cpu().numpy())
+    err, namb = check_stage2(inp, par64, vs64, cn64, g, inp.P, inp.T)
+    _say(f"  max|dY|={err:.3e} ambiguous keys={a['n_ambiguous']} tiles={namb}")
+    assert err <= Y_TOL[inp.dtype], err
 
 
 # ------------------------------------------------------------------ edge shapes
@@ -276,8 +312,8 @@ def test_constant_values_give_constant_output(avq):
         ch = to_dev(inp.children, "bf16")
         K, V, Q = (to_dev(x, "bf16") for x in (inp.K, inp.V, inp.Q))
         parents, sq = avq.build_tree(ch)
-        _, _, _, pack = avq.assign_aggregate(K, V, parents, ch, sq)
-        Y, _, _ = avq.attention_fwd(Q, parents, ch, pack, P, 128, inp.scale)
+        vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq)
+        Y, _, _ = avq.attention_fwd(Q, parents, ch, vsum, count, P, 128, inp.scale)
         torch.cuda.synchronize()
         assert np.abs(tensor_to_f64(Y, "bf16") - 0.75).max() <= 4e-3
 
@@ -290,8 +326,8 @@ def test_forward_equals_the_stages(avq):
     K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
     Y1 = avq.forward(Q, K, V, ch, inp.P, inp.T, inp.scale)
     parents, sq = avq.build_tree(ch)
-    _, _, _, pack = avq.assign_aggregate(K, V, parents, ch, sq)
-    Y2, _, _ = avq.attention_fwd(Q, parents, ch, pack, inp.P, inp.T, inp.scale)
+    vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq)
+    Y2, _, _ = avq.attention_fwd(Q, parents, ch, vsum, count, inp.P, inp.T, inp.scale)
     Y3 = avq.forward(Q, K, V, ch, inp.P, inp.T, inp.scale, tree=(parents, sq))
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2) and torch.equal(Y1, Y3)
@@ -309,11 +345,9 @@ def test_repeated_runs_are_bitwise_identical(avq):
     parents, sq = avq.build_tree(ch)
     ref = None
     for it in range(12):
-        vsum, count, leaf, pack = avq.assign_aggregate(K, V, parents, ch, sq, want_leaf=True)
-        Y, sel, imp = avq.attention_fwd(Q, parents, ch, pack, inp.P, inp.T, inp.scale,
+        vsum, count, leaf = avq.assign_aggregate(K, V, parents, ch, sq, want_leaf=True)
+        Y, sel, imp = avq.attention_fwd(Q, parents, ch, vsum, count, inp.P, inp.T, inp.scale,
                                         want_sel=True, want_importance=True)
-        # (the operand pack's alignment gaps are never written, so it is
-        # compared through Y, which reads every byte it needs)
         got = dict(vsum=vsum, count=count, leaf=leaf, Y=Y, sel=sel, imp=imp)
         got = {k: t.clone() for k, t in got.items()}
         if ref is None:
@@ -331,26 +365,33 @@ def test_invalid_arguments_raise(avq):
     ch = to_dev(inp.children, "bf16")
     K, V, Q = (to_dev(x, "bf16") for x in (inp.K, inp.V, inp.Q))
     parents, sq = avq.build_tree(ch)
-    _, _, _, pack = avq.assign_aggregate(K, V, parents, ch, sq)
+    vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq)
     with pytest.raises(avq.AvqError, match="INVALID_ARG"):
-        avq.attention_fwd(Q, parents, ch, pack, 9, 128, inp.scale)   # P > M0
+        avq.attention_fwd(Q, parents, ch, vsum, count, 9, 128, inp.scale)   # P > M0
     with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
-        avq.attention_fwd(Q, parents, ch, pack, 2, 48, inp.scale)   # tile 48
+        avq.attention_fwd(Q, parents, ch, vsum, count, 2, 48, inp.scale)   # tile 48
     with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
-        avq.attention_fwd(Q, parents, ch, pack, 2, 16, inp.scale)   # tile 16
+        avq.attention_fwd(Q, parents, ch, vsum, count, 2, 16, inp.scale)   # tile 16
     with pytest.raises(avq.AvqError, match="INVALID_ARG"):
-        avq.attention_fwd(Q, parents, ch, pack, 2, 128, float("nan"))
+        avq.attention_fwd(Q, parents, ch, vsum, count, 2, 128, float("nan"))
     with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
         bad = torch.zeros((1, 8, 4, 96), dtype=torch.bfloat16, device=DEV)
         avq.build_tree(bad)   # d = 96
-    # output buffers of the wrong shape or type are refused before any launch
+    # output buffers, aggregates and workspaces of the wrong shape or type
+    # are refused before any launch
     with pytest.raises(avq.AvqError, match="Q's shape"):
-        avq.attention_fwd(Q, parents, ch, pack, 2, 128, inp.scale, out=Q[:, :, :128].contiguous())
+        avq.attention_fwd(Q, parents, ch, vsum, count, 2, 128, inp.scale, out=Q[:, :, :128].contiguous())
     with pytest.raises(avq.AvqError, match="dtype"):
-        avq.attention_fwd(Q, parents, ch, pack, 2, 128, inp.scale, out=Q.float())
-    vsum, count, _, pk = avq.assign_aggregate(K, V, parents, ch, sq)
+        avq.attention_fwd(Q, parents, ch, vsum, count, 2, 128, inp.scale, out=Q.float())
     with pytest.raises(avq.AvqError, match="do not match"):
-        avq.assign_aggregate(K, V, parents, ch, sq, out=(vsum[:, :, :-1].contiguous(), count, pk))
+        avq.attention_fwd(Q, parents, ch, vsum[:, :, :-1].contiguous(), count, 2, 128, inp.scale)
+    with pytest.raises(avq.AvqError, match="dtype"):
+        avq.attention_fwd(Q, parents, ch, vsum, count.float(), 2, 128, inp.scale)
+    with pytest.raises(avq.AvqError, match="too small"):
+        avq.attention_fwd(Q, parents, ch, vsum, count, 2, 128, inp.scale,
+                          workspace=torch.empty(64, dtype=torch.uint8, device=DEV))
     with pytest.raises(avq.AvqError, match="do not match"):
-        avq.assign_aggregate(K, V, parents, ch, sq, out=(vsum, count, pk[:-1]))
+        avq.assign_aggregate(K, V, parents, ch, sq, out=(vsum[:, :, :-1].contiguous(), count))
+    with pytest.raises(avq.AvqError, match="too small"):
+        avq.assign_aggregate(K, V, parents, ch, sq, workspace=torch.empty(64, dtype=torch.uint8, device=DEV))
     torch.cuda.synchronize()

@@ -123,6 +123,32 @@ def test_assign_hand_geometry():
     assert a["gap_parent"][0, 0, 3] == 0.0 and a["gap_leaf"][0, 0, 5] == 0.0
 
 
+def test_assign_relative_gap_hand_values():
+    # The near-tie measure is (D_(2) - D_(1)) / D_(2), normalised by the
+    # second-smallest distance.  Key at the origin, d = 2; parents at squared
+    # distances 4, 1, 9 (best not listed first), each with two children at
+    # +-0.5 across the parent, i.e. 0.25 farther than it.
+    ch = np.array([[[[2.0, 0.5], [2.0, -0.5]],
+                    [[1.0, 0.5], [1.0, -0.5]],
+                    [[3.0, 0.5], [3.0, -0.5]]]])
+    par, _ = oracle.build_tree(ch, "f32")
+    np.testing.assert_array_equal(par[0], [[2, 0], [1, 0], [3, 0]])
+    a = oracle.assign(np.zeros((1, 1, 1, 2)), par, ch)
+    assert a["pstar"][0, 0, 0] == 1 and a["leaf"][0, 0, 0] == 1
+    assert a["gap_parent"][0, 0, 0] == 0.75          # (4 - 1) / 4, not (4 - 1) / 1
+    assert a["gap_leaf"][0, 0, 0] == 0.2             # {1, 1.25, 1.25}: (1.25 - 1) / 1.25
+    # parents at squared distances 1, 2, 5 give (2 - 1) / 2
+    ch2 = np.array([[[[1.0, 0.5], [1.0, -0.5]],
+                     [[1.0, 1.5], [1.0, 0.5]],
+                     [[2.0, 1.5], [2.0, 0.5]]]])
+    par2, _ = oracle.build_tree(ch2, "f32")
+    b = oracle.assign(np.zeros((1, 1, 1, 2)), par2, ch2)
+    assert b["gap_parent"][0, 0, 0] == 0.5
+    # with the parent excluded (force_child) the two children tie: gap 0
+    f = oracle.assign(np.zeros((1, 1, 1, 2)), par, ch, force_child=True)
+    assert f["leaf"][0, 0, 0] == 3 + 1 * 2 and f["gap_leaf"][0, 0, 0] == 0.0
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_assign_brute_force_tiny(seed):
     rnd = random.Random(seed)
