@@ -20,10 +20,12 @@ __all__ = [
     "AvqError", "library_path", "load_library", "abi_version",
     "build_tree", "assign_aggregate", "attention_fwd", "exact_attention_fwd",
     "assign_aggregate_workspace_size", "attention_workspace_size", "forward",
+    "assign_aggregate_noalloc", "NOALLOC_SCRATCH_BYTES",
     "AVQ_FLAG_FORCE_CHILD",
 ]
 
 AVQ_FLAG_FORCE_CHILD = 1
+NOALLOC_SCRATCH_BYTES = 16 << 20   # AVQ_NOALLOC_SCRATCH_BYTES of include/avq.h
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -56,6 +58,9 @@ def load_library():
     lib.avq_build_tree.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.avq_assign_aggregate_workspace_size.restype = sz
     lib.avq_assign_aggregate_workspace_size.argtypes = [i32] * 6
+    lib.avq_assign_aggregate_noalloc.restype = i32
+    lib.avq_assign_aggregate_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, u32,
+                                                 vp, vp, vp, vp]
     lib.avq_attention_workspace_size.restype = sz
     lib.avq_attention_workspace_size.argtypes = [i32] * 6
     lib.avq_assign_aggregate.restype = i32
@@ -178,6 +183,41 @@ def assign_aggregate(K, V, parents, children, sqnorm, force_child: bool = False,
             AVQ_FLAG_FORCE_CHILD if force_child else 0, _ptr(vsum), _ptr(count), _ptr(leaf),
             _ptr(workspace), workspace.numel(), _stream(dev)))
     return vsum, count, leaf
+
+
+def assign_aggregate_noalloc(K, V, parents, children, sqnorm, out, force_child: bool = False,
+                             leaf: Optional[torch.Tensor] = None):
+    """Stage 1 through the allocation-free entry point: the caller passes the
+    outputs out = (vsum [B][H][S_tot][d] fp32, count [B][H][S_tot] int32) and
+    optionally leaf [B][H][N] int32; the library uses its own static device
+    scratch (calls that overlap on one device race).  Returns out."""
+    _need(K, "K", 4)
+    dev, dt = K.device, K.dtype
+    _need(V, "V", 4, dt, dev)
+    _need(children, "children", 4, dt, dev)
+    _need(parents, "parents", 3, dt, dev)
+    _need(sqnorm, "sqnorm", 2, torch.float32, dev)
+    B, H, N, d = K.shape
+    M0, C = children.shape[1], children.shape[2]
+    if V.shape != K.shape or children.shape[0] != H or children.shape[3] != d or \
+            parents.shape != (H, M0, d) or sqnorm.shape != (H, M0 * (1 + C)):
+        raise AvqError("inconsistent shapes")
+    S = M0 * (1 + C)
+    vsum, count = out
+    _need(vsum, "vsum", 4, torch.float32, dev)
+    _need(count, "count", 3, torch.int32, dev)
+    if vsum.shape != (B, H, S, d) or count.shape != (B, H, S):
+        raise AvqError("output buffers do not match the shape")
+    if leaf is not None:
+        _need(leaf, "leaf", 3, torch.int32, dev)
+        if leaf.shape != (B, H, N):
+            raise AvqError("leaf does not match the shape")
+    with _on(dev):
+        _check(load_library().avq_assign_aggregate_noalloc(
+            _ptr(K), _ptr(V), _ptr(parents), _ptr(children), _ptr(sqnorm), B, H, N, d, M0, C, _dt(K),
+            AVQ_FLAG_FORCE_CHILD if force_child else 0, _ptr(vsum), _ptr(count), _ptr(leaf),
+            _stream(dev)))
+    return vsum, count
 
 
 def attention_fwd(Q, parents, children, vsum, count, P: int, tile: int, scale: float,

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "avq.h"
 #include "avq_kernels.h"
@@ -57,6 +58,40 @@ int hip_status(hipError_t e)
 {
     if (e == hipSuccess) return AVQ_OK;
     return fail(AVQ_ERR_HIP, "HIP error: %s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+// Stage-1 scratch of the allocation-free entry point: one copy per device,
+// held from the library's load until the process ends.  In host code
+// `scratch` is only a handle; its device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[AVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the current device (resolved on the first
+// call made with that device current)
+int scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    AVQ_REQUIRE(dev >= 0 && dev < kMaxDevices, AVQ_ERR_UNSUPPORTED, "device index beyond 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        AVQ_REQUIRE(p != nullptr, AVQ_ERR_HIP, "hipGetSymbolAddress returned a null scratch address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return AVQ_OK;
 }
 
 }  // namespace
@@ -116,6 +151,33 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents, cons
     AVQ_REQUIRE(workspace_bytes >= need, AVQ_ERR_INVALID_ARG, "workspace too small");
     AVQ_REQUIRE(((uintptr_t)workspace & 255u) == 0, AVQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     const avq::AssignWorkspace ws = avq::carve_assign_workspace(workspace, B, H, N, M0, C, d);
+    return hip_status(avq::launch_assign_aggregate(K, V, parents, children, sqnorm, B, H, N, d, M0, C,
+                                                   dtype, flags, vsum_out, count_out, leaf_out, ws,
+                                                   (hipStream_t)stream));
+}
+
+int avq_assign_aggregate_noalloc(const void *K, const void *V, const void *parents, const void *children,
+                                 const float *sqnorm, int B, int H, int N, int d, int M0, int C, int dtype,
+                                 unsigned flags, float *vsum_out, int32_t *count_out, int32_t *leaf_out,
+                                 void *stream)
+{
+    AVQ_REQUIRE(K && V && parents && children && sqnorm && vsum_out && count_out, AVQ_ERR_INVALID_ARG,
+                "null pointer argument");
+    AVQ_REQUIRE((flags & ~(unsigned)AVQ_FLAG_FORCE_CHILD) == 0, AVQ_ERR_INVALID_ARG, "unknown flag bits");
+    int st = check_tree(H, M0, C, d, dtype);
+    if (st != AVQ_OK) return st;
+    st = check_seq(B, N);
+    if (st != AVQ_OK) return st;
+    const size_t need = avq::assign_workspace_bytes(B, H, N, M0, C, d);
+    AVQ_REQUIRE(need <= (size_t)AVQ_NOALLOC_SCRATCH_BYTES, AVQ_ERR_UNSUPPORTED,
+                "shape needs more stage-1 scratch than the allocation-free entry point holds "
+                "(AVQ_NOALLOC_SCRATCH_BYTES); use avq_assign_aggregate with a workspace");
+    void *base = nullptr;
+    st = scratch_address(&base);
+    if (st != AVQ_OK) return st;
+    // every byte of the scratch that the kernels read is written earlier in
+    // the same call, so nothing is cleared
+    const avq::AssignWorkspace ws = avq::carve_assign_workspace(base, B, H, N, M0, C, d);
     return hip_status(avq::launch_assign_aggregate(K, V, parents, children, sqnorm, B, H, N, d, M0, C,
                                                    dtype, flags, vsum_out, count_out, leaf_out, ws,
                                                    (hipStream_t)stream));

@@ -129,6 +129,29 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents,
                          void *stream);
 
 /*
+ * avq_assign_aggregate_noalloc -- avq_assign_aggregate for callers that
+ *   cannot allocate device memory (code under stream capture, tight serving
+ *   loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ *   errors, minus the workspace: the stage-1 scratch lives in a static
+ *   device array of AVQ_NOALLOC_SCRATCH_BYTES bytes that the library holds
+ *   on every device it runs on until the process ends.  The call allocates
+ *   and frees nothing.
+ *   Shapes whose scratch (avq_assign_aggregate_workspace_size) exceeds
+ *   AVQ_NOALLOC_SCRATCH_BYTES return AVQ_ERR_UNSUPPORTED before anything is
+ *   enqueued (16 MiB covers about 3.9 million keys over all (b, h), e.g.
+ *   B*H*N = 524288 at N = 65536, H = 8).
+ *   All calls on one device share that device's array: calls that overlap
+ *   in time on one device (different streams, or different host threads)
+ *   race and must be serialised by the caller.
+ */
+#define AVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int avq_assign_aggregate_noalloc(const void *K, const void *V, const void *parents,
+                                 const void *children, const float *sqnorm,
+                                 int B, int H, int N, int d, int M0, int C, int dtype,
+                                 unsigned flags, float *vsum_out, int32_t *count_out,
+                                 int32_t *leaf_out, void *stream);
+
+/*
  * avq_attention_workspace_size -- bytes of device workspace that
  * avq_attention_fwd needs for this shape (0 if the shape is invalid or
  * unsupported).  The workspace receives the aggregates rearranged as the
