@@ -55,16 +55,16 @@ def load_library():
     lib.avq_status_string.argtypes = [i32]
     lib.avq_last_error.restype = ctypes.c_char_p
     lib.avq_build_tree.restype = i32
-    lib.avq_build_tree.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.avq_build_tree.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.avq_assign_aggregate_workspace_size.restype = sz
     lib.avq_assign_aggregate_workspace_size.argtypes = [i32] * 6
     lib.avq_assign_aggregate_noalloc.restype = i32
-    lib.avq_assign_aggregate_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, u32,
-                                                 vp, vp, vp, vp]
+    lib.avq_assign_aggregate_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                                 u32, vp, vp, vp, vp]
     lib.avq_attention_workspace_size.restype = sz
     lib.avq_attention_workspace_size.argtypes = [i32] * 6
     lib.avq_assign_aggregate.restype = i32
-    lib.avq_assign_aggregate.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, u32,
+    lib.avq_assign_aggregate.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, u32,
                                          vp, vp, vp, vp, sz, vp]
     lib.avq_attention_fwd.restype = i32
     lib.avq_attention_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
@@ -119,15 +119,17 @@ def _need(t: torch.Tensor, name: str, ndim: int, dtype=None, dev=None):
 
 
 def build_tree(children: torch.Tensor):
-    """children [H][M0][C][d] -> (parents [H][M0][d], sqnorm [H][M0(1+C)] fp32)."""
+    """children [H][M0][C][d] -> (parents [H][M0][d], sqnorm [H][M0(1+C)] fp32,
+    frame [H][d] fp32): the tree stage 1 reads (norms are in the frame)."""
     _need(children, "children", 4)
     H, M0, C, d = children.shape
     parents = torch.empty((H, M0, d), dtype=children.dtype, device=children.device)
     sqnorm = torch.empty((H, M0 * (1 + C)), dtype=torch.float32, device=children.device)
+    frame = torch.empty((H, d), dtype=torch.float32, device=children.device)
     with _on(children.device):
         _check(load_library().avq_build_tree(_ptr(children), H, M0, C, d, _dt(children), _ptr(parents),
-                                             _ptr(sqnorm), _stream(children.device)))
-    return parents, sqnorm
+                                             _ptr(sqnorm), _ptr(frame), _stream(children.device)))
+    return parents, sqnorm, frame
 
 
 def assign_aggregate_workspace_size(B, H, N, M0, C, d) -> int:
@@ -147,7 +149,7 @@ def _workspace(ws, need: int, dev, name: str):
     return ws
 
 
-def assign_aggregate(K, V, parents, children, sqnorm, force_child: bool = False,
+def assign_aggregate(K, V, parents, children, sqnorm, frame, force_child: bool = False,
                      want_leaf: bool = False, workspace: Optional[torch.Tensor] = None,
                      out: Optional[tuple] = None):
     """Stage 1.  K, V [B][H][N][d] -> (vsum [B][H][S_tot][d] fp32,
@@ -158,10 +160,11 @@ def assign_aggregate(K, V, parents, children, sqnorm, force_child: bool = False,
     _need(children, "children", 4, dt, dev)
     _need(parents, "parents", 3, dt, dev)
     _need(sqnorm, "sqnorm", 2, torch.float32, dev)
+    _need(frame, "frame", 2, torch.float32, dev)
     B, H, N, d = K.shape
     M0, C = children.shape[1], children.shape[2]
     if V.shape != K.shape or children.shape[0] != H or children.shape[3] != d or \
-            parents.shape != (H, M0, d) or sqnorm.shape != (H, M0 * (1 + C)):
+            parents.shape != (H, M0, d) or sqnorm.shape != (H, M0 * (1 + C)) or frame.shape != (H, d):
         raise AvqError("inconsistent shapes")
     S = M0 * (1 + C)
     lib = load_library()
@@ -179,13 +182,13 @@ def assign_aggregate(K, V, parents, children, sqnorm, force_child: bool = False,
     leaf = torch.empty((B, H, N), dtype=torch.int32, device=dev) if want_leaf else None
     with _on(dev):
         _check(lib.avq_assign_aggregate(
-            _ptr(K), _ptr(V), _ptr(parents), _ptr(children), _ptr(sqnorm), B, H, N, d, M0, C, _dt(K),
+            _ptr(K), _ptr(V), _ptr(parents), _ptr(children), _ptr(sqnorm), _ptr(frame), B, H, N, d, M0, C, _dt(K),
             AVQ_FLAG_FORCE_CHILD if force_child else 0, _ptr(vsum), _ptr(count), _ptr(leaf),
             _ptr(workspace), workspace.numel(), _stream(dev)))
     return vsum, count, leaf
 
 
-def assign_aggregate_noalloc(K, V, parents, children, sqnorm, out, force_child: bool = False,
+def assign_aggregate_noalloc(K, V, parents, children, sqnorm, frame, out, force_child: bool = False,
                              leaf: Optional[torch.Tensor] = None):
     """Stage 1 through the allocation-free entry point: the caller passes the
     outputs out = (vsum [B][H][S_tot][d] fp32, count [B][H][S_tot] int32) and
@@ -197,10 +200,11 @@ def assign_aggregate_noalloc(K, V, parents, children, sqnorm, out, force_child: 
     _need(children, "children", 4, dt, dev)
     _need(parents, "parents", 3, dt, dev)
     _need(sqnorm, "sqnorm", 2, torch.float32, dev)
+    _need(frame, "frame", 2, torch.float32, dev)
     B, H, N, d = K.shape
     M0, C = children.shape[1], children.shape[2]
     if V.shape != K.shape or children.shape[0] != H or children.shape[3] != d or \
-            parents.shape != (H, M0, d) or sqnorm.shape != (H, M0 * (1 + C)):
+            parents.shape != (H, M0, d) or sqnorm.shape != (H, M0 * (1 + C)) or frame.shape != (H, d):
         raise AvqError("inconsistent shapes")
     S = M0 * (1 + C)
     vsum, count = out
@@ -214,7 +218,7 @@ def assign_aggregate_noalloc(K, V, parents, children, sqnorm, out, force_child: 
             raise AvqError("leaf does not match the shape")
     with _on(dev):
         _check(load_library().avq_assign_aggregate_noalloc(
-            _ptr(K), _ptr(V), _ptr(parents), _ptr(children), _ptr(sqnorm), B, H, N, d, M0, C, _dt(K),
+            _ptr(K), _ptr(V), _ptr(parents), _ptr(children), _ptr(sqnorm), _ptr(frame), B, H, N, d, M0, C, _dt(K),
             AVQ_FLAG_FORCE_CHILD if force_child else 0, _ptr(vsum), _ptr(count), _ptr(leaf),
             _stream(dev)))
     return vsum, count
@@ -278,7 +282,7 @@ def exact_attention_fwd(Q, K, V, scale: float, out: Optional[torch.Tensor] = Non
 def forward(Q, K, V, children, P: int, tile: int, scale: float, tree=None, force_child=False):
     """Whole AVQ-Attention forward: build (or reuse) the tree, stage 1,
     stage 2.  Returns Y."""
-    parents, sqnorm = tree if tree is not None else build_tree(children)
-    vsum, count, _ = assign_aggregate(K, V, parents, children, sqnorm, force_child=force_child)
+    parents, sqnorm, frame = tree if tree is not None else build_tree(children)
+    vsum, count, _ = assign_aggregate(K, V, parents, children, sqnorm, frame, force_child=force_child)
     Y, _, _ = attention_fwd(Q, parents, children, vsum, count, P, tile, scale)
     return Y

@@ -7,7 +7,11 @@
 //
 // Distances use ||c||^2 - 2 k.c (the ||k||^2 term is common to all
 // candidates): the MFMA accumulator starts at ||c||^2 and the LDS copy of the
-// parents holds -2c (exact in bf16 and fp32).  Candidates are compared on 22
+// parents holds -2c (exact in bf16 and fp32).  Keys and parents are first
+// moved into the frame of the head's reference point r (avq_build_tree; r =
+// 0 for a centred codebook, see avq_device.h), so that the rounding error
+// scales with the codebook's spread, not its offset; the norms passed in are
+// ||c - r||^2.  Candidates are compared on 22
 // of fp32's 24 significand bits; ties go to the lowest row block, and inside
 // a lane's group of four rows to the lower row when the compared value is
 // non-negative and to the higher one when it is negative (it is ||c||^2 -
@@ -71,7 +75,7 @@ template <typename T, int D> constexpr int assign_waves_per_simd()
 template <typename T, int D, int NRB>
 __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(assign_waves_per_simd<T, D>()))) void assign_parent_kernel(
     const T *__restrict__ K, const T *__restrict__ parents, const float *__restrict__ sqnorm,
-    int H, int N, int M0, int C, int nchunks, int32_t *__restrict__ sorted,
+    const float *__restrict__ frame, int H, int N, int M0, int C, int nchunks, int32_t *__restrict__ sorted,
     int2 *__restrict__ seg)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -86,7 +90,8 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
     static_assert(kAssignChunk % (NWV * KEYS) == 0, "chunk must be a whole number of steps");
     T *Pm2 = reinterpret_cast<T *>(smem);
     float *pn = reinterpret_cast<float *>(smem + (size_t)M0p * LDP * sizeof(T));
-    unsigned char *pst = reinterpret_cast<unsigned char *>(pn + M0p);   // [kAssignChunk]
+    float *rv = pn + M0p;                                              // [D] frame reference (16-B aligned)
+    unsigned char *pst = reinterpret_cast<unsigned char *>(rv + D);    // [kAssignChunk]
     int *hist = reinterpret_cast<int *>(pst + kAssignChunk);           // [257]
     int *wcnt = hist + 257;                                            // [NWV][256]
 
@@ -111,9 +116,11 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
     Frag<T> b[KB][KS];
     load_keys(0, b);   // in flight while the parents are staged
 
-    // stage -2 * parents and the parent norms (all loads issued before the
-    // first store; rows past M0 read the last parent and store zeros)
+    // stage -2 (parent - r) and the parent norms in the frame (all loads
+    // issued before the first store; rows past M0 read the last parent and
+    // store zeros)
     const T *Ph = parents + (int64_t)h * M0 * D;
+    const float *fr = frame + (int64_t)h * D;
     constexpr int kStage = (M0p * D + NT * 8 - 1) / (NT * 8);
     Frag<T> sf[kStage];
 #pragma unroll
@@ -122,10 +129,19 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
         sf[k] = load_frag(Ph + (int64_t)r * D + c);
     }
     float snorm = sqnorm[(int64_t)h * S + min(tid, M0 - 1)];
+    // the frame is all zero for a centred codebook: keys are then used as
+    // they are (the same value in every wave)
+    const float rl = fr[lane % D], rh = fr[(lane + 64) % D];
+    const bool shift = __ballot(rl != 0.f || rh != 0.f) != 0ull;
+    if (tid < D) rv[tid] = fr[tid];
 #pragma unroll
     for (int k = 0; k < kStage; ++k) {
         const int e = (tid + NT * k) * 8, r = e / D, c = e % D;
-        if (e < M0p * D) store_scaled_frag(Pm2 + r * LDP + c, r < M0 ? sf[k] : zero_frag<T>(), -2.0f);
+        if (e < M0p * D) {
+            const f32x4 r0 = *reinterpret_cast<const f32x4 *>(fr + c);
+            const f32x4 r1 = *reinterpret_cast<const f32x4 *>(fr + c + 4);
+            store_frag(Pm2 + r * LDP + c, r < M0 ? frame_m2(sf[k], r0, r1) : zero_frag<T>());
+        }
     }
     if (tid < M0p) pn[tid] = tid < M0 ? snorm : FLT_MAX;   // padding rows never win
     for (int r = tid; r < 257; r += NT) hist[r] = 0;
@@ -180,6 +196,12 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
             }
         };
         const bool more = it + 1 < kIters;
+        if (shift) {   // keys into the distance frame
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) b[kb][ks] = shift_frag(b[kb][ks], rv, 32 * ks + 8 * g);
+        }
         load_rows(0, a[0], c0[0]);
         if constexpr (NRB == 1) {
             issue(0);
@@ -313,42 +335,43 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
 }
 
 template <typename T, int D, int NRB>
-static hipError_t launch_assign(const void *K, const void *parents, const float *sqnorm, int B, int H,
-                                int N, int M0, int C, const AssignWorkspace &ws, hipStream_t stream)
+static hipError_t launch_assign(const void *K, const void *parents, const float *sqnorm, const float *frame,
+                                int B, int H, int N, int M0, int C, const AssignWorkspace &ws, hipStream_t stream)
 {
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     const size_t lds = (size_t)16 * NRB * (D + 8) * sizeof(T) + (size_t)16 * NRB * 4 +
-                       kAssignChunk + 257 * 4 + (kAssignThreads / 64) * 256 * 4;
+                       kAssignChunk + 257 * 4 + (kAssignThreads / 64) * 256 * 4 + D * 4;
     allow_full_lds<assign_parent_kernel<T, D, NRB>>();
     hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(kAssignThreads), lds, stream,
-                       (const T *)K, (const T *)parents, sqnorm, H, N, M0, C, nchunks, ws.sorted,
+                       (const T *)K, (const T *)parents, sqnorm, frame, H, N, M0, C, nchunks, ws.sorted,
                        ws.seg);
     return hipGetLastError();
 }
 
 
 template <typename T, int D>
-static hipError_t launch_parent_t(const void *K, const void *parents, const float *sqnorm, int B, int H,
-                                  int N, int M0, int C, const AssignWorkspace &ws, hipStream_t stream)
+static hipError_t launch_parent_t(const void *K, const void *parents, const float *sqnorm, const float *frame,
+                                  int B, int H, int N, int M0, int C, const AssignWorkspace &ws,
+                                  hipStream_t stream)
 {
     const int m = round16(M0);
-    if (m <= 16) return launch_assign<T, D, 1>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-    if (m <= 32) return launch_assign<T, D, 2>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-    if (m <= 64) return launch_assign<T, D, 4>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-    if (m <= 128) return launch_assign<T, D, 8>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-    return launch_assign<T, D, 16>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    if (m <= 16) return launch_assign<T, D, 1>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
+    if (m <= 32) return launch_assign<T, D, 2>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
+    if (m <= 64) return launch_assign<T, D, 4>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
+    if (m <= 128) return launch_assign<T, D, 8>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
+    return launch_assign<T, D, 16>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
 }
 
-hipError_t launch_assign_parent(const void *K, const void *parents, const float *sqnorm, int B, int H,
-                                int N, int d, int M0, int C, int dtype, const AssignWorkspace &ws,
-                                hipStream_t stream)
+hipError_t launch_assign_parent(const void *K, const void *parents, const float *sqnorm, const float *frame,
+                                int B, int H, int N, int d, int M0, int C, int dtype,
+                                const AssignWorkspace &ws, hipStream_t stream)
 {
     if (dtype == 1) {
-        if (d == 64) return launch_parent_t<bf16, 64>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-        return launch_parent_t<bf16, 128>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+        if (d == 64) return launch_parent_t<bf16, 64>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
+        return launch_parent_t<bf16, 128>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
     }
-    if (d == 64) return launch_parent_t<float, 64>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
-    return launch_parent_t<float, 128>(K, parents, sqnorm, B, H, N, M0, C, ws, stream);
+    if (d == 64) return launch_parent_t<float, 64>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
+    return launch_parent_t<float, 128>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
 }
 
 }  // namespace avq

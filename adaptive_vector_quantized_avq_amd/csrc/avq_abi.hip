@@ -114,12 +114,13 @@ const char *avq_status_string(int status)
 const char *avq_last_error(void) { return g_last_error; }
 
 int avq_build_tree(const void *children, int H, int M0, int C, int d, int dtype, void *parents_out,
-                   float *sqnorm_out, void *stream)
+                   float *sqnorm_out, float *frame_out, void *stream)
 {
-    AVQ_REQUIRE(children && parents_out && sqnorm_out, AVQ_ERR_INVALID_ARG, "null pointer argument");
+    AVQ_REQUIRE(children && parents_out && sqnorm_out && frame_out, AVQ_ERR_INVALID_ARG,
+                "null pointer argument");
     int st = check_tree(H, M0, C, d, dtype);
     if (st != AVQ_OK) return st;
-    return hip_status(avq::launch_build_tree(children, H, M0, C, d, dtype, parents_out, sqnorm_out,
+    return hip_status(avq::launch_build_tree(children, H, M0, C, d, dtype, parents_out, sqnorm_out, frame_out,
                                              (hipStream_t)stream));
 }
 
@@ -136,11 +137,11 @@ size_t avq_attention_workspace_size(int B, int H, int M0, int C, int d, int dtyp
 }
 
 int avq_assign_aggregate(const void *K, const void *V, const void *parents, const void *children,
-                         const float *sqnorm, int B, int H, int N, int d, int M0, int C, int dtype,
-                         unsigned flags, float *vsum_out, int32_t *count_out, int32_t *leaf_out,
+                         const float *sqnorm, const float *frame, int B, int H, int N, int d, int M0, int C,
+                         int dtype, unsigned flags, float *vsum_out, int32_t *count_out, int32_t *leaf_out,
                          void *workspace, size_t workspace_bytes, void *stream)
 {
-    AVQ_REQUIRE(K && V && parents && children && sqnorm && vsum_out && count_out && workspace,
+    AVQ_REQUIRE(K && V && parents && children && sqnorm && frame && vsum_out && count_out && workspace,
                 AVQ_ERR_INVALID_ARG, "null pointer argument");
     AVQ_REQUIRE((flags & ~(unsigned)AVQ_FLAG_FORCE_CHILD) == 0, AVQ_ERR_INVALID_ARG, "unknown flag bits");
     int st = check_tree(H, M0, C, d, dtype);
@@ -151,17 +152,17 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents, cons
     AVQ_REQUIRE(workspace_bytes >= need, AVQ_ERR_INVALID_ARG, "workspace too small");
     AVQ_REQUIRE(((uintptr_t)workspace & 255u) == 0, AVQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     const avq::AssignWorkspace ws = avq::carve_assign_workspace(workspace, B, H, N, M0, C, d);
-    return hip_status(avq::launch_assign_aggregate(K, V, parents, children, sqnorm, B, H, N, d, M0, C,
+    return hip_status(avq::launch_assign_aggregate(K, V, parents, children, sqnorm, frame, B, H, N, d, M0, C,
                                                    dtype, flags, vsum_out, count_out, leaf_out, ws,
                                                    (hipStream_t)stream));
 }
 
 int avq_assign_aggregate_noalloc(const void *K, const void *V, const void *parents, const void *children,
-                                 const float *sqnorm, int B, int H, int N, int d, int M0, int C, int dtype,
-                                 unsigned flags, float *vsum_out, int32_t *count_out, int32_t *leaf_out,
-                                 void *stream)
+                                 const float *sqnorm, const float *frame, int B, int H, int N, int d, int M0,
+                                 int C, int dtype, unsigned flags, float *vsum_out, int32_t *count_out,
+                                 int32_t *leaf_out, void *stream)
 {
-    AVQ_REQUIRE(K && V && parents && children && sqnorm && vsum_out && count_out, AVQ_ERR_INVALID_ARG,
+    AVQ_REQUIRE(K && V && parents && children && sqnorm && frame && vsum_out && count_out, AVQ_ERR_INVALID_ARG,
                 "null pointer argument");
     AVQ_REQUIRE((flags & ~(unsigned)AVQ_FLAG_FORCE_CHILD) == 0, AVQ_ERR_INVALID_ARG, "unknown flag bits");
     int st = check_tree(H, M0, C, d, dtype);
@@ -178,7 +179,7 @@ int avq_assign_aggregate_noalloc(const void *K, const void *V, const void *paren
     // every byte of the scratch that the kernels read is written earlier in
     // the same call, so nothing is cleared
     const avq::AssignWorkspace ws = avq::carve_assign_workspace(base, B, H, N, M0, C, d);
-    return hip_status(avq::launch_assign_aggregate(K, V, parents, children, sqnorm, B, H, N, d, M0, C,
+    return hip_status(avq::launch_assign_aggregate(K, V, parents, children, sqnorm, frame, B, H, N, d, M0, C,
                                                    dtype, flags, vsum_out, count_out, leaf_out, ws,
                                                    (hipStream_t)stream));
 }

@@ -353,4 +353,68 @@ __device__ __forceinline__ int mbcnt(unsigned long long mask)
                                           __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
 }
 
+// ---------------------------------------------------------------- distance frame
+// Squared distances are compared as ||c||^2 - 2 k.c, whose fp32 rounding
+// error grows with ||k||^2 and ||c||^2 rather than with the distance itself:
+// a codebook far from the origin (every coordinate near +32, say) would make
+// near-tied keys undecidable.  Translating keys and codewords by a common
+// point r changes no distance, so the assignment kernels compare in the
+// frame of a per-head reference point r that avq_build_tree derives from the
+// codebook (r = 0 for a centred codebook; otherwise coordinates of 3
+// significant bits for which every c_t - r_t is exact in the storage type).
+// Codewords are staged as -2(c - r), keys shifted in registers, u = k - r,
+// rounded to the storage type: exact for any key on the same side of zero
+// as an offset coordinate of the codebook.
+
+// round to 3 significant bits (representable in bf16)
+__device__ __forceinline__ float coarse3(float x)
+{
+    return __uint_as_float((__float_as_uint(x) + (1u << 20)) & 0xFFE00000u);
+}
+
+template <typename T> __device__ __forceinline__ bool exact_in(float x);
+template <> __device__ __forceinline__ bool exact_in<bf16>(float x) { return (float)(bf16)x == x; }
+template <> __device__ __forceinline__ bool exact_in<float>(float) { return true; }
+
+// -2 (f - r) for the 8 dimensions of fragment f (r0, r1: r of those
+// dimensions); exact in bf16 for the codebook the frame was built from
+__device__ __forceinline__ Frag<bf16> frame_m2(const Frag<bf16> &f, f32x4 r0, f32x4 r1)
+{
+    Frag<bf16> o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        o.v[k] = (bf16)(-2.f * ((float)f.v[k] - r0[k]));
+        o.v[4 + k] = (bf16)(-2.f * ((float)f.v[4 + k] - r1[k]));
+    }
+    return o;
+}
+__device__ __forceinline__ Frag<float> frame_m2(const Frag<float> &f, f32x4 r0, f32x4 r1)
+{
+    Frag<float> o;
+    o.lo = -2.f * (f.lo - r0);
+    o.hi = -2.f * (f.hi - r1);
+    return o;
+}
+
+// key fragment of dimensions dim0..dim0+7 moved into the frame: k - r
+__device__ __forceinline__ Frag<bf16> shift_frag(const Frag<bf16> &f, const float *rv, int dim0)
+{
+    const f32x4 r0 = *reinterpret_cast<const f32x4 *>(rv + dim0);
+    const f32x4 r1 = *reinterpret_cast<const f32x4 *>(rv + dim0 + 4);
+    Frag<bf16> o;   // (rounded to nearest: exact for keys the frame covers)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        o.v[k] = (bf16)((float)f.v[k] - r0[k]);
+        o.v[4 + k] = (bf16)((float)f.v[4 + k] - r1[k]);
+    }
+    return o;
+}
+__device__ __forceinline__ Frag<float> shift_frag(const Frag<float> &f, const float *rv, int dim0)
+{
+    Frag<float> o;
+    o.lo = f.lo - *reinterpret_cast<const f32x4 *>(rv + dim0);
+    o.hi = f.hi - *reinterpret_cast<const f32x4 *>(rv + dim0 + 4);
+    return o;
+}
+
 }  // namespace avq

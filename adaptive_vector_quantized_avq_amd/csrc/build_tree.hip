@@ -1,7 +1,9 @@
 // Frozen-tree preparation ("AVQ-Attention", Sec. 4.1 parent-child
-// constraint): every parent is the mean of its C children, and every stored
-// codeword gets its squared norm for the distance expansion
-// ||k - c||^2 = ||k||^2 + ||c||^2 - 2 k.c used by the assignment kernels.
+// constraint): every parent is the mean of its C children; every head gets
+// the reference point r of its distance frame (see codebook frame below),
+// and every stored codeword its squared norm in that frame for the
+// expansion ||k - c||^2 = ||u||^2 + ||c - r||^2 - 2 u.(c - r), u = k - r,
+// used by the assignment kernels.
 //
 // Runs once per codebook; it is not on the per-forward path, so it favours
 // exactness over speed: sums are taken in fp64 in index order and rounded
@@ -31,11 +33,57 @@ __global__ void tree_parents_kernel(const T *__restrict__ children, int H, int M
     }
 }
 
+// Codebook frame of each head: r_t = 0 unless coordinate t of the head's
+// stored codewords (parents and children) is offset from zero by more than
+// twice its spread, max |c_t - mean_t|; then r_t is the mean rounded to 3
+// significant bits, kept only if c_t - r_t is exact in the storage type for
+// every codeword (else r_t = 0).  Comparing distances as
+// ||c - r||^2 - 2 (k - r).(c - r) changes no distance but makes the fp32
+// rounding scale with the codebook's spread rather than its offset from the
+// origin.  One thread per (head, coordinate).
+template <typename T>
+__global__ void tree_frame_kernel(const T *__restrict__ parents, const T *__restrict__ children, int H,
+                                  int M0, int C, int d, float *__restrict__ frame)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)H * d) return;
+    const int h = (int)(i / d), t = (int)(i % d);
+    const int S = M0 * (1 + C);
+    auto coord = [&](int j) -> float {
+        return to_float(j < M0 ? parents[((int64_t)h * M0 + j) * d + t]
+                               : children[((int64_t)h * M0 * C + (j - M0)) * d + t]);
+    };
+    double s = 0.0;
+    float lo = INFINITY, hi = -INFINITY;
+    for (int j = 0; j < S; ++j) {
+        const float c = coord(j);
+        s += (double)c;
+        lo = fminf(lo, c);
+        hi = fmaxf(hi, c);
+    }
+    const float mu = (float)(s / (double)S);
+    const float spread = fmaxf(hi - mu, mu - lo);
+    float r = fabsf(mu) > 2.f * spread ? coarse3(mu) : 0.f;
+    if (r != 0.f) {   // c - r must be exact in the storage type for every codeword
+        for (int j = 0; j < S; ++j) {
+            const double dl = (double)coord(j) - (double)r;   // exact in fp64
+            const float df = (float)dl;
+            if (!((double)df == dl && exact_in<T>(df))) {
+                r = 0.f;
+                break;
+            }
+        }
+    }
+    frame[i] = r;
+}
+
 // one thread per stored codeword row; rows [0, M0) of a head are parents,
-// rows [M0, S_tot) children in slot order
+// rows [M0, S_tot) children in slot order; norms are taken in the head's
+// frame, ||c - r||^2, in fp64 and rounded once
 template <typename T>
 __global__ void tree_sqnorm_kernel(const T *__restrict__ parents, const T *__restrict__ children,
-                                   int H, int M0, int C, int d, float *__restrict__ sqnorm)
+                                   const float *__restrict__ frame, int H, int M0, int C, int d,
+                                   float *__restrict__ sqnorm)
 {
     const int S = M0 * (1 + C);
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -44,9 +92,10 @@ __global__ void tree_sqnorm_kernel(const T *__restrict__ parents, const T *__res
     const int j = (int)(i % S);
     const T *row = j < M0 ? parents + ((int64_t)h * M0 + j) * d
                           : children + ((int64_t)h * M0 * C + (j - M0)) * d;
+    const float *r = frame + (int64_t)h * d;
     double s = 0.0;
     for (int t = 0; t < d; ++t) {
-        const double x = (double)to_float(row[t]);
+        const double x = (double)to_float(row[t]) - (double)r[t];
         s += x * x;
     }
     sqnorm[i] = (float)s;
@@ -54,24 +103,27 @@ __global__ void tree_sqnorm_kernel(const T *__restrict__ parents, const T *__res
 
 template <typename T>
 static hipError_t launch_tree_t(const void *children, int H, int M0, int C, int d, void *parents,
-                                float *sqnorm, hipStream_t stream)
+                                float *sqnorm, float *frame, hipStream_t stream)
 {
     const int64_t np = (int64_t)H * M0 * d;
     const int threads = 256;
     hipLaunchKernelGGL(tree_parents_kernel<T>, dim3((unsigned)((np + threads - 1) / threads)),
                        dim3(threads), 0, stream, (const T *)children, H, M0, C, d, (T *)parents);
+    const int64_t nf = (int64_t)H * d;
+    hipLaunchKernelGGL(tree_frame_kernel<T>, dim3((unsigned)((nf + 63) / 64)), dim3(64), 0, stream,
+                       (const T *)parents, (const T *)children, H, M0, C, d, frame);
     const int64_t nr = (int64_t)H * M0 * (1 + C);
     hipLaunchKernelGGL(tree_sqnorm_kernel<T>, dim3((unsigned)((nr + threads - 1) / threads)),
-                       dim3(threads), 0, stream, (const T *)parents, (const T *)children, H, M0, C,
-                       d, sqnorm);
+                       dim3(threads), 0, stream, (const T *)parents, (const T *)children,
+                       (const float *)frame, H, M0, C, d, sqnorm);
     return hipGetLastError();
 }
 
 hipError_t launch_build_tree(const void *children, int H, int M0, int C, int d, int dtype,
-                             void *parents, float *sqnorm, hipStream_t stream)
+                             void *parents, float *sqnorm, float *frame, hipStream_t stream)
 {
-    if (dtype == 1) return launch_tree_t<bf16>(children, H, M0, C, d, parents, sqnorm, stream);
-    return launch_tree_t<float>(children, H, M0, C, d, parents, sqnorm, stream);
+    if (dtype == 1) return launch_tree_t<bf16>(children, H, M0, C, d, parents, sqnorm, frame, stream);
+    return launch_tree_t<float>(children, H, M0, C, d, parents, sqnorm, frame, stream);
 }
 
 }  // namespace avq

@@ -17,7 +17,9 @@ namespace avq {
 // Distances: the codeword rows of parent lp occupy a block of BR = 16 or 32
 // rows (row j < CC: child j, row CC: the parent itself, the rest padding with
 // norm +inf); one MFMA pass covers the G blocks and each key keeps only the
-// rows of its own parent's block.
+// rows of its own parent's block.  Keys and codewords are compared in the
+// frame of the head's reference point r (avq_build_tree; r = 0 for a
+// centred codebook, see avq_device.h); the norms passed in are ||c - r||^2.
 //
 // Aggregation is a product on the matrix cores: for a chunk of 32 keys,
 //   sums[slot][dim] += onehot[slot][key] * V[key][dim],  counts likewise with
@@ -54,7 +56,7 @@ template <typename T, int D, int CC> struct RefineCfg {
     static constexpr int LDK = KEYS + 16 / (int)sizeof(T) * 2; // transposed-V row stride
     static constexpr int LDA = D + 1;                          // accumulator row stride
     static constexpr size_t cw_bytes = (size_t)G * BR * LDP * sizeof(T);
-    static constexpr size_t rn_bytes = (size_t)G * BR * 4;
+    static constexpr size_t rn_bytes = (size_t)G * BR * 4 + (size_t)D * 4;   // norms, frame reference
     static constexpr size_t vt_bytes = (size_t)NW * (D * LDK * sizeof(T) + KEYS);
     static constexpr size_t acc1_bytes = (size_t)NSB * 16 * (LDA + 1) * 4;
     // partial-sum slices in LDS (they share the region of the V tiles): one
@@ -130,7 +132,8 @@ template <typename T, int D, int CC>
 __global__ __launch_bounds__(kRefineThreads) __attribute__((amdgpu_waves_per_eu(refine_waves_per_simd<T, D, CC>())))
 void refine_aggregate_kernel(
     const T *__restrict__ K, const T *__restrict__ V, const T *__restrict__ parents,
-    const T *__restrict__ children, const float *__restrict__ sqnorm, int H, int N, int M0,
+    const T *__restrict__ children, const float *__restrict__ sqnorm, const float *__restrict__ frame,
+    int H, int N, int M0,
     int nchunks, int force_child, const int32_t *__restrict__ sorted,
     const int2 *__restrict__ seg, float *__restrict__ vsum, int32_t *__restrict__ count,
     int32_t *__restrict__ leaf)
@@ -143,6 +146,7 @@ void refine_aggregate_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     T *Cw = reinterpret_cast<T *>(smem);                                   // [G*BR][LDP]
     float *rn = reinterpret_cast<float *>(smem + Cfg::cw_bytes);           // [G*BR]
+    float *rv = rn + G * BR;                                               // [D] frame reference
     unsigned char *un = smem + Cfg::cw_bytes + Cfg::rn_bytes;              // union region
     int *pre = reinterpret_cast<int *>(un + ((Cfg::union_bytes + 15) & ~(size_t)15));   // [nchunks+1]
     int *segs = pre + nchunks + 1;                                         // [nchunks]
@@ -185,11 +189,20 @@ void refine_aggregate_kernel(
         pre[c] = sg.y;
         segs[c] = c * kAssignChunk + sg.x;
     }
+    // the frame is all zero for a centred codebook: keys are then used as
+    // they are (the same value in every wave)
+    const float *fr = frame + (int64_t)h * D;
+    const float rl = fr[lane % D], rh = fr[(lane + 64) % D];
+    const bool shift = __ballot(rl != 0.f || rh != 0.f) != 0ull;
+    if (tid < D) rv[tid] = fr[tid];
 #pragma unroll
     for (int k = 0; k < kStage; ++k) {
         const int e = (tid + NT * k) * 8, r = e / D, c = e % D, lp = r / BR, j = r % BR;
-        if (e < kRows * D)
-            store_scaled_frag(Cw + r * LDP + c, (lp < Gv && j <= CC) ? sf[k] : zero_frag<T>(), -2.0f);
+        if (e < kRows * D) {
+            const f32x4 r0 = *reinterpret_cast<const f32x4 *>(fr + c);
+            const f32x4 r1 = *reinterpret_cast<const f32x4 *>(fr + c + 4);
+            store_frag(Cw + r * LDP + c, (lp < Gv && j <= CC) ? frame_m2(sf[k], r0, r1) : zero_frag<T>());
+        }
     }
     if (tid < kRows) rn[tid] = nrm;
     __syncthreads();
@@ -254,6 +267,12 @@ void refine_aggregate_kernel(
     auto compute = [&](int s, unsigned e, bool more, unsigned en, Frag<T> (&kf)[KB][KS],
                        Frag<T> (&vf)[KB][KS]) {
         const int x0 = xpos(s);
+        if (shift) {   // keys into the distance frame
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = shift_frag(kf[kb][ks], rv, 32 * ks + 8 * g);
+        }
         int key[KB], lp[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -435,8 +454,8 @@ void refine_aggregate_kernel(
 
 template <typename T, int D, int CC>
 static hipError_t launch_refine(const void *K, const void *V, const void *parents,
-                                const void *children, const float *sqnorm, int B, int H, int N,
-                                int M0, unsigned flags, float *vsum, int32_t *count, int32_t *leaf,
+                                const void *children, const float *sqnorm, const float *frame, int B, int H,
+                                int N, int M0, unsigned flags, float *vsum, int32_t *count, int32_t *leaf,
                                 const AssignWorkspace &ws, hipStream_t stream)
 {
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
@@ -445,19 +464,20 @@ static hipError_t launch_refine(const void *K, const void *V, const void *parent
     const int ngroups = (M0 + RefineCfg<T, D, CC>::G - 1) / RefineCfg<T, D, CC>::G;
     hipLaunchKernelGGL((refine_aggregate_kernel<T, D, CC>), dim3(ngroups, B * H), dim3(kRefineThreads),
                        lds, stream, (const T *)K, (const T *)V, (const T *)parents,
-                       (const T *)children, sqnorm, H, N, M0, nchunks, (flags & 1u) ? 1 : 0,
+                       (const T *)children, sqnorm, frame, H, N, M0, nchunks, (flags & 1u) ? 1 : 0,
                        ws.sorted, ws.seg, vsum, count, leaf);
     return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_refine_t(const void *K, const void *V, const void *parents, const void *children,
-                                  const float *sqnorm, int B, int H, int N, int M0, int C, unsigned flags,
+                                  const float *sqnorm, const float *frame, int B, int H, int N, int M0, int C,
+                                  unsigned flags,
                                   float *vsum, int32_t *count, int32_t *leaf,
                                   const AssignWorkspace &ws, hipStream_t stream)
 {
 #define AVQ_REFINE(CCV) \
-    launch_refine<T, D, CCV>(K, V, parents, children, sqnorm, B, H, N, M0, flags, vsum, count, leaf, ws, stream)
+    launch_refine<T, D, CCV>(K, V, parents, children, sqnorm, frame, B, H, N, M0, flags, vsum, count, leaf, ws, stream)
     switch (C) {
     case 2: return AVQ_REFINE(2);
     case 4: return AVQ_REFINE(4);
@@ -468,21 +488,22 @@ static hipError_t launch_refine_t(const void *K, const void *V, const void *pare
 }
 
 hipError_t launch_assign_aggregate(const void *K, const void *V, const void *parents,
-                                   const void *children, const float *sqnorm, int B, int H, int N,
+                                   const void *children, const float *sqnorm, const float *frame, int B,
+                                   int H, int N,
                                    int d, int M0, int C, int dtype, unsigned flags, float *vsum,
                                    int32_t *count, int32_t *leaf, const AssignWorkspace &ws,
                                    hipStream_t stream)
 {
-    hipError_t err = launch_assign_parent(K, parents, sqnorm, B, H, N, d, M0, C, dtype, ws, stream);
+    hipError_t err = launch_assign_parent(K, parents, sqnorm, frame, B, H, N, d, M0, C, dtype, ws, stream);
     if (err != hipSuccess) return err;
     if (dtype == 1) {
         if (d == 64)
-            return launch_refine_t<bf16, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
-        return launch_refine_t<bf16, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
+            return launch_refine_t<bf16, 64>(K, V, parents, children, sqnorm, frame, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
+        return launch_refine_t<bf16, 128>(K, V, parents, children, sqnorm, frame, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
     }
     if (d == 64)
-        return launch_refine_t<float, 64>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
-    return launch_refine_t<float, 128>(K, V, parents, children, sqnorm, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
+        return launch_refine_t<float, 64>(K, V, parents, children, sqnorm, frame, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
+    return launch_refine_t<float, 128>(K, V, parents, children, sqnorm, frame, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
 }
 
 }  // namespace avq

@@ -155,7 +155,7 @@ def main():
         sh = s * 7 * inp.T % inp.N
         sets.append(tuple(torch.roll(x, shifts=sh, dims=2).contiguous() for x in (Q0, K0, V0)))
     del Q0, K0, V0
-    parents, sq = avq.build_tree(ch)
+    parents, sq, fr = avq.build_tree(ch)
     B, H, N, d, S = inp.B, inp.H, inp.N, inp.d, inp.S_tot
     vsum = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
     count = torch.empty((B, H, S), dtype=torch.int32, device=dev)
@@ -169,7 +169,7 @@ def main():
         Q, K, V = sets[i % len(sets)]
         if ev is not None:
             ev[0].record()
-        avq.assign_aggregate(K, V, parents, ch, sq, workspace=ws1, out=(vsum, count))
+        avq.assign_aggregate(K, V, parents, ch, sq, fr, workspace=ws1, out=(vsum, count))
         if ev is not None:
             ev[1].record()
         avq.attention_fwd(Q, parents, ch, vsum, count, P, inp.T, inp.scale, workspace=ws2, out=Y)

@@ -69,21 +69,35 @@ const char *avq_status_string(int status);
 const char *avq_last_error(void);
 
 /*
- * avq_build_tree -- parents and squared codeword norms of a frozen tree.
+ * avq_build_tree -- parents, distance frame and squared codeword norms of a
+ * frozen tree (once per codebook).
  *   Sec. 4.1 "Parent-child constraint": each parent is the mean of its C
  *   children.
  *   children   [H][M0][C][d]  dtype   input
  *   parents_out[H][M0][d]     dtype   output: mean of the C children,
  *                                     accumulated in fp64, rounded once to
  *                                     dtype (nearest, ties to even)
- *   sqnorm_out [H][S_tot]     fp32    output: squared norm of every stored
+ *   frame_out  [H][d]         fp32    output: reference point r of each
+ *                                     head's distance frame.  r_t = 0 unless
+ *                                     coordinate t of the head's stored
+ *                                     codewords lies further from zero than
+ *                                     twice its spread (|mean| > 2 max|c_t -
+ *                                     mean|); then r_t is the mean rounded to
+ *                                     3 significant bits, provided c_t - r_t
+ *                                     is exact in dtype for every codeword
+ *                                     (else 0).  Stage 1 compares distances
+ *                                     as ||c - r||^2 - 2 (k - r).(c - r):
+ *                                     the same distances, with fp32 rounding
+ *                                     that scales with the codebook's spread
+ *                                     instead of its offset from the origin.
+ *   sqnorm_out [H][S_tot]     fp32    output: ||c - r||^2 of every stored
  *                                     codeword (parents first, then
  *                                     children in slot order), accumulated
  *                                     in fp64 over the stored values,
  *                                     rounded once to fp32
  */
 int avq_build_tree(const void *children, int H, int M0, int C, int d, int dtype,
-                   void *parents_out, float *sqnorm_out, void *stream);
+                   void *parents_out, float *sqnorm_out, float *frame_out, void *stream);
 
 /*
  * avq_assign_aggregate_workspace_size -- bytes of device workspace that
@@ -105,6 +119,7 @@ size_t avq_assign_aggregate_workspace_size(int B, int H, int N, int M0, int C, i
  *   parents    [H][M0][d]     dtype   from avq_build_tree
  *   children   [H][M0][C][d]  dtype
  *   sqnorm     [H][S_tot]     fp32    from avq_build_tree
+ *   frame      [H][d]         fp32    from avq_build_tree
  *   flags      0 or AVQ_FLAG_FORCE_CHILD
  *   vsum_out   [B][H][S_tot][d] fp32  output value sums (every slot written)
  *   count_out  [B][H][S_tot]  int32   output key counts (every slot written)
@@ -122,7 +137,7 @@ size_t avq_assign_aggregate_workspace_size(int B, int H, int N, int M0, int C, i
  *   sequence split over several devices would all-reduce.
  */
 int avq_assign_aggregate(const void *K, const void *V, const void *parents,
-                         const void *children, const float *sqnorm,
+                         const void *children, const float *sqnorm, const float *frame,
                          int B, int H, int N, int d, int M0, int C, int dtype,
                          unsigned flags, float *vsum_out, int32_t *count_out,
                          int32_t *leaf_out, void *workspace, size_t workspace_bytes,
@@ -146,7 +161,7 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents,
  */
 #define AVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
 int avq_assign_aggregate_noalloc(const void *K, const void *V, const void *parents,
-                                 const void *children, const float *sqnorm,
+                                 const void *children, const float *sqnorm, const float *frame,
                                  int B, int H, int N, int d, int M0, int C, int dtype,
                                  unsigned flags, float *vsum_out, int32_t *count_out,
                                  int32_t *leaf_out, void *stream);

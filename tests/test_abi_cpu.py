@@ -117,19 +117,23 @@ def test_invalid_arguments_are_rejected_before_launch(lib):
 
     aa = lib.avq_assign_aggregate
     # a valid call template; each case below breaks exactly one argument
-    base = [p, p, p, p, p, 1, 1, 128, 64, 16, 4, 1, 0, p, p, None, p, 1 << 20, None]
+    base = [p, p, p, p, p, p, 1, 1, 128, 64, 16, 4, 1, 0, p, p, None, p, 1 << 20, None]
     bad_flags = list(base)
-    bad_flags[12] = 2
+    bad_flags[13] = 2
     assert aa(*bad_flags) == -1
+    no_frame = list(base)
+    no_frame[5] = None
+    assert aa(*no_frame) == -1
     no_ws = list(base)
-    no_ws[16] = None
+    no_ws[17] = None
     assert aa(*no_ws) == -1
     small_ws = list(base)
-    small_ws[17] = 16
+    small_ws[18] = 16
     assert aa(*small_ws) == -1
     misaligned = list(base)
-    misaligned[16] = ctypes.c_void_p(0x1004)
+    misaligned[17] = ctypes.c_void_p(0x1004)
     assert aa(*misaligned) == -1
-    assert lib.avq_build_tree(None, 1, 4, 4, 64, 1, p, p, None) == -1
-    assert lib.avq_build_tree(p, 1, 4, 4, 64, 5, p, p, None) == -1
+    assert lib.avq_build_tree(None, 1, 4, 4, 64, 1, p, p, p, None) == -1
+    assert lib.avq_build_tree(p, 1, 4, 4, 64, 1, p, p, None, None) == -1
+    assert lib.avq_build_tree(p, 1, 4, 4, 64, 5, p, p, p, None) == -1
     assert lib.avq_exact_attention_fwd(p, p, p, 1, 1, 16, 80, 1.0, 1, p, None) == -2

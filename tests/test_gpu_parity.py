@@ -44,16 +44,33 @@ def to_dev(arr, dtype):
 def run_gpu(avq, inp, P, T, force_child=False):
     ch = to_dev(inp.children, inp.dtype)
     K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
-    parents, sq = avq.build_tree(ch)
-    vsum, count, leaf = avq.assign_aggregate(K, V, parents, ch, sq, force_child=force_child,
+    parents, sq, fr = avq.build_tree(ch)
+    vsum, count, leaf = avq.assign_aggregate(K, V, parents, ch, sq, fr, force_child=force_child,
                                              want_leaf=True)
     Y, sel, imp = avq.attention_fwd(Q, parents, ch, vsum, count, P, T, inp.scale,
                                     want_sel=True, want_importance=True)
     torch.cuda.synchronize()
     return dict(parents=tensor_to_f64(parents, inp.dtype), sqnorm=sq.cpu().numpy(),
+                frame=fr.cpu().numpy().astype(np.float64),
                 vsum=vsum.cpu().numpy().astype(np.float64), count=count.cpu().numpy(),
                 leaf=leaf.cpu().numpy(), Y=tensor_to_f64(Y, inp.dtype),
                 sel=sel.cpu().numpy(), imp=imp.cpu().numpy().astype(np.float64))
+
+
+def check_tree_frame(inp, par64, sq64, frame, sqnorm):
+    """The tree's distance frame: every r_t is 0 or leaves c_t - r_t exact
+    in the storage type for every stored codeword of its head; the norms are
+    ||c - r||^2 rounded to fp32 (the oracle's own ||c||^2 where r = 0)."""
+    H, M0, C, d = inp.H, inp.M0, inp.C, inp.d
+    rows = np.concatenate([par64, inp.f64("children").reshape(H, M0 * C, d)], axis=1)
+    diff = rows - frame[:, None, :]                     # exact in fp64
+    exact = oracle.round_to(diff, inp.dtype) == diff
+    assert (exact | (frame == 0.0)[:, None, :]).all()
+    ref = np.sum(diff * diff, axis=-1)
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert (np.abs(sqnorm.astype(np.float64) - ref) <= ulp).all()
+    if not frame.any():
+        np.testing.assert_array_equal(sqnorm, sq64.astype(np.float32))
 
 
 def check_stage2(inp, par64, vsum, count, g, P, T):
@@ -82,7 +99,7 @@ def check_all(avq, inp, P=None, T=None, force_child=False):
     ch64 = inp.f64("children")
     par64, sq64 = oracle.build_tree(ch64, inp.dtype)
     np.testing.assert_array_equal(g["parents"], par64)
-    np.testing.assert_array_equal(g["sqnorm"], sq64.astype(np.float32))
+    check_tree_frame(inp, par64, sq64, g["frame"], g["sqnorm"])
     a, vsum, count = check_stage1(inp, par64, g["leaf"], g["vsum"], g["count"], force_child)
     err, namb = check_stage2(inp, par64, vsum, count, g, P, T)
     _say(f"  max|dY|={err:.3e} ambiguous keys={a['n_ambiguous']} tiles={namb} "
@@ -138,9 +155,9 @@ def test_stage2_on_summed_partial_aggregates(avq):
     _say(f"summed partial aggregates: {inp.name} H={inp.H} N={inp.N}")
     ch = to_dev(inp.children, inp.dtype)
     K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
-    parents, sq = avq.build_tree(ch)
+    parents, sq, fr = avq.build_tree(ch)
     cut = 4321
-    parts = [avq.assign_aggregate(K[:, :, a:b].contiguous(), V[:, :, a:b].contiguous(), parents, ch, sq,
+    parts = [avq.assign_aggregate(K[:, :, a:b].contiguous(), V[:, :, a:b].contiguous(), parents, ch, sq, fr,
                                   want_leaf=True) for a, b in ((0, cut), (cut, inp.N))]
     vsum = parts[0][0] + parts[1][0]
     count = parts[0][1] + parts[1][1]
@@ -311,8 +328,8 @@ def test_constant_values_give_constant_output(avq):
     for P in (0, 16, 256):
         ch = to_dev(inp.children, "bf16")
         K, V, Q = (to_dev(x, "bf16") for x in (inp.K, inp.V, inp.Q))
-        parents, sq = avq.build_tree(ch)
-        vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq)
+        parents, sq, fr = avq.build_tree(ch)
+        vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq, fr)
         Y, _, _ = avq.attention_fwd(Q, parents, ch, vsum, count, P, 128, inp.scale)
         torch.cuda.synchronize()
         assert np.abs(tensor_to_f64(Y, "bf16") - 0.75).max() <= 4e-3
@@ -325,10 +342,10 @@ def test_forward_equals_the_stages(avq):
     ch = to_dev(inp.children, inp.dtype)
     K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
     Y1 = avq.forward(Q, K, V, ch, inp.P, inp.T, inp.scale)
-    parents, sq = avq.build_tree(ch)
-    vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq)
+    parents, sq, fr = avq.build_tree(ch)
+    vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq, fr)
     Y2, _, _ = avq.attention_fwd(Q, parents, ch, vsum, count, inp.P, inp.T, inp.scale)
-    Y3 = avq.forward(Q, K, V, ch, inp.P, inp.T, inp.scale, tree=(parents, sq))
+    Y3 = avq.forward(Q, K, V, ch, inp.P, inp.T, inp.scale, tree=(parents, sq, fr))
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2) and torch.equal(Y1, Y3)
 
@@ -342,10 +359,10 @@ def test_repeated_runs_are_bitwise_identical(avq):
     ch = to_dev(inp.children, inp.dtype)
     K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
     Kb, Vb, Qb = (torch.flip(x, dims=[2]).contiguous() for x in (K, V, Q))
-    parents, sq = avq.build_tree(ch)
+    parents, sq, fr = avq.build_tree(ch)
     ref = None
     for it in range(12):
-        vsum, count, leaf = avq.assign_aggregate(K, V, parents, ch, sq, want_leaf=True)
+        vsum, count, leaf = avq.assign_aggregate(K, V, parents, ch, sq, fr, want_leaf=True)
         Y, sel, imp = avq.attention_fwd(Q, parents, ch, vsum, count, inp.P, inp.T, inp.scale,
                                         want_sel=True, want_importance=True)
         got = dict(vsum=vsum, count=count, leaf=leaf, Y=Y, sel=sel, imp=imp)
@@ -355,7 +372,7 @@ def test_repeated_runs_are_bitwise_identical(avq):
         else:
             for k in ref:
                 assert torch.equal(ref[k], got[k]), (it, k)
-        avq.forward(Qb, Kb, Vb, ch, inp.P, inp.T, inp.scale, tree=(parents, sq))
+        avq.forward(Qb, Kb, Vb, ch, inp.P, inp.T, inp.scale, tree=(parents, sq, fr))
     torch.cuda.synchronize()
 
 
@@ -364,8 +381,8 @@ def test_invalid_arguments_raise(avq):
     inp = synth.generate("vit-b", B=1, H=1, N=256, M0=8)
     ch = to_dev(inp.children, "bf16")
     K, V, Q = (to_dev(x, "bf16") for x in (inp.K, inp.V, inp.Q))
-    parents, sq = avq.build_tree(ch)
-    vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq)
+    parents, sq, fr = avq.build_tree(ch)
+    vsum, count, _ = avq.assign_aggregate(K, V, parents, ch, sq, fr)
     with pytest.raises(avq.AvqError, match="INVALID_ARG"):
         avq.attention_fwd(Q, parents, ch, vsum, count, 9, 128, inp.scale)   # P > M0
     with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
@@ -391,7 +408,55 @@ def test_invalid_arguments_raise(avq):
         avq.attention_fwd(Q, parents, ch, vsum, count, 2, 128, inp.scale,
                           workspace=torch.empty(64, dtype=torch.uint8, device=DEV))
     with pytest.raises(avq.AvqError, match="do not match"):
-        avq.assign_aggregate(K, V, parents, ch, sq, out=(vsum[:, :, :-1].contiguous(), count))
+        avq.assign_aggregate(K, V, parents, ch, sq, fr, out=(vsum[:, :, :-1].contiguous(), count))
     with pytest.raises(avq.AvqError, match="too small"):
-        avq.assign_aggregate(K, V, parents, ch, sq, workspace=torch.empty(64, dtype=torch.uint8, device=DEV))
+        avq.assign_aggregate(K, V, parents, ch, sq, fr, workspace=torch.empty(64, dtype=torch.uint8, device=DEV))
     torch.cuda.synchronize()
+
+
+def _near_tie_keys(inp, offset, seed):
+    """Keys near the midpoint of two children of one parent (60 %) or of two
+    parents (20 %), the rest as generated; then the children and the keys are
+    translated by `offset` in every coordinate (queries are not, so the
+    logits keep their size).  The oracle's leaves do not depend on the
+    translation; a kernel that forms ||c||^2 - 2 k.c loses precision in
+    proportion to ||k||^2."""
+    rng = np.random.default_rng(seed)
+    ch = inp.f64("children")
+    par = ch.mean(axis=2)
+    K = inp.f64("K")
+    B, H, N, d = K.shape
+    M0, C = inp.M0, inp.C
+    u = rng.random((B, H, N))
+    t = rng.uniform(0.47, 0.53, size=(B, H, N, 1))
+    p = rng.integers(0, M0, size=(B, H, N))
+    c1 = rng.integers(0, C, size=(B, H, N))
+    c2 = (c1 + rng.integers(1, C, size=(B, H, N))) % C
+    p2 = (p + rng.integers(1, max(M0, 2), size=(B, H, N))) % M0
+    hh = np.arange(H)[None, :, None]
+    child_mid = ch[hh, p, c1] + t * (ch[hh, p, c2] - ch[hh, p, c1])
+    parent_mid = par[hh, p] + t * (par[hh, p2] - par[hh, p])
+    noise = 0.01 * rng.standard_normal(K.shape)
+    K = np.where((u < 0.6)[..., None], child_mid + noise, np.where((u < 0.8)[..., None], parent_mid + noise, K))
+    inp.children = synth.to_storage(ch + offset, inp.dtype)
+    inp.K = synth.to_storage(K + offset, inp.dtype)
+    return inp
+
+
+@pytest.mark.parametrize("dtype,d,C,offset", [("f32", 64, 8, 0.0), ("f32", 64, 8, 8.0), ("bf16", 64, 8, 8.0),
+                                              ("f32", 64, 8, 32.0), ("bf16", 64, 8, 32.0),
+                                              ("bf16", 128, 16, 32.0), ("f32", 128, 4, 32.0)])
+def test_near_ties_on_a_translated_codebook(avq, dtype, d, C, offset):
+    inp = synth.generate("vit-b", B=1, H=2, N=3000, d=d, M0=48, C=C, P=6, T=64, dtype=dtype,
+                         seed=71 + int(offset) + d)
+    inp = _near_tie_keys(inp, offset, seed=5 + int(offset))
+    r = check_all(avq, inp)
+    assert r["g"]["frame"].any() == (offset >= 8.0)   # offset codebooks are compared in a moved frame
+    # the case must actually hold keys close to a tie that are still decided
+    ch64 = inp.f64("children")
+    par64, _ = oracle.build_tree(ch64, dtype)
+    a = oracle.assign(inp.f64("K"), par64, ch64)
+    g = np.minimum(a["gap_parent"], a["gap_leaf"])
+    close = ((g >= 1e-4) & (g < 1e-2)).sum()
+    _say(f"  keys with a top-2 gap in [1e-4, 1e-2): {close}")
+    assert close > 50

@@ -43,13 +43,13 @@ def _compare(avq, inp, force):
          f"d={inp.d} M0={inp.M0} C={inp.C} force_child={force}")
     ch = _dev(inp.children, inp.dtype)
     K, V = _dev(inp.K, inp.dtype), _dev(inp.V, inp.dtype)
-    parents, sq = avq.build_tree(ch)
-    ref_v, ref_c, ref_l = avq.assign_aggregate(K, V, parents, ch, sq, force_child=force, want_leaf=True)
+    parents, sq, fr = avq.build_tree(ch)
+    ref_v, ref_c, ref_l = avq.assign_aggregate(K, V, parents, ch, sq, fr, force_child=force, want_leaf=True)
     S = inp.M0 * (1 + inp.C)
     vsum = torch.full((inp.B, inp.H, S, inp.d), float("nan"), dtype=torch.float32, device=DEV)
     count = torch.full((inp.B, inp.H, S), -7, dtype=torch.int32, device=DEV)
     leaf = torch.full((inp.B, inp.H, inp.N), -7, dtype=torch.int32, device=DEV)
-    avq.assign_aggregate_noalloc(K, V, parents, ch, sq, (vsum, count), force_child=force, leaf=leaf)
+    avq.assign_aggregate_noalloc(K, V, parents, ch, sq, fr, (vsum, count), force_child=force, leaf=leaf)
     torch.cuda.synchronize()
     assert torch.equal(vsum, ref_v)
     assert torch.equal(count, ref_c)
@@ -69,10 +69,10 @@ def test_noalloc_refuses_shapes_past_the_scratch(avq):
     assert avq.assign_aggregate_workspace_size(B, H, N, M0, C, d) > avq.NOALLOC_SCRATCH_BYTES
     K = torch.zeros((B, H, N, d), dtype=torch.bfloat16, device=DEV)
     ch = torch.zeros((H, M0, C, d), dtype=torch.bfloat16, device=DEV)
-    parents, sq = avq.build_tree(ch)
+    parents, sq, fr = avq.build_tree(ch)
     S = M0 * (1 + C)
     out = (torch.empty((B, H, S, d), dtype=torch.float32, device=DEV),
            torch.empty((B, H, S), dtype=torch.int32, device=DEV))
     with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
-        avq.assign_aggregate_noalloc(K, K, parents, ch, sq, out)
+        avq.assign_aggregate_noalloc(K, K, parents, ch, sq, fr, out)
     torch.cuda.synchronize()
