@@ -21,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libavq.so")
+PROBES = os.path.join(PKG, "probes")
+PROBE_LIB = os.path.join(PKG, "libavq_peaks.so")   # throughput probes for bench.py --peaks
 ARCH = "gfx950"
 
 
@@ -73,8 +75,17 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    # the throughput probes are a separate library: bench.py loads them, the
+    # AVQ library does not contain them
+    psrc = os.path.join(PROBES, "peaks.hip")
+    ptmp = PROBE_LIB + f".tmp{os.getpid()}"
+    cmd = [_hipcc(), *COMMON, "-shared", psrc, "-o", ptmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe library build failed:\n" + r.stdout + r.stderr)
+    os.replace(ptmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources, and {PROBE_LIB}")
     return LIB
 
 

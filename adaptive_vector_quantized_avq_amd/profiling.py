@@ -3,6 +3,10 @@
     python -m adaptive_vector_quantized_avq_amd.profiling kernels STATS_CSV CMD OUT_TXT
         per-kernel call count and mean duration from --kernel-trace --stats
 
+    python -m adaptive_vector_quantized_avq_amd.profiling counters COUNTER_CSV CMD OUT_TXT
+        per-kernel mean of every counter in one --pmc run (e.g. the SQ_*
+        instruction and busy-cycle counters)
+
     python -m adaptive_vector_quantized_avq_amd.profiling traffic FETCH_CSV WRITE_CSV WORKLOAD CMD
         HBM bytes per launch of the stage kernels from two --pmc runs
         (FETCH_SIZE, then WRITE_SIZE), calibrated against the plain 256 MiB
@@ -28,15 +32,16 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # stage kernels and the sources their code comes from (for the digest that
 # ties a traffic measurement to the kernel it was taken on)
+_HDRS = ["adaptive_vector_quantized_avq_amd/csrc/avq_device.h",
+         "adaptive_vector_quantized_avq_amd/csrc/avq_kernels.h"]
 KERNEL_SOURCES = {
-    "attention_kernel": ["adaptive_vector_quantized_avq_amd/csrc/attention_fwd.hip",
-                         "adaptive_vector_quantized_avq_amd/csrc/avq_device.h"],
-    "assign_parent_kernel": ["adaptive_vector_quantized_avq_amd/csrc/assign_parent.hip",
-                             "adaptive_vector_quantized_avq_amd/csrc/avq_device.h"],
-    "refine_aggregate_kernel": ["adaptive_vector_quantized_avq_amd/csrc/refine_aggregate.hip",
-                                "adaptive_vector_quantized_avq_amd/csrc/avq_device.h"],
+    "attention_kernel": ["adaptive_vector_quantized_avq_amd/csrc/attention_fwd.hip", *_HDRS],
+    "pack_aggregates_kernel": ["adaptive_vector_quantized_avq_amd/csrc/pack_aggregates.hip", *_HDRS],
+    "assign_parent_kernel": ["adaptive_vector_quantized_avq_amd/csrc/assign_parent.hip", *_HDRS],
+    "refine_aggregate_kernel": ["adaptive_vector_quantized_avq_amd/csrc/refine_aggregate.hip", *_HDRS],
+    "exact_attention_kernel": ["adaptive_vector_quantized_avq_amd/csrc/exact_attention.hip", *_HDRS],
 }
-COPY_KERNEL = "copy"          # substring of the device-copy kernel's name
+COPY_KERNEL = "probe_copy_kernel"   # the calibration copy (bench.py --copy-probe)
 COPY_BYTES = 256 << 20        # bytes read and bytes written per copy launch
 
 
@@ -52,7 +57,7 @@ def short_name(name: str) -> str:
     for k in KERNEL_SOURCES:
         if k in name:
             return k
-    if COPY_KERNEL in name.lower():
+    if COPY_KERNEL in name:
         return COPY_KERNEL
     return name.split("(")[0][:60]
 
@@ -84,11 +89,25 @@ def cmd_kernels(stats_csv: str, cmd: str, out_txt: str) -> None:
     print("\n".join(lines))
 
 
+def cmd_counters(csv_path: str, cmd: str, out_txt: str) -> None:
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        acc[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = ["# rocprofv3 --pmc (one pass; mean per dispatch)", f"# command: {cmd}", ""]
+    for k in sorted(acc):
+        lines.append(f"{k}  ({len(next(iter(acc[k].values())))} dispatches)")
+        for c in sorted(acc[k]):
+            v = acc[k][c]
+            lines.append(f"  {c:32s} {sum(v) / len(v):16.1f}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cmd_traffic(fetch_csv: str, write_csv: str, workload: str, cmd: str) -> None:
     fetch = counter_means(fetch_csv, "FETCH_SIZE")
     write = counter_means(write_csv, "WRITE_SIZE")
     if COPY_KERNEL not in fetch or COPY_KERNEL not in write:
-        raise SystemExit("no copy-kernel dispatch in the counter files (run bench.py with --copy-probe)")
+        raise SystemExit("no probe_copy_kernel dispatch in the counter files (run bench.py with --copy-probe)")
     # counters are in KiB per dispatch; scale so the copy reads and writes
     # exactly COPY_BYTES
     f_scale = COPY_BYTES / (fetch[COPY_KERNEL][1] * 1024.0)
@@ -121,6 +140,8 @@ def cmd_traffic(fetch_csv: str, write_csv: str, workload: str, cmd: str) -> None
 if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "kernels" and len(sys.argv) == 5:
         cmd_kernels(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif len(sys.argv) >= 2 and sys.argv[1] == "counters" and len(sys.argv) == 5:
+        cmd_counters(sys.argv[2], sys.argv[3], sys.argv[4])
     elif len(sys.argv) >= 2 and sys.argv[1] == "traffic" and len(sys.argv) == 6:
         cmd_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
     else:

@@ -4,15 +4,17 @@
 
 A step is one whole forward over one batch of synthetic inputs already
 resident in HBM: stage 1 (avq_assign_aggregate: two kernels) then stage 2
-(avq_attention_fwd: one kernel).  The frozen tree (avq_build_tree) is built
+(avq_attention_fwd: the operand pack, then the attention kernel).  The frozen tree (avq_build_tree) is built
 once before timing, as it is once per codebook.  Input sets rotate between
 steps (4 sets, 768 MiB at the default workload) so that no step is served
 from the 256 MiB Infinity Cache.
 
 Prints ONE JSON line: the headline metric (tokens/s/head = B*N*H / step
-time), the roofline of the dominant kernel measured with HIP events on the
-stream the kernels run on, and the CPU oracle timed on a bounded sample on
-this host's cores.
+time), the roofline of the dominant stage measured with HIP events on the
+stream the kernels run on, the in-repo exact softmax attention timed at the
+same shape as context, and the CPU oracle timed on a bounded sample on this
+host's cores, whose outputs are then compared with the GPU's on the same
+inputs (oracle_check).
 """
 
 from __future__ import annotations
@@ -73,8 +75,7 @@ def measured_traffic(kernel, workload):
 def cpu_baseline(inp, P, heads):
     """The CPU oracle, as it stands, on the first `heads` heads of batch 0 of
     the workload: stage 1 on all their keys, stage 2 on all their query
-    tiles."""
-    import numpy as np
+    tiles.  Returns the timing record and the oracle's outputs."""
     import oracle
     import synth
 
@@ -91,13 +92,113 @@ def cpu_baseline(inp, P, heads):
     a = oracle.assign(K64, par, ch, threads=threads)
     vsum, count = oracle.aggregate(V64, a["leaf"], inp.M0, inp.C, threads=threads)
     t1 = time.perf_counter()
-    oracle.attention(Q64, par, ch, vsum, count, P, inp.T, inp.scale, threads=threads)
+    Y, imp, sel = oracle.attention(Q64, par, ch, vsum, count, P, inp.T, inp.scale, threads=threads)
     t2 = time.perf_counter()
     tok = heads * inp.N
-    return dict(value=tok / (t2 - t0), unit="tokens/s/head", cores=threads, kind="oracle",
-                sample=f"{heads} of {inp.B * inp.H} (b,h) units of {inp.name}: stage 1 on all "
-                       f"{inp.N} keys and stage 2 on all {inp.ntiles} query tiles of each, fp64",
-                stage1_s=round(t1 - t0, 3), stage2_s=round(t2 - t1, 3))
+    rec = dict(value=tok / (t2 - t0), unit="tokens/s/head", cores=threads, kind="oracle",
+               sample=f"{heads} of {inp.B * inp.H} (b,h) units of {inp.name}: stage 1 on all "
+                      f"{inp.N} keys and stage 2 on all {inp.ntiles} query tiles of each, fp64",
+               stage1_s=round(t1 - t0, 3), stage2_s=round(t2 - t1, 3))
+    return rec, dict(a=a, count=count, Y=Y, imp=imp, sel=sel)
+
+
+AMBIG = 1e-4   # relative top-2 gap below which two results are both correct
+
+
+def oracle_comparison(inp, P, ref, g):
+    """The GPU's outputs on the timed inputs (input set 0, batch 0, the
+    heads the oracle ran on) against the oracle's: leaves outside the
+    near-tie band, counts, selected sets, and the largest |dY| over the
+    tiles whose selection agrees."""
+    import numpy as np
+    heads = ref["Y"].shape[1]
+    M0 = inp.M0
+    gap = np.minimum(ref["a"]["gap_parent"], ref["a"]["gap_leaf"])
+    amb_keys = gap < AMBIG
+    leaf = g["leaf"][:1, :heads]
+    leaf_bad = int(((leaf != ref["a"]["leaf"]) & ~amb_keys).sum())
+    cnt = g["count"][:1, :heads]
+    w = ref["imp"]
+    if 0 < P < M0:
+        srt = -np.sort(-w, axis=-1)
+        wp, wn = srt[..., P - 1], srt[..., P]
+        amb_tiles = ((wp - wn) <= AMBIG * wp) & ~((wp == 0) & (wn == 0))
+    else:
+        amb_tiles = np.zeros(w.shape[:-1], dtype=bool)
+    same = (np.sort(g["sel"][:1, :heads], axis=-1) == np.sort(ref["sel"], axis=-1)).all(axis=-1)
+    rows = np.repeat(same, inp.T, axis=-1)[..., :inp.N]
+    dY = np.abs(g["Y"][:1, :heads] - ref["Y"])
+    return dict(
+        sample=f"input set 0, batch 0, {heads} head(s)",
+        max_abs_err=float(dY[rows].max()) if rows.any() else None,
+        tolerance=2e-2 if inp.dtype == "bf16" else 1e-4,
+        n_ambiguous_keys=int(amb_keys.sum()),
+        leaf_mismatch_outside_band=leaf_bad,
+        count_mismatch_slots=int((cnt != ref["count"]).sum()),
+        n_ambiguous_tiles=int(amb_tiles.sum()),
+        selection_mismatch_tiles=int((~same).sum()),
+        selection_mismatch_outside_band=int((~same & ~amb_tiles).sum()),
+        sum_residual=int(g["count"][..., :M0].sum() - g["count"][..., M0:].sum()),
+    )
+
+
+def _probe_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "adaptive_vector_quantized_avq_amd", "libavq_peaks.so"))
+    lib.avq_probe_launch.restype = ctypes.c_int
+    lib.avq_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.avq_probe_copy.restype = ctypes.c_int
+    lib.avq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    return lib
+
+
+def copy_probe(torch, dev, nbytes=256 << 20, launches=5):
+    """A kernel of known traffic for calibrating the profiler's byte
+    counters: probe_copy_kernel reads and writes exactly nbytes per launch."""
+    import ctypes
+    lib = _probe_lib()
+    xa = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+    ya = torch.empty_like(xa)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(launches):
+        if lib.avq_probe_copy(ctypes.c_void_p(xa.data_ptr()), ctypes.c_void_p(ya.data_ptr()), nbytes, stream):
+            raise RuntimeError("copy probe failed to launch")
+    c1.record()
+    torch.cuda.synchronize()
+    return {"kernel": "probe_copy_kernel", "bytes_read": nbytes, "bytes_written": nbytes,
+            "launches": launches, "GBps": round(2 * nbytes * launches / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)}
+
+
+def measure_peaks(torch, dev):
+    """Rates measured on this GPU: bf16 MFMA (TFLOP/s), fp32 FMA (TFLOP/s),
+    v_exp_f32 (exponentials/s), and a 1 GiB device copy (GB/s, read + write).
+    4096 blocks of 256 threads: 16 waves per CU, 4 per SIMD."""
+    import ctypes
+    lib = _probe_lib()
+    blocks = 4096
+    outb = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    res = {}
+    # (kind, iterations, work per lane-iteration, unit scale)
+    for name, kind, iters, per in (("mfma_bf16_TFLOPs", 0, 4000, 16 * 16 * 32 * 2 * 8 / 64),
+                                   ("fma_f32_TFLOPs", 1, 20000, 2 * 8),
+                                   ("exp_f32_per_s", 2, 20000, 8)):
+        for rep in range(2):   # the first launch warms up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = lib.avq_probe_launch(kind, blocks, iters, ctypes.c_void_p(outb.data_ptr()), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"probe {name} failed to launch")
+        secs = e0.elapsed_time(e1) * 1e-3
+        work = blocks * 256 * iters * per
+        res[name] = round(work / secs / (1e12 if "TFLOPs" in name else 1.0), 1 if "TFLOPs" in name else -9)
+    res["copy_GBps"] = copy_probe(torch, dev, nbytes=1 << 30)["GBps"]
+    return res
 
 
 def main():
@@ -111,11 +212,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads of batch 0 the CPU oracle runs on (0 = all of them)")
-    ap.add_argument("--exact-context", action="store_true",
-                    help="also time the in-repo exact softmax attention at the same shape")
+    ap.add_argument("--no-exact-context", action="store_true",
+                    help="skip timing the in-repo exact softmax attention at the same shape")
+    ap.add_argument("--peaks", action="store_true",
+                    help="also measure the chip's bf16 MFMA, fp32 FMA and v_exp_f32 rates and the "
+                         "device-copy bandwidth (throughput probes, libavq_peaks.so)")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain 256 MiB device copy 5 times (a kernel of known "
-                         "traffic, to calibrate the profiler's byte counters)")
+                    help="also run a plain 256 MiB device copy kernel 5 times (known traffic, "
+                         "to calibrate the profiler's byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -123,7 +227,7 @@ def main():
               "multi-GPU split is described in DESIGN.md but not built", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np  # noqa: F401
+    import numpy as np
     import torch
 
     import adaptive_vector_quantized_avq_amd as avq
@@ -213,23 +317,30 @@ def main():
     s2_tfs = alg["s2_flops"] / (s2_ms * 1e-3) / 1e12
     s2_gbs = alg["s2_bytes"] / (s2_ms * 1e-3) / 1e9
     s2_bound = "mfma" if alg["s2_flops"] / (peak_mf * 1e12) >= alg["s2_bytes"] / (HBM_PEAK_GBS * 1e9) else "hbm"
+    tr = {k: measured_traffic(k, inp.name) for k in
+          ("assign_parent_kernel", "refine_aggregate_kernel", "pack_aggregates_kernel", "attention_kernel")}
+
+    def total(*ks):
+        return None if any(tr[k] is None for k in ks) else sum(tr[k] for k in ks)
+
+    s1_traffic = total("assign_parent_kernel", "refine_aggregate_kernel")
+    s2_traffic = total("pack_aggregates_kernel", "attention_kernel")
     if s2_ms >= s1_ms:
+        # avq_attention_fwd is two kernels: the operand pack, then attention
+        kname = "attention_fwd (pack_aggregates_kernel + attention_kernel)"
         if s2_bound == "mfma":
-            roof = dict(kernel="attention_kernel", bound="mfma", achieved=round(s2_tfs, 2),
+            roof = dict(kernel=kname, bound="mfma", achieved=round(s2_tfs, 2),
                         peak=peak_mf, unit="TFLOP/s", frac=round(s2_tfs / peak_mf, 4))
         else:
-            roof = dict(kernel="attention_kernel", bound="hbm", achieved=round(s2_gbs, 1),
+            roof = dict(kernel=kname, bound="hbm", achieved=round(s2_gbs, 1),
                         peak=HBM_PEAK_GBS, unit="GB/s", frac=round(s2_gbs / HBM_PEAK_GBS, 4))
-        roof["traffic"] = measured_traffic("attention_kernel", inp.name)
+        roof["traffic"] = s2_traffic
         roof["traffic_unit"] = "bytes per launch"
         roof["launch_ms"] = round(s2_ms, 5)
     else:
-        t1 = measured_traffic("assign_parent_kernel", inp.name)
-        t2 = measured_traffic("refine_aggregate_kernel", inp.name)
         roof = dict(kernel="assign_aggregate (assign_parent_kernel + refine_aggregate_kernel)", bound="hbm",
                     achieved=round(s1_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(s1_gbs / HBM_PEAK_GBS, 4),
-                    traffic=(t1 + t2) if (t1 is not None and t2 is not None) else None,
+                    frac=round(s1_gbs / HBM_PEAK_GBS, 4), traffic=s1_traffic,
                     traffic_unit="bytes per launch", launch_ms=round(s1_ms, 5))
 
     out = {
@@ -250,20 +361,40 @@ def main():
         "roofline": roof,
         "stages": {
             "assign_aggregate": {"ms": round(s1_ms, 5), "alg_bytes": alg["s1_bytes"],
-                                 "GBps": round(s1_gbs, 1), "frac_hbm": round(s1_gbs / HBM_PEAK_GBS, 4)},
+                                 "GBps": round(s1_gbs, 1), "frac_hbm": round(s1_gbs / HBM_PEAK_GBS, 4),
+                                 "counter_bytes": s1_traffic,
+                                 "counter_GBps": None if s1_traffic is None else
+                                 round(s1_traffic / (s1_ms * 1e-3) / 1e9, 1)},
             "attention_fwd": {"ms": round(s2_ms, 5), "alg_flops": alg["s2_flops"],
                               "alg_bytes": alg["s2_bytes"], "TFLOPs": round(s2_tfs, 2),
                               "GBps": round(s2_gbs, 1), "bound": s2_bound,
                               "frac_mfma": round(s2_tfs / peak_mf, 4),
                               "frac_hbm": round(s2_gbs / HBM_PEAK_GBS, 4),
                               "alg_exps": alg["s2_exps"],
-                              "exp_bound_ms": round(alg["s2_exps"] / EXP_PEAK_PER_S * 1e3, 5)},
+                              "exp_bound_ms": round(alg["s2_exps"] / EXP_PEAK_PER_S * 1e3, 5),
+                              "counter_bytes": s2_traffic,
+                              "counter_GBps": None if s2_traffic is None else
+                              round(s2_traffic / (s2_ms * 1e-3) / 1e9, 1)},
         },
+        "counter_bytes_per_kernel": tr,
         "host_wall_ms_per_step": round(wall / args.steps * 1e3, 5),
         "ms_per_step_with_stage_events": round(ms_step_instrumented, 5),
     }
 
-    if args.exact_context:
+    # outputs on input set 0 (the unrotated workload) for the oracle check
+    Q, K, V = sets[0]
+    vs0, cn0, lf0 = avq.assign_aggregate(K, V, parents, ch, sq, fr, want_leaf=True)
+    Y0, sel0, imp0 = avq.attention_fwd(Q, parents, ch, vs0, cn0, P, inp.T, inp.scale,
+                                       want_sel=True, want_importance=True)
+    torch.cuda.synchronize()
+    if inp.dtype == "bf16":
+        y0 = synth.bf16_bits_to_f64(Y0.cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+    else:
+        y0 = Y0.cpu().double().numpy()
+    g0 = dict(leaf=lf0.cpu().numpy(), count=cn0.cpu().numpy(), sel=sel0.cpu().numpy(), Y=y0)
+    del vs0, Y0, imp0
+
+    if not args.no_exact_context:
         Q, K, V = sets[0]
         for _ in range(2):
             avq.exact_attention_fwd(Q, K, V, inp.scale, out=Y)
@@ -275,28 +406,23 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ex_ms = e0.elapsed_time(e1) / reps
+        out["exact_baseline_ms"] = round(ex_ms, 4)
         out["exact_attention_context"] = {
-            "ms": round(ex_ms, 4),
+            "ms": round(ex_ms, 4), "kernel": "exact_attention_kernel (in-repo flash-style, bf16 MFMA)",
             "TFLOPs": round(4.0 * N * N * d * B * H / (ex_ms * 1e-3) / 1e12, 1),
             "speedup_avq": round(ex_ms / ms_step, 1)}
 
     if args.copy_probe:
-        nbytes = 256 << 20
-        xa = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
-        ya = torch.empty_like(xa)
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        for _ in range(5):
-            ya.copy_(xa)
-        c1.record()
-        torch.cuda.synchronize()
-        out["copy_probe"] = {"bytes_read": nbytes, "bytes_written": nbytes, "launches": 5,
-                             "GBps": round(2 * nbytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)}
+        out["copy_probe"] = copy_probe(torch, dev)
+
+    if args.peaks:
+        out["measured_peaks"] = measure_peaks(torch, dev)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
-        out["cpu_baseline"] = cpu_baseline(inp, P, max(1, min(args.cpu_heads or H, H)))
+        rec, ref = cpu_baseline(inp, P, max(1, min(args.cpu_heads or H, H)))
+        out["cpu_baseline"] = rec
+        out["oracle_check"] = oracle_comparison(inp, P, ref, g0)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -31,8 +31,12 @@ def test_bench_json_line():
     d = _run("--workload", "vit-b", "--steps", "3", "--warmup", "1", "--sets", "2", "--cpu-heads", "1")
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
               "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
-              "roofline", "cpu_baseline"):
+              "roofline", "cpu_baseline", "oracle_check", "exact_baseline_ms"):
         assert k in d, k
+    oc = d["oracle_check"]
+    assert oc["max_abs_err"] is not None and oc["max_abs_err"] <= oc["tolerance"]
+    assert oc["leaf_mismatch_outside_band"] == 0 and oc["selection_mismatch_outside_band"] == 0
+    assert d["exact_baseline_ms"] > 0
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
     assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
     assert d["config"]["workload"] == "vit-b" and d["dtype"] == "bf16"
