@@ -114,9 +114,18 @@ def round_to(x, dtype: str) -> np.ndarray:
 
 def build_tree(children, dtype: str):
     """children [H][M0][C][d] float64 -> (parents [H][M0][d] rounded to dtype,
-    sqnorm [H][M0(1+C)] float64: parents first, then children)."""
+    sqnorm [H][M0(1+C)] float64: parents first, then children).
+
+    A flat codebook (plain VQ, no children) is passed as [H][M0][d]: its
+    codewords are the parents, C = 0."""
     lib = _load()
     children = _f64(children)
+    if children.ndim == 3:
+        H, M0, d = children.shape
+        sq = np.empty((H, M0))
+        for h in range(H):
+            lib.avqo_sqnorm(_p(children[h], _dp), M0, d, _p(sq[h], _dp))
+        return children.copy(), sq
     H, M0, C, d = children.shape
     parents = np.empty((H, M0, d))
     sq = np.empty((H, M0 * (1 + C)))
@@ -130,13 +139,18 @@ def build_tree(children, dtype: str):
     return parents, sq
 
 
+def _tree_shape(children):
+    """(M0, C) of a tree's children array, C = 0 for a flat [H][M0][d] codebook."""
+    return (children.shape[1], 0) if children.ndim == 3 else (children.shape[1], children.shape[2])
+
+
 def assign(K, parents, children, force_child: bool = False, threads: Optional[int] = None):
     """K [B][H][N][d] -> dict of [B][H][N] arrays: pstar, leaf (int32),
     gap_parent, gap_leaf (float64 relative top-2 gaps)."""
     lib = _load()
     K, parents, children = _f64(K), _f64(parents), _f64(children)
     B, H, N, d = K.shape
-    M0, C = children.shape[1], children.shape[2]
+    M0, C = _tree_shape(children)
     out = {k: np.empty((B, H, N), dtype=np.int32) for k in ("pstar", "leaf")}
     out.update({k: np.empty((B, H, N)) for k in ("gap_parent", "gap_leaf")})
 
@@ -181,7 +195,7 @@ def attention(Q, parents, children, vsum, count, P: int, T: int, scale: float,
     Q, parents, children, vsum = _f64(Q), _f64(parents), _f64(children), _f64(vsum)
     count = np.ascontiguousarray(count, dtype=np.int64)
     B, H, N, d = Q.shape
-    M0, C = children.shape[1], children.shape[2]
+    M0, C = _tree_shape(children)
     nt = -(-N // T)
     t0, t1 = tiles if tiles is not None else (0, nt)
     Y = np.full((B, H, N, d), np.nan)

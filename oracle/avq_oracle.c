@@ -113,6 +113,7 @@ static double rel_gap(const double *v, int n)
 /*     child is closer than the cached parent distance).                */
 /*     leaf = p* (key stays at its parent) or M0 + p*C + c*.            */
 /*     force_child != 0 treats the parent distance as +infinity.        */
+/*     C == 0 is flat VQ (Sec. 3.2): the nearest codeword is the leaf.  */
 /*     gap_parent: relative top-2 gap over the M0 parents;              */
 /*     gap_leaf:   relative top-2 gap over {p*} U children(p*).         */
 /* ------------------------------------------------------------------ */
@@ -130,15 +131,20 @@ void avqo_assign(const double *K /*[N][d]*/, int64_t N, int d,
             Dp[p] = sqdist(key, parents + (int64_t)p * d, d);
             if (Dp[p] < Dp[best]) best = p;
         }
+        pstar[k] = best;
+        if (gap_parent) gap_parent[k] = rel_gap(Dp, M0);
+        if (C == 0) {                   /* flat codebook: the parent is the leaf */
+            leaf[k] = best;
+            if (gap_leaf) gap_leaf[k] = INFINITY;
+            continue;
+        }
         int cbest = 0;
         for (int c = 0; c < C; ++c) {
             Dl[c] = sqdist(key, children + ((int64_t)best * C + c) * d, d);
             if (Dl[c] < Dl[cbest]) cbest = c;
         }
         int to_child = force_child || Dl[cbest] < Dp[best];
-        pstar[k] = best;
         leaf[k] = to_child ? M0 + best * C + cbest : best;
-        if (gap_parent) gap_parent[k] = rel_gap(Dp, M0);
         if (gap_leaf) {
             Dl[C] = Dp[best];
             gap_leaf[k] = rel_gap(Dl, force_child ? C : C + 1);

@@ -8,6 +8,7 @@ arithmetic: no distances, no assignment, no aggregation, no softmax.
 from .generators import (  # noqa: F401
     WORKLOADS,
     WORKLOAD_ORDER,
+    EXTRA_WORKLOADS,
     Inputs,
     generate,
     generate_dyadic,

@@ -47,8 +47,14 @@ WORKLOADS = {
     # anisotropic per-leaf key spread.
     "wide-d128": dict(B=2, H=10, N=32768, d=128, M0=256, C=16, P=32, T=64,
                       dtype="bf16", keys="anisotropic", queries="clustered"),
+    # Flat VQ-attention (no children, C = 0) at the long-sequence shape: the
+    # pages' fixed-codebook baseline with M = 256 codewords (Table 2).
+    "flat-64k": dict(B=1, H=8, N=65536, d=64, M0=256, C=0, P=0, T=128,
+                     dtype="bf16", keys="uniform", queries="clustered"),
 }
 WORKLOAD_ORDER = ["tiny-f32", "vit-b", "seg-zipf", "long-64k", "wide-d128"]
+# further workloads (not among the five the parity suite sweeps by name)
+EXTRA_WORKLOADS = ["flat-64k"]
 
 CHILD_SPREAD = 0.3      # std of child offsets around their parent
 KEY_SPREAD = 0.1        # std of key noise around its generating leaf
@@ -112,11 +118,11 @@ class Inputs:
     dtype: str
     scale: float
     seed: int
-    children: np.ndarray      # [H][M0][C][d] storage dtype
+    children: np.ndarray      # [H][M0][C][d] storage dtype ([H][M0][d] for a flat codebook, C = 0)
     Q: np.ndarray             # [B][H][N][d]
     K: np.ndarray
     V: np.ndarray
-    true_leaf: np.ndarray     # [B][H][N] int32: slot id M0 + p*C + c of the generating child
+    true_leaf: np.ndarray     # [B][H][N] int32: slot of the generating leaf (M0 + p*C + c; p if C = 0)
 
     @property
     def S_tot(self) -> int:
@@ -153,12 +159,13 @@ def generate(name: str, seed: Optional[int] = None, **overrides) -> Inputs:
     spec.pop("P_sweep", None)
     spec.update(overrides)
     if seed is None:
-        seed = 1000 + WORKLOAD_ORDER.index(name)
+        seed = 1000 + (WORKLOAD_ORDER + EXTRA_WORKLOADS).index(name)
     B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]
     M0, C, P, T = spec["M0"], spec["C"], spec["P"], spec["T"]
     dtype = spec["dtype"]
     rng = np.random.Generator(np.random.PCG64(seed))
-    L = M0 * C
+    flat_vq = C == 0          # a flat codebook: the M0 codewords are the leaves
+    L = M0 if flat_vq else M0 * C
 
     parents64 = np.empty((H, M0, d))
     children64 = np.empty((H, M0, C, d))
@@ -166,10 +173,11 @@ def generate(name: str, seed: Optional[int] = None, **overrides) -> Inputs:
     aniso = [None] * H
     for h in range(H):
         par = rng.standard_normal((M0, d))
-        off = rng.normal(0.0, CHILD_SPREAD, size=(M0, C, d))
-        off -= off.mean(axis=1, keepdims=True)
         parents64[h] = par
-        children64[h] = par[:, None, :] + off
+        if not flat_vq:
+            off = rng.normal(0.0, CHILD_SPREAD, size=(M0, C, d))
+            off -= off.mean(axis=1, keepdims=True)
+            children64[h] = par[:, None, :] + off
         if spec["keys"] == "zipf":
             zipf_perm[h] = rng.permutation(L)
         elif spec["keys"] == "anisotropic":
@@ -184,7 +192,7 @@ def generate(name: str, seed: Optional[int] = None, **overrides) -> Inputs:
 
     for b in range(B):
         for h in range(H):
-            flat = children64[h].reshape(L, d)
+            flat = parents64[h] if flat_vq else children64[h].reshape(L, d)
             if spec["keys"] == "zipf":
                 rank = rng.choice(L, size=N, p=zp)
                 leaf = zipf_perm[h][rank]
@@ -204,11 +212,13 @@ def generate(name: str, seed: Optional[int] = None, **overrides) -> Inputs:
             K[b, h] = to_storage(k64, dtype)
             Q[b, h] = to_storage(q64, dtype)
             V[b, h] = to_storage(v64, dtype)
-            true_leaf[b, h] = M0 + leaf
+            true_leaf[b, h] = leaf if flat_vq else M0 + leaf
 
+    # a flat codebook is passed as [H][M0][d]: its codewords are the parents
+    codebook = parents64 if flat_vq else children64
     return Inputs(name=name, B=B, H=H, N=N, d=d, M0=M0, C=C, P=P, T=T,
                   dtype=dtype, scale=1.0 / math.sqrt(d), seed=seed,
-                  children=to_storage(children64, dtype), Q=Q, K=K, V=V,
+                  children=to_storage(codebook, dtype), Q=Q, K=K, V=V,
                   true_leaf=true_leaf)
 
 

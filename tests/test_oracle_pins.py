@@ -380,3 +380,56 @@ def test_generators_are_deterministic_per_seed(name):
     d2 = synth.generate_dyadic(3, N=100)
     for f in ("children", "Q", "K", "V"):
         np.testing.assert_array_equal(getattr(d1, f), getattr(d2, f))
+
+
+# ---------------------------------------------------------------- flat VQ (C = 0)
+
+@pytest.mark.parametrize("seed", range(4))
+def test_flat_vq_assignment_brute_force(seed):
+    # plain VQ (Sec. 3.2): every key goes to its nearest codeword, ties to the
+    # lowest index; small integer grids make exact ties common
+    rnd = random.Random(100 + seed)
+    M0, d, N = rnd.randint(1, 6), rnd.randint(1, 4), 80
+    cb = [[rnd.randint(-3, 3) for _ in range(d)] for _ in range(M0)]
+    keys = [[rnd.randint(-4, 4) for _ in range(d)] for _ in range(N)]
+    par, _ = oracle.build_tree(np.array(cb, dtype=np.float64)[None], "f32")
+    a = oracle.assign(np.array(keys, dtype=np.float64)[None, None], par, par)
+    dist = lambda x, y: sum((u - v) ** 2 for u, v in zip(x, y))
+    ref = [min(range(M0), key=lambda j: (dist(k, cb[j]), j)) for k in keys]
+    assert a["leaf"][0, 0].tolist() == ref and a["pstar"][0, 0].tolist() == ref
+    assert np.isinf(a["gap_leaf"]).all()
+
+
+def test_flat_vq_recovers_generating_codeword():
+    inp = synth.generate("flat-64k", H=2, N=2048)
+    par, _ = oracle.build_tree(inp.f64("children"), inp.dtype)
+    a = oracle.assign(inp.f64("K"), par, inp.f64("children"))
+    assert (a["leaf"] == inp.true_leaf).all()
+
+
+def test_flat_vq_attention_is_key_level_vq_attention():
+    # Sec. 3.2: attention with every key replaced by its nearest codeword,
+    # summed over keys (no aggregation), equals the count-weighted attention
+    # over the codewords
+    inp = synth.generate("flat-64k", B=1, H=2, N=700, M0=24, T=64, seed=9)
+    r = oracle.forward(inp)
+    cb, Q, V = inp.f64("children"), inp.f64("Q"), inp.f64("V")
+    for h in range(inp.H):
+        ref = softmax_attention(Q[0, h], cb[h][r["pstar"][0, h]], V[0, h], inp.scale)
+        assert np.abs(r["Y"][0, h] - ref).max() < 1e-10
+    # constant-rank invariants: counts sum to N, the value sums to the total
+    assert (r["count"].sum(axis=-1) == inp.N).all()
+    np.testing.assert_allclose(r["vsum"].sum(axis=2), V.sum(axis=2), rtol=1e-12, atol=1e-9)
+
+
+def test_flat_codebook_is_the_parent_level_of_a_tree():
+    # a flat codebook made of a tree's parents gives the tree's P = 0 result
+    tree = synth.generate_dyadic(12, B=1, H=2, N=900, d=64, M0=8, C=4, P=0, T=64, dtype="f32")
+    t = oracle.forward(tree, P=0)
+    flat = synth.Inputs(**{**tree.__dict__})
+    flat.C = 0
+    flat.children = synth.to_storage(t["parents"], "f32")
+    f = oracle.forward(flat, P=0)
+    assert (f["pstar"] == t["pstar"]).all()
+    np.testing.assert_array_equal(f["count"], t["count"][..., :tree.M0])
+    assert np.abs(f["Y"] - t["Y"]).max() < 1e-12
