@@ -21,10 +21,11 @@ __all__ = [
     "build_tree", "assign_aggregate", "attention_fwd", "exact_attention_fwd",
     "assign_aggregate_workspace_size", "attention_workspace_size", "forward",
     "assign_aggregate_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "AVQ_FLAG_FORCE_CHILD",
+    "AVQ_FLAG_FORCE_CHILD", "AVQ_FLAG_UNFUSED",
 ]
 
 AVQ_FLAG_FORCE_CHILD = 1
+AVQ_FLAG_UNFUSED = 2
 NOALLOC_SCRATCH_BYTES = 16 << 20   # AVQ_NOALLOC_SCRATCH_BYTES of include/avq.h
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -118,11 +119,23 @@ def _need(t: torch.Tensor, name: str, ndim: int, dtype=None, dev=None):
         raise AvqError(f"{name} is on {t.device}, expected {dev}")
 
 
+def _tree_dims(children: torch.Tensor):
+    """(H, M0, C, d) of a tree's children [H][M0][C][d], or of a flat
+    codebook [H][M0][d] (C = 0)."""
+    if not isinstance(children, torch.Tensor) or children.dim() not in (3, 4):
+        raise AvqError("children must be [H][M0][C][d] (or a flat codebook [H][M0][d])")
+    if children.dim() == 3:
+        H, M0, d = children.shape
+        return H, M0, 0, d
+    return tuple(children.shape)
+
+
 def build_tree(children: torch.Tensor):
-    """children [H][M0][C][d] -> (parents [H][M0][d], sqnorm [H][M0(1+C)] fp32,
-    frame [H][d] fp32): the tree stage 1 reads (norms are in the frame)."""
-    _need(children, "children", 4)
-    H, M0, C, d = children.shape
+    """children [H][M0][C][d] (or a flat codebook [H][M0][d], C = 0) ->
+    (parents [H][M0][d], sqnorm [H][M0(1+C)] fp32, frame [H][d] fp32): the
+    tree stage 1 reads (norms are in the frame)."""
+    H, M0, C, d = _tree_dims(children)
+    _need(children, "children", children.dim())
     parents = torch.empty((H, M0, d), dtype=children.dtype, device=children.device)
     sqnorm = torch.empty((H, M0 * (1 + C)), dtype=torch.float32, device=children.device)
     frame = torch.empty((H, d), dtype=torch.float32, device=children.device)
@@ -151,19 +164,21 @@ def _workspace(ws, need: int, dev, name: str):
 
 def assign_aggregate(K, V, parents, children, sqnorm, frame, force_child: bool = False,
                      want_leaf: bool = False, workspace: Optional[torch.Tensor] = None,
-                     out: Optional[tuple] = None):
+                     out: Optional[tuple] = None, unfused: bool = False):
     """Stage 1.  K, V [B][H][N][d] -> (vsum [B][H][S_tot][d] fp32,
-    count [B][H][S_tot] int32, leaf [B][H][N] int32 or None)."""
+    count [B][H][S_tot] int32, leaf [B][H][N] int32 or None).  `unfused`
+    (flat codebooks only) runs the separate assign-then-scatter comparison
+    path."""
     _need(K, "K", 4)
     dev, dt = K.device, K.dtype
     _need(V, "V", 4, dt, dev)
-    _need(children, "children", 4, dt, dev)
+    Hc, M0, C, dc = _tree_dims(children)
+    _need(children, "children", children.dim(), dt, dev)
     _need(parents, "parents", 3, dt, dev)
     _need(sqnorm, "sqnorm", 2, torch.float32, dev)
     _need(frame, "frame", 2, torch.float32, dev)
     B, H, N, d = K.shape
-    M0, C = children.shape[1], children.shape[2]
-    if V.shape != K.shape or children.shape[0] != H or children.shape[3] != d or \
+    if V.shape != K.shape or Hc != H or dc != d or \
             parents.shape != (H, M0, d) or sqnorm.shape != (H, M0 * (1 + C)) or frame.shape != (H, d):
         raise AvqError("inconsistent shapes")
     S = M0 * (1 + C)
@@ -183,8 +198,8 @@ def assign_aggregate(K, V, parents, children, sqnorm, frame, force_child: bool =
     with _on(dev):
         _check(lib.avq_assign_aggregate(
             _ptr(K), _ptr(V), _ptr(parents), _ptr(children), _ptr(sqnorm), _ptr(frame), B, H, N, d, M0, C, _dt(K),
-            AVQ_FLAG_FORCE_CHILD if force_child else 0, _ptr(vsum), _ptr(count), _ptr(leaf),
-            _ptr(workspace), workspace.numel(), _stream(dev)))
+            (AVQ_FLAG_FORCE_CHILD if force_child else 0) | (AVQ_FLAG_UNFUSED if unfused else 0),
+            _ptr(vsum), _ptr(count), _ptr(leaf), _ptr(workspace), workspace.numel(), _stream(dev)))
     return vsum, count, leaf
 
 
@@ -197,13 +212,13 @@ def assign_aggregate_noalloc(K, V, parents, children, sqnorm, frame, out, force_
     _need(K, "K", 4)
     dev, dt = K.device, K.dtype
     _need(V, "V", 4, dt, dev)
-    _need(children, "children", 4, dt, dev)
+    Hc, M0, C, dc = _tree_dims(children)
+    _need(children, "children", children.dim(), dt, dev)
     _need(parents, "parents", 3, dt, dev)
     _need(sqnorm, "sqnorm", 2, torch.float32, dev)
     _need(frame, "frame", 2, torch.float32, dev)
     B, H, N, d = K.shape
-    M0, C = children.shape[1], children.shape[2]
-    if V.shape != K.shape or children.shape[0] != H or children.shape[3] != d or \
+    if V.shape != K.shape or Hc != H or dc != d or \
             parents.shape != (H, M0, d) or sqnorm.shape != (H, M0 * (1 + C)) or frame.shape != (H, d):
         raise AvqError("inconsistent shapes")
     S = M0 * (1 + C)
@@ -232,14 +247,14 @@ def attention_fwd(Q, parents, children, vsum, count, P: int, tile: int, scale: f
     None, importance [B][H][ntiles][M0] or None)."""
     _need(Q, "Q", 4)
     dev, dt = Q.device, Q.dtype
-    _need(children, "children", 4, dt, dev)
+    Hc, M0, C, dc = _tree_dims(children)
+    _need(children, "children", children.dim(), dt, dev)
     _need(parents, "parents", 3, dt, dev)
     _need(vsum, "vsum", 4, torch.float32, dev)
     _need(count, "count", 3, torch.int32, dev)
     B, H, N, d = Q.shape
-    M0, C = children.shape[1], children.shape[2]
     S = M0 * (1 + C)
-    if parents.shape != (H, M0, d) or children.shape[0] != H or children.shape[3] != d:
+    if parents.shape != (H, M0, d) or Hc != H or dc != d:
         raise AvqError("inconsistent shapes")
     if vsum.shape != (B, H, S, d) or count.shape != (B, H, S):
         raise AvqError("vsum / count do not match the shape")

@@ -76,7 +76,7 @@ template <typename T, int D, int NRB>
 __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(assign_waves_per_simd<T, D>()))) void assign_parent_kernel(
     const T *__restrict__ K, const T *__restrict__ parents, const float *__restrict__ sqnorm,
     const float *__restrict__ frame, int H, int N, int M0, int C, int nchunks, int32_t *__restrict__ sorted,
-    int2 *__restrict__ seg)
+    int2 *__restrict__ seg, int32_t *__restrict__ leaf_direct)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NT = kAssignThreads;
@@ -244,6 +244,11 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
         }
     }
     __syncthreads();
+    const int nk = min(kAssignChunk, N - key0);
+    if (leaf_direct) {   // unfused stage 1: each key's parent, no bucketing
+        for (int x = tid; x < nk; x += NT) leaf_direct[head + key0 + x] = pst[x];
+        return;
+    }
 
     // Stable counting sort of the chunk's keys by parent, so that a bucket
     // lists its keys in key order and the sums the second kernel forms over
@@ -251,7 +256,6 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
     // a key's position is its parent's bucket start, plus that parent's keys
     // in earlier waves, plus those earlier in its own wave (same-parent lanes
     // are matched with one ballot per bit of the parent index).
-    const int nk = min(kAssignChunk, N - key0);
     constexpr int KPW = kAssignChunk / NWV;
     static_assert(KPW % 64 == 0, "a wave's keys must be whole rounds of 64");
     auto same_parent = [&](bool v, int p) {   // lanes holding a key of parent p
@@ -336,7 +340,8 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
 
 template <typename T, int D, int NRB>
 static hipError_t launch_assign(const void *K, const void *parents, const float *sqnorm, const float *frame,
-                                int B, int H, int N, int M0, int C, const AssignWorkspace &ws, hipStream_t stream)
+                                int B, int H, int N, int M0, int C, const AssignWorkspace &ws, int32_t *leaf_direct,
+                                hipStream_t stream)
 {
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     const size_t lds = (size_t)16 * NRB * (D + 8) * sizeof(T) + (size_t)16 * NRB * 4 +
@@ -344,7 +349,7 @@ static hipError_t launch_assign(const void *K, const void *parents, const float 
     allow_full_lds<assign_parent_kernel<T, D, NRB>>();
     hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(kAssignThreads), lds, stream,
                        (const T *)K, (const T *)parents, sqnorm, frame, H, N, M0, C, nchunks, ws.sorted,
-                       ws.seg);
+                       ws.seg, leaf_direct);
     return hipGetLastError();
 }
 
@@ -352,26 +357,26 @@ static hipError_t launch_assign(const void *K, const void *parents, const float 
 template <typename T, int D>
 static hipError_t launch_parent_t(const void *K, const void *parents, const float *sqnorm, const float *frame,
                                   int B, int H, int N, int M0, int C, const AssignWorkspace &ws,
-                                  hipStream_t stream)
+                                  int32_t *leaf_direct, hipStream_t stream)
 {
     const int m = round16(M0);
-    if (m <= 16) return launch_assign<T, D, 1>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
-    if (m <= 32) return launch_assign<T, D, 2>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
-    if (m <= 64) return launch_assign<T, D, 4>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
-    if (m <= 128) return launch_assign<T, D, 8>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
-    return launch_assign<T, D, 16>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
+    if (m <= 16) return launch_assign<T, D, 1>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, leaf_direct, stream);
+    if (m <= 32) return launch_assign<T, D, 2>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, leaf_direct, stream);
+    if (m <= 64) return launch_assign<T, D, 4>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, leaf_direct, stream);
+    if (m <= 128) return launch_assign<T, D, 8>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, leaf_direct, stream);
+    return launch_assign<T, D, 16>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, leaf_direct, stream);
 }
 
 hipError_t launch_assign_parent(const void *K, const void *parents, const float *sqnorm, const float *frame,
                                 int B, int H, int N, int d, int M0, int C, int dtype,
-                                const AssignWorkspace &ws, hipStream_t stream)
+                                const AssignWorkspace &ws, int32_t *leaf_direct, hipStream_t stream)
 {
     if (dtype == 1) {
-        if (d == 64) return launch_parent_t<bf16, 64>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
-        return launch_parent_t<bf16, 128>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
+        if (d == 64) return launch_parent_t<bf16, 64>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, leaf_direct, stream);
+        return launch_parent_t<bf16, 128>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, leaf_direct, stream);
     }
-    if (d == 64) return launch_parent_t<float, 64>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
-    return launch_parent_t<float, 128>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, stream);
+    if (d == 64) return launch_parent_t<float, 64>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, leaf_direct, stream);
+    return launch_parent_t<float, 128>(K, parents, sqnorm, frame, B, H, N, M0, C, ws, leaf_direct, stream);
 }
 
 }  // namespace avq

@@ -465,11 +465,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
         // (at d = 128 the query fragments are read again here rather than
         // held through the weights, value sums and selection, which keeps
         // the parent pass out of scratch)
+        float dz0 = 0.f, dz1 = 0.f;
+        if constexpr (CC > 0) {   // (a flat codebook, CC = 0, has no child level)
         if constexpr (D == 128) {
             asm volatile("" ::: "memory");
             load_q();
         }
-        float dz0 = 0.f, dz1 = 0.f;
         const float sl2c = sl2 * (1.0f / (float)CC);   // mean over CC children, scaled
         constexpr int SC = 32 * SCH;                    // children per super-chunk
 
@@ -630,6 +631,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                 super_chunk(c0 + SC, cwB, cwA, c0 + 2 * SC < PC);
             }
         }
+        }   // CC > 0
 
         // ---- Y = X / Z: lane (g, i) holds dims 16*db + 4g .. +3 of its query
         const float Z0 = Zf0 + xgroup_sum(dz0), Z1 = Zf1 + xgroup_sum(dz1);
@@ -724,6 +726,7 @@ static hipError_t launch_attn_nrb(const void *Q, const void *parents, const void
                                   hipStream_t stream)
 {
     switch (C) {
+    case 0: return launch_attn_w<T, D, VT, NRB, 0>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
     case 2: return launch_attn_w<T, D, VT, NRB, 2>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
     case 4: return launch_attn_w<T, D, VT, NRB, 4>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
     case 8: return launch_attn_w<T, D, VT, NRB, 8>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);

@@ -26,7 +26,7 @@ int fail(int status, const char *fmt, const char *what)
     } while (0)
 
 bool supported_d(int d) { return d == 64 || d == 128; }
-bool supported_C(int C) { return C == 2 || C == 4 || C == 8 || C == 16; }
+bool supported_C(int C) { return C == 0 || C == 2 || C == 4 || C == 8 || C == 16; }
 bool valid_dtype(int dt) { return dt == AVQ_F32 || dt == AVQ_BF16; }
 
 // hard limits of the kernels
@@ -37,11 +37,11 @@ int check_tree(int H, int M0, int C, int d, int dtype)
 {
     AVQ_REQUIRE(H >= 1, AVQ_ERR_INVALID_ARG, "H must be >= 1");
     AVQ_REQUIRE(M0 >= 1, AVQ_ERR_INVALID_ARG, "M0 must be >= 1");
-    AVQ_REQUIRE(C >= 1, AVQ_ERR_INVALID_ARG, "C must be >= 1");
+    AVQ_REQUIRE(C >= 0, AVQ_ERR_INVALID_ARG, "C must be >= 0");
     AVQ_REQUIRE(d >= 1, AVQ_ERR_INVALID_ARG, "d must be >= 1");
     AVQ_REQUIRE(valid_dtype(dtype), AVQ_ERR_INVALID_ARG, "dtype must be AVQ_F32 or AVQ_BF16");
     AVQ_REQUIRE(supported_d(d), AVQ_ERR_UNSUPPORTED, "d must be 64 or 128");
-    AVQ_REQUIRE(supported_C(C), AVQ_ERR_UNSUPPORTED, "C must be 2, 4, 8 or 16");
+    AVQ_REQUIRE(supported_C(C), AVQ_ERR_UNSUPPORTED, "C must be 0, 2, 4, 8 or 16");
     AVQ_REQUIRE(M0 <= kMaxM0, AVQ_ERR_UNSUPPORTED, "M0 must be <= 256");
     return AVQ_OK;
 }
@@ -51,6 +51,17 @@ int check_seq(int B, int N)
     AVQ_REQUIRE(B >= 1, AVQ_ERR_INVALID_ARG, "B must be >= 1");
     AVQ_REQUIRE(N >= 1, AVQ_ERR_INVALID_ARG, "N must be >= 1");
     AVQ_REQUIRE(N <= kMaxN, AVQ_ERR_UNSUPPORTED, "N must be <= 1048576");
+    return AVQ_OK;
+}
+
+int check_assign_flags(unsigned flags, int C)
+{
+    AVQ_REQUIRE((flags & ~(unsigned)(AVQ_FLAG_FORCE_CHILD | AVQ_FLAG_UNFUSED)) == 0, AVQ_ERR_INVALID_ARG,
+                "unknown flag bits");
+    AVQ_REQUIRE(!(C == 0 && (flags & AVQ_FLAG_FORCE_CHILD)), AVQ_ERR_INVALID_ARG,
+                "AVQ_FLAG_FORCE_CHILD needs children (C > 0)");
+    AVQ_REQUIRE(!((flags & AVQ_FLAG_UNFUSED) && C != 0), AVQ_ERR_UNSUPPORTED,
+                "AVQ_FLAG_UNFUSED is the flat-codebook (C = 0) comparison path");
     return AVQ_OK;
 }
 
@@ -143,15 +154,20 @@ int avq_assign_aggregate(const void *K, const void *V, const void *parents, cons
 {
     AVQ_REQUIRE(K && V && parents && children && sqnorm && frame && vsum_out && count_out && workspace,
                 AVQ_ERR_INVALID_ARG, "null pointer argument");
-    AVQ_REQUIRE((flags & ~(unsigned)AVQ_FLAG_FORCE_CHILD) == 0, AVQ_ERR_INVALID_ARG, "unknown flag bits");
     int st = check_tree(H, M0, C, d, dtype);
     if (st != AVQ_OK) return st;
     st = check_seq(B, N);
+    if (st != AVQ_OK) return st;
+    st = check_assign_flags(flags, C);
     if (st != AVQ_OK) return st;
     const size_t need = avq::assign_workspace_bytes(B, H, N, M0, C, d);
     AVQ_REQUIRE(workspace_bytes >= need, AVQ_ERR_INVALID_ARG, "workspace too small");
     AVQ_REQUIRE(((uintptr_t)workspace & 255u) == 0, AVQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     const avq::AssignWorkspace ws = avq::carve_assign_workspace(workspace, B, H, N, M0, C, d);
+    if (flags & AVQ_FLAG_UNFUSED)
+        return hip_status(avq::launch_assign_aggregate_unfused(K, V, parents, sqnorm, frame, B, H, N, d, M0, dtype,
+                                                               vsum_out, count_out, leaf_out, ws,
+                                                               (hipStream_t)stream));
     return hip_status(avq::launch_assign_aggregate(K, V, parents, children, sqnorm, frame, B, H, N, d, M0, C,
                                                    dtype, flags, vsum_out, count_out, leaf_out, ws,
                                                    (hipStream_t)stream));
@@ -164,11 +180,14 @@ int avq_assign_aggregate_noalloc(const void *K, const void *V, const void *paren
 {
     AVQ_REQUIRE(K && V && parents && children && sqnorm && frame && vsum_out && count_out, AVQ_ERR_INVALID_ARG,
                 "null pointer argument");
-    AVQ_REQUIRE((flags & ~(unsigned)AVQ_FLAG_FORCE_CHILD) == 0, AVQ_ERR_INVALID_ARG, "unknown flag bits");
     int st = check_tree(H, M0, C, d, dtype);
     if (st != AVQ_OK) return st;
     st = check_seq(B, N);
     if (st != AVQ_OK) return st;
+    st = check_assign_flags(flags, C);
+    if (st != AVQ_OK) return st;
+    AVQ_REQUIRE(!(flags & AVQ_FLAG_UNFUSED), AVQ_ERR_UNSUPPORTED,
+                "the allocation-free entry point runs the fused stage 1 only");
     const size_t need = avq::assign_workspace_bytes(B, H, N, M0, C, d);
     AVQ_REQUIRE(need <= (size_t)AVQ_NOALLOC_SCRATCH_BYTES, AVQ_ERR_UNSUPPORTED,
                 "shape needs more stage-1 scratch than the allocation-free entry point holds "
@@ -196,6 +215,7 @@ int avq_attention_fwd(const void *Q, const void *parents, const void *children, 
     st = check_seq(B, N);
     if (st != AVQ_OK) return st;
     AVQ_REQUIRE(P >= 0 && P <= M0, AVQ_ERR_INVALID_ARG, "P must satisfy 0 <= P <= M0");
+    AVQ_REQUIRE(C > 0 || P == 0, AVQ_ERR_INVALID_ARG, "a flat codebook (C = 0) has no children to refine: P must be 0");
     AVQ_REQUIRE(tile >= 1, AVQ_ERR_INVALID_ARG, "tile must be >= 1");
     AVQ_REQUIRE(isfinite(scale), AVQ_ERR_INVALID_ARG, "scale must be finite");
     AVQ_REQUIRE(tile == 32 || tile == 64 || tile == 128 || tile == 256, AVQ_ERR_UNSUPPORTED,

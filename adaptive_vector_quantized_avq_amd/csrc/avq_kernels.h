@@ -88,9 +88,19 @@ hipError_t launch_build_tree(const void *children, int H, int M0, int C, int d, 
                              void *parents, float *sqnorm, float *frame, hipStream_t stream);
 
 // first stage-1 kernel alone (nearest parent + per-chunk bucketing)
+// (leaf_direct != nullptr: write each key's parent there instead of the
+// bucketed lists -- the unfused stage 1 of a flat codebook)
 hipError_t launch_assign_parent(const void *K, const void *parents, const float *sqnorm, const float *frame,
                                 int B, int H, int N, int d, int M0, int C, int dtype,
-                                const AssignWorkspace &ws, hipStream_t stream);
+                                const AssignWorkspace &ws, int32_t *leaf_direct, hipStream_t stream);
+
+// Unfused stage 1 of a flat codebook (C = 0): nearest codeword of every key
+// written to memory, then a separate scatter of values and counts with
+// global atomics (fp32 sums in a nondeterministic order)
+hipError_t launch_assign_aggregate_unfused(const void *K, const void *V, const void *parents, const float *sqnorm,
+                                           const float *frame, int B, int H, int N, int d, int M0, int dtype,
+                                           float *vsum, int32_t *count, int32_t *leaf, const AssignWorkspace &ws,
+                                           hipStream_t stream);
 
 hipError_t launch_assign_aggregate(const void *K, const void *V, const void *parents,
                                    const void *children, const float *sqnorm, const float *frame, int B,

@@ -1,5 +1,6 @@
 // Frozen-tree preparation ("AVQ-Attention", Sec. 4.1 parent-child
-// constraint): every parent is the mean of its C children; every head gets
+// constraint): every parent is the mean of its C children (a flat codebook,
+// C = 0, is copied: its codewords are the parents); every head gets
 // the reference point r of its distance frame (see codebook frame below),
 // and every stored codeword its squared norm in that frame for the
 // expansion ||k - c||^2 = ||u||^2 + ||c - r||^2 - 2 u.(c - r), u = k - r,
@@ -19,6 +20,10 @@ __global__ void tree_parents_kernel(const T *__restrict__ children, int H, int M
     const int64_t total = (int64_t)H * M0 * d;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
+    if (C == 0) {   // a flat codebook ([H][M0][d]) is its own parent level
+        parents[i] = children[i];
+        return;
+    }
     const int t = (int)(i % d);
     const int64_t hp = i / d;                       // h * M0 + p
     const T *src = children + hp * C * d + t;

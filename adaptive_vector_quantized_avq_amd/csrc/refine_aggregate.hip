@@ -166,8 +166,10 @@ void refine_aggregate_kernel(
     constexpr int kStage = (kRows * D / 8 + NT - 1) / NT;
     const T *any_row = children + ((int64_t)h * M0 + p0) * CC * D;
     Frag<T> sf[kStage];
+    // (a flat codebook, CC = 0, has no child level: nothing to stage, the
+    // keys' distances are never needed)
 #pragma unroll
-    for (int k = 0; k < kStage; ++k) {
+    for (int k = 0; k < (CC > 0 ? kStage : 0); ++k) {
         const int e = (tid + NT * k) * 8, r = e / D, c = e % D, lp = r / BR, j = r % BR;
         const T *src = any_row;
         if (e < kRows * D && lp < Gv) {
@@ -196,7 +198,7 @@ void refine_aggregate_kernel(
     const bool shift = __ballot(rl != 0.f || rh != 0.f) != 0ull;
     if (tid < D) rv[tid] = fr[tid];
 #pragma unroll
-    for (int k = 0; k < kStage; ++k) {
+    for (int k = 0; k < (CC > 0 ? kStage : 0); ++k) {
         const int e = (tid + NT * k) * 8, r = e / D, c = e % D, lp = r / BR, j = r % BR;
         if (e < kRows * D) {
             const f32x4 r0 = *reinterpret_cast<const f32x4 *>(fr + c);
@@ -245,7 +247,7 @@ void refine_aggregate_kernel(
             const int key = (int)((unsigned)__shfl((int)e, 16 * kb + i16) & 0xFFFFFFu);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                kf[kb][ks] = load_frag(K + (head + key) * D + 32 * ks + 8 * g);
+                if constexpr (CC > 0) kf[kb][ks] = load_frag(K + (head + key) * D + 32 * ks + 8 * g);
                 vf[kb][ks] = load_frag(V + (head + key) * D + 32 * ks + 8 * g);
             }
         }
@@ -267,7 +269,7 @@ void refine_aggregate_kernel(
     auto compute = [&](int s, unsigned e, bool more, unsigned en, Frag<T> (&kf)[KB][KS],
                        Frag<T> (&vf)[KB][KS]) {
         const int x0 = xpos(s);
-        if (shift) {   // keys into the distance frame
+        if (CC > 0 && shift) {   // keys into the distance frame
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -283,7 +285,7 @@ void refine_aggregate_kernel(
         // distances to every codeword row; keep the key's own parent block
         f32x4 own[KB][BRB];
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
+        for (int rb = 0; rb < (CC > 0 ? NRB : 0); ++rb) {
             Frag<T> a[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) a[ks] = load_frag(Cw + (16 * rb + i16) * LDP + 32 * ks + 8 * g);
@@ -300,7 +302,7 @@ void refine_aggregate_kernel(
         int nkey[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) nkey[kb] = (int)((unsigned)__shfl((int)en, 16 * kb + i16) & 0xFFFFFFu);
-        if (more) {
+        if (CC > 0 && more) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -311,20 +313,22 @@ void refine_aggregate_kernel(
         for (int kb = 0; kb < KB; ++kb) {
             float cbest = INFINITY, pe = INFINITY;
             int crow = 0;
+            if constexpr (CC > 0) {
 #pragma unroll
-            for (int q = 0; q < BRB; ++q)
+                for (int q = 0; q < BRB; ++q)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * q + 4 * g + r;   // row inside the parent block
-                    const float v = own[kb][q][r];
-                    const bool lt = j < CC && v < cbest;
-                    cbest = lt ? v : cbest;
-                    crow = lt ? j : crow;
-                    pe = j == CC ? v : pe;
-                }
-            xgroup_argmin(cbest, crow);
-            pe = xgroup_min(pe);
-            const bool to_child = force_child || cbest < pe;
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * q + 4 * g + r;   // row inside the parent block
+                        const float v = own[kb][q][r];
+                        const bool lt = j < CC && v < cbest;
+                        cbest = lt ? v : cbest;
+                        crow = lt ? j : crow;
+                        pe = j == CC ? v : pe;
+                    }
+                xgroup_argmin(cbest, crow);
+                pe = xgroup_min(pe);
+            }
+            const bool to_child = CC > 0 && (force_child || cbest < pe);
             const int j = to_child ? crow : CC;
             const bool valid = x0 + 16 * kb + i16 < total;
             if (g == 0) {
@@ -432,9 +436,12 @@ void refine_aggregate_kernel(
     // ---- outputs: child slots as accumulated; parent = stayed + children
     float *vs = vsum + (int64_t)bh * S * D;
     int32_t *cs = count + (int64_t)bh * S;
-    for (int e = tid; e < Gv * CC * D; e += NT) {
-        const int lp = e / (CC * D), c = (e / D) % CC, t = e % D;
-        vs[((int64_t)M0 + p0 * CC) * D + e] = acc[(lp * (CC + 1) + c) * LDA + t];
+    if constexpr (CC > 0) {
+        for (int e = tid; e < Gv * CC * D; e += NT) {
+            const int lp = e / (CC * D), c = (e / D) % CC, t = e % D;
+            vs[((int64_t)M0 + p0 * CC) * D + e] = acc[(lp * (CC + 1) + c) * LDA + t];
+        }
+        for (int e = tid; e < Gv * CC; e += NT) cs[M0 + p0 * CC + e] = (int)cntf[(e / CC) * (CC + 1) + e % CC];
     }
     for (int e = tid; e < Gv * D; e += NT) {
         const int lp = e / D, t = e % D;
@@ -443,7 +450,6 @@ void refine_aggregate_kernel(
         for (int c = 0; c < CC; ++c) s += acc[(lp * (CC + 1) + c) * LDA + t];
         vs[(int64_t)(p0 + lp) * D + t] = s;
     }
-    for (int e = tid; e < Gv * CC; e += NT) cs[M0 + p0 * CC + e] = (int)cntf[(e / CC) * (CC + 1) + e % CC];
     for (int lp = tid; lp < Gv; lp += NT) {
         float s = 0.f;
 #pragma unroll
@@ -479,6 +485,7 @@ static hipError_t launch_refine_t(const void *K, const void *V, const void *pare
 #define AVQ_REFINE(CCV) \
     launch_refine<T, D, CCV>(K, V, parents, children, sqnorm, frame, B, H, N, M0, flags, vsum, count, leaf, ws, stream)
     switch (C) {
+    case 0: return AVQ_REFINE(0);
     case 2: return AVQ_REFINE(2);
     case 4: return AVQ_REFINE(4);
     case 8: return AVQ_REFINE(8);
@@ -494,7 +501,7 @@ hipError_t launch_assign_aggregate(const void *K, const void *V, const void *par
                                    int32_t *count, int32_t *leaf, const AssignWorkspace &ws,
                                    hipStream_t stream)
 {
-    hipError_t err = launch_assign_parent(K, parents, sqnorm, frame, B, H, N, d, M0, C, dtype, ws, stream);
+    hipError_t err = launch_assign_parent(K, parents, sqnorm, frame, B, H, N, d, M0, C, dtype, ws, nullptr, stream);
     if (err != hipSuccess) return err;
     if (dtype == 1) {
         if (d == 64)

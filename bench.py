@@ -138,7 +138,8 @@ def oracle_comparison(inp, P, ref, g):
         n_ambiguous_tiles=int(amb_tiles.sum()),
         selection_mismatch_tiles=int((~same).sum()),
         selection_mismatch_outside_band=int((~same & ~amb_tiles).sum()),
-        sum_residual=int(g["count"][..., :M0].sum() - g["count"][..., M0:].sum()),
+        # keys that stayed at their parent (none is possible without children)
+        sum_residual=None if inp.C == 0 else int(g["count"][..., :M0].sum() - g["count"][..., M0:].sum()),
     )
 
 
@@ -209,6 +210,9 @@ def main():
     ap.add_argument("--workload", default="long-64k")
     ap.add_argument("--P", type=int, default=None)
     ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--unfused", action="store_true",
+                    help="flat codebooks (C = 0): time the unfused stage 1 (leaf ids, then an atomic "
+                         "scatter) instead of the fused one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads of batch 0 the CPU oracle runs on (0 = all of them)")
@@ -273,7 +277,7 @@ def main():
         Q, K, V = sets[i % len(sets)]
         if ev is not None:
             ev[0].record()
-        avq.assign_aggregate(K, V, parents, ch, sq, fr, workspace=ws1, out=(vsum, count))
+        avq.assign_aggregate(K, V, parents, ch, sq, fr, workspace=ws1, out=(vsum, count), unfused=args.unfused)
         if ev is not None:
             ev[1].record()
         avq.attention_fwd(Q, parents, ch, vsum, count, P, inp.T, inp.scale, workspace=ws2, out=Y)
@@ -357,7 +361,8 @@ def main():
         "dtype": inp.dtype,
         "data": "synthetic (seeded PCG64; shapes of the pages' long-sequence timing sweep)",
         "config": {"workload": inp.name, "B": B, "H": H, "N": N, "d": d, "M0": inp.M0,
-                   "C": inp.C, "P": P, "tile": inp.T, "input_sets": args.sets},
+                   "C": inp.C, "P": P, "tile": inp.T, "input_sets": args.sets,
+                   "stage1": "unfused" if args.unfused else "fused"},
         "roofline": roof,
         "stages": {
             "assign_aggregate": {"ms": round(s1_ms, 5), "alg_bytes": alg["s1_bytes"],
@@ -383,7 +388,7 @@ def main():
 
     # outputs on input set 0 (the unrotated workload) for the oracle check
     Q, K, V = sets[0]
-    vs0, cn0, lf0 = avq.assign_aggregate(K, V, parents, ch, sq, fr, want_leaf=True)
+    vs0, cn0, lf0 = avq.assign_aggregate(K, V, parents, ch, sq, fr, want_leaf=True, unfused=args.unfused)
     Y0, sel0, imp0 = avq.attention_fwd(Q, parents, ch, vs0, cn0, P, inp.T, inp.scale,
                                        want_sel=True, want_importance=True)
     torch.cuda.synchronize()

@@ -29,10 +29,14 @@
  *    avq_last_error() gives a message for the last failure on the calling
  *    thread.
  *  - Supported shapes: head dim d in {64, 128}; C in {2, 4, 8, 16} children
- *    per parent; 1 <= M0 <= 256 parents; 1 <= N <= 1048576; query tile in
- *    {32, 64, 128, 256} (the pages use tiles of 32 to 128 queries, Table 8).
+ *    per parent, or C = 0 for a flat codebook (plain VQ-attention, Sec.
+ *    3.2: no child level, P = 0); 1 <= M0 <= 256 parents; 1 <= N <= 1048576;
+ *    query tile in {32, 64, 128, 256} (the pages use tiles of 32 to 128
+ *    queries, Table 8).
  *  - Codeword slots: j in [0, M0) is parent j; j = M0 + p*C + c is child c
  *    of parent p.  S_tot = M0 * (1 + C).
+ *  - With C = 0 the `children` argument of every call is the flat codebook
+ *    [H][M0][d] itself; avq_build_tree copies it to parents_out.
  *  - Calls are stateless and thread-safe; no C++ exception crosses the ABI.
  */
 #ifndef AVQ_H
@@ -60,8 +64,15 @@ enum avq_dtype { AVQ_F32 = 0, AVQ_BF16 = 1 };
 enum {
     /* Treat the cached parent distance as +infinity in the child step, so
      * every key moves to its nearest child and the children of a parent
-     * partition its cell (no residual keys). */
-    AVQ_FLAG_FORCE_CHILD = 1
+     * partition its cell (no residual keys).  Needs C > 0. */
+    AVQ_FLAG_FORCE_CHILD = 1,
+    /* Flat codebook (C = 0) only: the unfused precomputation the pages
+     * compare the fused kernel with (Sec. 4.2, Table 2): the nearest
+     * codeword of every key is written to memory (leaf_out if given, else
+     * the workspace), then a separate pass adds values and counts with
+     * global atomics.  Same results; the fp32 summation order then depends
+     * on scheduling. */
+    AVQ_FLAG_UNFUSED = 2
 };
 
 int avq_abi_version(void);
@@ -120,7 +131,7 @@ size_t avq_assign_aggregate_workspace_size(int B, int H, int N, int M0, int C, i
  *   children   [H][M0][C][d]  dtype
  *   sqnorm     [H][S_tot]     fp32    from avq_build_tree
  *   frame      [H][d]         fp32    from avq_build_tree
- *   flags      0 or AVQ_FLAG_FORCE_CHILD
+ *   flags      0, AVQ_FLAG_FORCE_CHILD (C > 0) or AVQ_FLAG_UNFUSED (C = 0)
  *   vsum_out   [B][H][S_tot][d] fp32  output value sums (every slot written)
  *   count_out  [B][H][S_tot]  int32   output key counts (every slot written)
  *   leaf_out   [B][H][N]      int32   optional (NULL = not written): slot of

@@ -47,7 +47,7 @@ def check_stage1(inp, parents64, gpu_leaf, gpu_vsum, gpu_count, force_child=Fals
     # an ambiguous key's GPU leaf must at least be a slot of a valid shape
     assert ((gpu_leaf >= 0) & (gpu_leaf < M0 * (1 + C))).all()
     leaf = np.where(amb, gpu_leaf, a["leaf"])
-    pst = np.where(leaf < M0, leaf, (leaf - M0) // C)
+    pst = leaf if C == 0 else np.where(leaf < M0, leaf, (leaf - M0) // C)
     vsum, count = oracle.aggregate(inp.f64("V"), leaf, M0, C)
     np.testing.assert_array_equal(gpu_count, count)
     # fp32 summation bound per slot and dimension

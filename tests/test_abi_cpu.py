@@ -105,6 +105,8 @@ def test_invalid_arguments_are_rejected_before_launch(lib):
     assert call(dt=7) == -1
     assert call(d=96) == -2
     assert call(C=3) == -2
+    assert call(C=0) == -1             # flat codebook: P must be 0
+    assert call(C=-1) == -1
     assert call(M0=300, P=4) == -2
     assert call(tile=48) == -2
     assert b"tile" in lib.avq_last_error()
@@ -119,8 +121,14 @@ def test_invalid_arguments_are_rejected_before_launch(lib):
     # a valid call template; each case below breaks exactly one argument
     base = [p, p, p, p, p, p, 1, 1, 128, 64, 16, 4, 1, 0, p, p, None, p, 1 << 20, None]
     bad_flags = list(base)
-    bad_flags[13] = 2
+    bad_flags[13] = 4
     assert aa(*bad_flags) == -1
+    unfused_tree = list(base)          # the unfused path is for flat codebooks only
+    unfused_tree[13] = 2
+    assert aa(*unfused_tree) == -2
+    flat_forced = list(base)           # C = 0 has no children to force
+    flat_forced[11], flat_forced[13] = 0, 1
+    assert aa(*flat_forced) == -1
     no_frame = list(base)
     no_frame[5] = None
     assert aa(*no_frame) == -1

@@ -41,12 +41,12 @@ def to_dev(arr, dtype):
     return t.to(DEV)
 
 
-def run_gpu(avq, inp, P, T, force_child=False):
+def run_gpu(avq, inp, P, T, force_child=False, unfused=False):
     ch = to_dev(inp.children, inp.dtype)
     K, V, Q = (to_dev(x, inp.dtype) for x in (inp.K, inp.V, inp.Q))
     parents, sq, fr = avq.build_tree(ch)
     vsum, count, leaf = avq.assign_aggregate(K, V, parents, ch, sq, fr, force_child=force_child,
-                                             want_leaf=True)
+                                             want_leaf=True, unfused=unfused)
     Y, sel, imp = avq.attention_fwd(Q, parents, ch, vsum, count, P, T, inp.scale,
                                     want_sel=True, want_importance=True)
     torch.cuda.synchronize()
@@ -62,7 +62,7 @@ def check_tree_frame(inp, par64, sq64, frame, sqnorm):
     in the storage type for every stored codeword of its head; the norms are
     ||c - r||^2 rounded to fp32 (the oracle's own ||c||^2 where r = 0)."""
     H, M0, C, d = inp.H, inp.M0, inp.C, inp.d
-    rows = np.concatenate([par64, inp.f64("children").reshape(H, M0 * C, d)], axis=1)
+    rows = par64 if C == 0 else np.concatenate([par64, inp.f64("children").reshape(H, M0 * C, d)], axis=1)
     diff = rows - frame[:, None, :]                     # exact in fp64
     exact = oracle.round_to(diff, inp.dtype) == diff
     assert (exact | (frame == 0.0)[:, None, :]).all()
@@ -88,14 +88,14 @@ def check_stage2(inp, par64, vsum, count, g, P, T):
     return float(np.abs(g["Y"] - Yf).max()), namb
 
 
-def check_all(avq, inp, P=None, T=None, force_child=False):
+def check_all(avq, inp, P=None, T=None, force_child=False, unfused=False):
     """Run the whole forward on the GPU once, check stage 1 on every key and
     stage 2 on every query tile."""
     P = inp.P if P is None else P
     T = inp.T if T is None else T
     _say(f"{inp.name} dtype={inp.dtype} B={inp.B} H={inp.H} N={inp.N} d={inp.d} M0={inp.M0} "
-         f"C={inp.C} P={P} T={T} force_child={force_child} seed={inp.seed}")
-    g = run_gpu(avq, inp, P, T, force_child)
+         f"C={inp.C} P={P} T={T} force_child={force_child} unfused={unfused} seed={inp.seed}")
+    g = run_gpu(avq, inp, P, T, force_child, unfused)
     ch64 = inp.f64("children")
     par64, sq64 = oracle.build_tree(ch64, inp.dtype)
     np.testing.assert_array_equal(g["parents"], par64)
@@ -460,3 +460,52 @@ def test_near_ties_on_a_translated_codebook(avq, dtype, d, C, offset):
     close = ((g >= 1e-4) & (g < 1e-2)).sum()
     _say(f"  keys with a top-2 gap in [1e-4, 1e-2): {close}")
     assert close > 50
+
+
+# ------------------------------------------------------------------ flat VQ (C = 0)
+
+FLAT = [
+    # dtype, d, M0, N, T
+    ("bf16", 64, 256, 5000, 128),
+    ("f32", 64, 40, 1500, 64),
+    ("bf16", 128, 100, 3000, 256),
+    ("f32", 128, 17, 777, 32),
+    ("bf16", 64, 1, 100, 64),
+]
+
+
+@pytest.mark.parametrize("unfused", [False, True])
+@pytest.mark.parametrize("dtype,d,M0,N,T", FLAT)
+def test_flat_vq(avq, dtype, d, M0, N, T, unfused):
+    """Plain VQ-attention over a flat codebook (C = 0): fused stage 1 (the
+    bucketed lists, then an aggregation that reads only V) and the unfused
+    comparison path (leaf ids, then an atomic scatter)."""
+    inp = synth.generate("flat-64k", B=2, H=2, N=N, d=d, M0=M0, T=T, dtype=dtype, seed=300 + M0 + N)
+    check_all(avq, inp, unfused=unfused)
+
+
+@pytest.mark.parametrize("unfused", [False, True])
+def test_flat_vq_full_size(avq, unfused):
+    check_all(avq, synth.generate("flat-64k"), unfused=unfused)
+
+
+def test_flat_vq_argument_checks(avq):
+    _say("flat VQ argument checks")
+    inp = synth.generate("flat-64k", B=1, H=1, N=256, M0=8)
+    cb = to_dev(inp.children, "bf16")
+    K, V, Q = (to_dev(x, "bf16") for x in (inp.K, inp.V, inp.Q))
+    parents, sq, fr = avq.build_tree(cb)
+    torch.cuda.synchronize()
+    assert torch.equal(parents, cb) and sq.shape == (1, 8)
+    vsum, count, _ = avq.assign_aggregate(K, V, parents, cb, sq, fr)
+    with pytest.raises(avq.AvqError, match="INVALID_ARG"):
+        avq.attention_fwd(Q, parents, cb, vsum, count, 2, 128, inp.scale)      # P > 0 without children
+    with pytest.raises(avq.AvqError, match="INVALID_ARG"):
+        avq.assign_aggregate(K, V, parents, cb, sq, fr, force_child=True)     # no children to force
+    tree = synth.generate("vit-b", B=1, H=1, N=256, M0=8)
+    ch = to_dev(tree.children, "bf16")
+    p2, s2, f2 = avq.build_tree(ch)
+    Kt, Vt = to_dev(tree.K, "bf16"), to_dev(tree.V, "bf16")
+    with pytest.raises(avq.AvqError, match="UNSUPPORTED"):
+        avq.assign_aggregate(Kt, Vt, p2, ch, s2, f2, unfused=True)           # unfused is flat-only
+    torch.cuda.synchronize()
