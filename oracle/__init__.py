@@ -72,6 +72,15 @@ def _load():
                                            ctypes.c_int, ctypes.c_int, ctypes.c_double, _i32p,
                                            ctypes.c_int64, ctypes.c_int64,
                                            _dp, _dp, _i32p]
+            lib.avqo_commitment.restype = ctypes.c_double
+            lib.avqo_commitment.argtypes = [_dp, ctypes.c_int64, ctypes.c_int, _dp, _dp,
+                                            ctypes.c_int, ctypes.c_int, _i32p]
+            lib.avqo_active_ratio.restype = ctypes.c_double
+            lib.avqo_active_ratio.argtypes = [_i64p, ctypes.c_int, ctypes.c_int64, ctypes.c_double]
+            lib.avqo_capture.restype = ctypes.c_int
+            lib.avqo_capture.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int, _i32p, _i32p,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                         _dp]
             _lib = lib
     return _lib
 
@@ -222,6 +231,61 @@ def attention(Q, parents, children, vsum, count, P: int, T: int, scale: float,
 
     _run(unit, units, threads)
     return Y, imp, sel
+
+
+def commitment(K, parents, children, leaf, threads: Optional[int] = None):
+    """K [B][H][N][d], leaf [B][H][N] -> [B][H]: mean over the keys of the
+    squared distance to the assigned leaf codeword (Table 7's E||k - k_hat||^2)."""
+    lib = _load()
+    K, parents, children = _f64(K), _f64(parents), _f64(children)
+    leaf = np.ascontiguousarray(leaf, dtype=np.int32)
+    B, H, N, d = K.shape
+    M0, C = _tree_shape(children)
+    out = np.empty((B, H))
+
+    def unit(bh):
+        b, h = bh
+        out[b, h] = lib.avqo_commitment(_p(K[b, h], _dp), N, d, _p(parents[h], _dp),
+                                        _p(children[h], _dp), M0, C, _p(leaf[b, h], _i32p))
+
+    _run(unit, [(b, h) for b in range(B) for h in range(H)], threads)
+    return out
+
+
+def active_ratio(count, N: int, share: float = 0.01):
+    """count [B][H][S_tot] -> [B][H]: fraction of codewords whose count
+    exceeds share * N / S_tot (Table 9's active ratio, share = 1 %)."""
+    lib = _load()
+    count = np.ascontiguousarray(count, dtype=np.int64)
+    B, H, S = count.shape
+    out = np.empty((B, H))
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = lib.avqo_active_ratio(_p(count[b, h], _i64p), S, N, share)
+    return out
+
+
+def capture(Q, K, pstar, sel, T: int, scale: float, M0: int, threads: Optional[int] = None):
+    """Q, K [B][H][N][d], pstar [B][H][N], sel [B][H][ntiles][P] -> [B][H][N]:
+    each query's fraction of exact softmax weight on keys whose parent its
+    tile selected (Sec. 5.2, Table 6 "capture").  O(N^2 d): small N only."""
+    lib = _load()
+    Q, K = _f64(Q), _f64(K)
+    pstar = np.ascontiguousarray(pstar, dtype=np.int32)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    B, H, N, d = Q.shape
+    P = sel.shape[-1]
+    out = np.empty((B, H, N))
+
+    def unit(bh):
+        b, h = bh
+        rc = lib.avqo_capture(_p(Q[b, h], _dp), _p(K[b, h], _dp), N, d, _p(pstar[b, h], _i32p),
+                              _p(sel[b, h], _i32p), P, T, float(scale), M0, _p(out[b, h], _dp))
+        if rc != 0:
+            raise MemoryError("oracle capture allocation failed")
+
+    _run(unit, [(b, h) for b in range(B) for h in range(H)], threads)
+    return out
 
 
 def forward(inp, P: Optional[int] = None, T: Optional[int] = None, force_child=False,

@@ -303,3 +303,69 @@ int avqo_attention(const double *Q /*[N][d]*/, int64_t N, int d,
     free(E); free(m); free(Z); free(X); free(s); free(w); free(order); free(chosen);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Diagnostics the pages report next to the method (Sec. 5.2, appendix  */
+/* "Per-layer codebook analysis" and "Codebook utilization").           */
+/* ------------------------------------------------------------------ */
+
+/* Commitment loss E[||k - k_hat||^2]: the mean over the N keys of the
+ * squared distance between each key and the codeword it is assigned to,
+ * its leaf (child, or the parent itself; the codeword for a flat
+ * codebook, C == 0).  Independent of P. */
+double avqo_commitment(const double *K /*[N][d]*/, int64_t N, int d, const double *parents /*[M0][d]*/,
+                       const double *children /*[M0][C][d]*/, int M0, int C, const int32_t *leaf)
+{
+    double s = 0.0;
+    for (int64_t k = 0; k < N; ++k) {
+        const int32_t l = leaf[k];
+        const double *cw = l < M0 ? parents + (int64_t)l * d : children + (int64_t)(l - M0) * d;
+        s += sqdist(K + k * d, cw, d);
+    }
+    return N > 0 ? s / (double)N : 0.0;
+}
+
+/* Active ratio: the fraction of the S codewords whose count exceeds
+ * `share` times the fair-share count N / S (the pages use 1 %). */
+double avqo_active_ratio(const int64_t *count, int S, int64_t N, double share)
+{
+    const double thresh = share * (double)N / (double)S;
+    int active = 0;
+    for (int j = 0; j < S; ++j) active += (double)count[j] > thresh;
+    return (double)active / (double)S;
+}
+
+/* Capture of every query: the fraction of its exact softmax attention
+ * weight (scale * q.k over all N keys) that falls on keys whose parent
+ * (pstar) is among its tile's P selected parents (sel [ntiles][P], tiles
+ * of T consecutive queries).  Returns 0, or -1 on allocation failure. */
+int avqo_capture(const double *Q /*[N][d]*/, const double *K /*[N][d]*/, int64_t N, int d,
+                 const int32_t *pstar, const int32_t *sel, int P, int T, double scale, int M0,
+                 double *capture /*[N]*/)
+{
+    double *s = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    char *chosen = (char *)malloc((size_t)(M0 > 0 ? M0 : 1));
+    if (!s || !chosen) { free(s); free(chosen); return -1; }
+    for (int64_t i = 0; i < N; ++i) {
+        const int64_t t = i / T;
+        memset(chosen, 0, (size_t)M0);
+        for (int k = 0; k < P; ++k) chosen[sel[t * P + k]] = 1;
+        double mx = -INFINITY;
+        for (int64_t k = 0; k < N; ++k) {
+            double dot = 0.0;
+            for (int u = 0; u < d; ++u) dot += Q[i * d + u] * K[k * d + u];
+            s[k] = scale * dot;
+            if (s[k] > mx) mx = s[k];
+        }
+        double all = 0.0, on_sel = 0.0;
+        for (int64_t k = 0; k < N; ++k) {
+            const double e = exp(s[k] - mx);
+            all += e;
+            if (chosen[pstar[k]]) on_sel += e;
+        }
+        capture[i] = on_sel / all;
+    }
+    free(s);
+    free(chosen);
+    return 0;
+}

@@ -433,3 +433,61 @@ def test_flat_codebook_is_the_parent_level_of_a_tree():
     assert (f["pstar"] == t["pstar"]).all()
     np.testing.assert_array_equal(f["count"], t["count"][..., :tree.M0])
     assert np.abs(f["Y"] - t["Y"]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- diagnostics
+
+def test_commitment_hand_values_and_zero_on_codewords():
+    # d = 2, one parent at the origin with children (+-1, 0): key (0.75, 0)
+    # -> child (1, 0) at 0.0625; key (0, 2) -> stays at the parent at 4
+    # (children at 5); mean 2.03125
+    ch = np.array([[[[1.0, 0.0], [-1.0, 0.0]]]])
+    par, _ = oracle.build_tree(ch, "f32")
+    keys = np.array([[0.75, 0.0], [0.0, 2.0]])[None, None]
+    a = oracle.assign(keys, par, ch)
+    assert a["leaf"][0, 0].tolist() == [1, 0]
+    assert oracle.commitment(keys, par, ch, a["leaf"])[0, 0] == 2.03125
+    # keys placed exactly on leaves: zero loss
+    inp = synth.generate_one_key_per_leaf(7, H=2, d=64, M0=8, C=4, dtype="f32")
+    r = oracle.forward(inp)
+    assert (oracle.commitment(inp.f64("K"), r["parents"], inp.f64("children"), r["leaf"]) == 0).all()
+
+
+def test_commitment_flat_is_mean_nearest_distance():
+    # flat codebook: the loss is the mean squared distance to the nearest
+    # codeword, by brute force
+    rng = np.random.default_rng(5)
+    cb = rng.standard_normal((1, 7, 3))
+    K = rng.standard_normal((1, 1, 50, 3))
+    par, _ = oracle.build_tree(cb, "f32")
+    a = oracle.assign(K, par, cb)
+    ref = np.mean([min(((k - c) ** 2).sum() for c in cb[0]) for k in K[0, 0]])
+    assert abs(oracle.commitment(K, par, cb, a["leaf"])[0, 0] - ref) < 1e-12
+
+
+def test_active_ratio_hand_values():
+    # 4 codewords, N = 400: fair share 100, threshold 1 key; counts {0, 1, 2, 397}
+    c = np.array([[[0, 1, 2, 397]]])
+    assert oracle.active_ratio(c, 400)[0, 0] == 0.5          # only counts > 1
+    assert oracle.active_ratio(c, 400, share=0.0)[0, 0] == 0.75
+
+
+def test_capture_limits_and_softmax_reformulation():
+    inp = synth.generate("vit-b", B=1, H=2, N=300, M0=12, C=4, P=3, T=64, dtype="f32", seed=17)
+    r = oracle.forward(inp)
+    Q, K = inp.f64("Q"), inp.f64("K")
+    cap = oracle.capture(Q, K, r["pstar"], r["sel"], inp.T, inp.scale, inp.M0)
+    # the same fraction from an explicit softmax matrix
+    for h in range(inp.H):
+        S = inp.scale * Q[0, h] @ K[0, h].T
+        A = np.exp(S - S.max(axis=1, keepdims=True))
+        A /= A.sum(axis=1, keepdims=True)
+        for t in range(inp.ntiles):
+            rows = slice(t * inp.T, min(inp.N, (t + 1) * inp.T))
+            on = np.isin(r["pstar"][0, h], r["sel"][0, h, t])
+            np.testing.assert_allclose(cap[0, h, rows], A[rows][:, on].sum(axis=1), rtol=1e-12, atol=1e-14)
+    # every parent selected -> all the weight; none -> nothing
+    all_sel = np.broadcast_to(np.arange(inp.M0, dtype=np.int32), (1, 2, inp.ntiles, inp.M0))
+    assert np.abs(oracle.capture(Q, K, r["pstar"], all_sel, inp.T, inp.scale, inp.M0) - 1).max() < 1e-12
+    none = np.zeros((1, 2, inp.ntiles, 0), dtype=np.int32)
+    assert (oracle.capture(Q, K, r["pstar"], none, inp.T, inp.scale, inp.M0) == 0).all()
