@@ -20,7 +20,7 @@ __all__ = [
     "AvqError", "library_path", "load_library", "abi_version",
     "build_tree", "assign_aggregate", "attention_fwd", "exact_attention_fwd",
     "assign_aggregate_workspace_size", "attention_workspace_size", "forward",
-    "assign_aggregate_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "assign_aggregate_noalloc", "NOALLOC_SCRATCH_BYTES", "codebook_diagnostics", "capture",
     "AVQ_FLAG_FORCE_CHILD", "AVQ_FLAG_UNFUSED",
 ]
 
@@ -70,6 +70,13 @@ def load_library():
     lib.avq_attention_fwd.restype = i32
     lib.avq_attention_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                       f32, i32, vp, vp, vp, vp, sz, vp]
+    lib.avq_diagnostics_workspace_size.restype = sz
+    lib.avq_diagnostics_workspace_size.argtypes = [i32, i32, i32]
+    lib.avq_codebook_diagnostics.restype = i32
+    lib.avq_codebook_diagnostics.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                             vp, vp, vp, sz, vp]
+    lib.avq_capture.restype = i32
+    lib.avq_capture.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.avq_exact_attention_fwd.restype = i32
     lib.avq_exact_attention_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
     _lib = lib
@@ -274,6 +281,52 @@ def attention_fwd(Q, parents, children, vsum, count, P: int, tile: int, scale: f
             tile, float(scale), _dt(Q), _ptr(Y), _ptr(sel), _ptr(imp), _ptr(workspace),
             workspace.numel(), _stream(dev)))
     return Y, sel, imp
+
+
+def codebook_diagnostics(K, parents, children, leaf, count, commitment: bool = True, active: bool = True):
+    """Commitment loss E||k - k_hat||^2 [B][H] (needs K and leaf) and active
+    ratio [B][H] (needs count) -> (commit or None, active or None)."""
+    _need(K, "K", 4)
+    dev, dt = K.device, K.dtype
+    H, M0, C, d = _tree_dims(children)
+    _need(children, "children", children.dim(), dt, dev)
+    _need(parents, "parents", 3, dt, dev)
+    _need(leaf, "leaf", 3, torch.int32, dev)
+    _need(count, "count", 3, torch.int32, dev)
+    B, Hk, N, dk = K.shape
+    if Hk != H or dk != d or parents.shape != (H, M0, d) or leaf.shape != (B, H, N) or \
+            count.shape != (B, H, M0 * (1 + C)):
+        raise AvqError("inconsistent shapes")
+    lib = load_library()
+    ws = _workspace(None, int(lib.avq_diagnostics_workspace_size(B, H, N)), dev, "workspace")
+    cm = torch.empty((B, H), dtype=torch.float32, device=dev) if commitment else None
+    ac = torch.empty((B, H), dtype=torch.float32, device=dev) if active else None
+    with _on(dev):
+        _check(lib.avq_codebook_diagnostics(_ptr(K), _ptr(parents), _ptr(children), _ptr(leaf), _ptr(count),
+                                            B, H, N, d, M0, C, _dt(K), _ptr(cm), _ptr(ac), _ptr(ws),
+                                            ws.numel(), _stream(dev)))
+    return cm, ac
+
+
+def capture(Q, K, children, leaf, sel, tile: int, scale: float):
+    """Per-query capture [B][H][N]: the fraction of exact softmax weight on
+    keys whose parent the query's tile selected (sel from attention_fwd)."""
+    _need(Q, "Q", 4)
+    dev, dt = Q.device, Q.dtype
+    _need(K, "K", 4, dt, dev)
+    H, M0, C, d = _tree_dims(children)
+    _need(leaf, "leaf", 3, torch.int32, dev)
+    _need(sel, "sel", 4, torch.int32, dev)
+    B, Hq, N, dq = Q.shape
+    nt = -(-N // tile) if tile > 0 else 0
+    if K.shape != Q.shape or Hq != H or dq != d or leaf.shape != (B, H, N) or sel.shape[:3] != (B, H, nt):
+        raise AvqError("inconsistent shapes")
+    P = sel.shape[3]
+    out = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    with _on(dev):
+        _check(load_library().avq_capture(_ptr(Q), _ptr(K), _ptr(leaf), _ptr(sel) if P > 0 else None, B, H, N,
+                                          d, M0, C, P, tile, float(scale), _dt(Q), _ptr(out), _stream(dev)))
+    return out
 
 
 def exact_attention_fwd(Q, K, V, scale: float, out: Optional[torch.Tensor] = None):

@@ -233,6 +233,50 @@ int avq_attention_fwd(const void *Q, const void *parents, const void *children, 
                                                 (hipStream_t)stream));
 }
 
+size_t avq_diagnostics_workspace_size(int B, int H, int N)
+{
+    if (B < 1 || H < 1 || check_seq(B, N) != AVQ_OK) return 0;
+    return avq::diagnostics_workspace_bytes(B, H, N);
+}
+
+int avq_codebook_diagnostics(const void *K, const void *parents, const void *children, const int32_t *leaf,
+                             const int32_t *count, int B, int H, int N, int d, int M0, int C, int dtype,
+                             float *commit_out, float *active_out, void *workspace, size_t workspace_bytes,
+                             void *stream)
+{
+    AVQ_REQUIRE(commit_out || active_out, AVQ_ERR_INVALID_ARG, "no output requested");
+    AVQ_REQUIRE(!commit_out || (K && parents && children && leaf && workspace), AVQ_ERR_INVALID_ARG,
+                "the commitment loss needs K, the tree, the leaf ids and a workspace");
+    AVQ_REQUIRE(!active_out || count, AVQ_ERR_INVALID_ARG, "the active ratio needs the counts");
+    int st = check_tree(H, M0, C, d, dtype);
+    if (st != AVQ_OK) return st;
+    st = check_seq(B, N);
+    if (st != AVQ_OK) return st;
+    if (commit_out) {
+        AVQ_REQUIRE(workspace_bytes >= avq::diagnostics_workspace_bytes(B, H, N), AVQ_ERR_INVALID_ARG,
+                    "workspace too small");
+        AVQ_REQUIRE(((uintptr_t)workspace & 255u) == 0, AVQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    }
+    return hip_status(avq::launch_codebook_diagnostics(K, parents, children, leaf, count, B, H, N, d, M0, C, dtype,
+                                                       commit_out, active_out, workspace, (hipStream_t)stream));
+}
+
+int avq_capture(const void *Q, const void *K, const int32_t *leaf, const int32_t *sel, int B, int H, int N, int d,
+                int M0, int C, int P, int tile, float scale, int dtype, float *capture_out, void *stream)
+{
+    AVQ_REQUIRE(Q && K && leaf && capture_out && (sel || P == 0), AVQ_ERR_INVALID_ARG, "null pointer argument");
+    int st = check_tree(H, M0, C, d, dtype);
+    if (st != AVQ_OK) return st;
+    st = check_seq(B, N);
+    if (st != AVQ_OK) return st;
+    AVQ_REQUIRE(P >= 0 && P <= M0, AVQ_ERR_INVALID_ARG, "P must satisfy 0 <= P <= M0");
+    AVQ_REQUIRE(isfinite(scale), AVQ_ERR_INVALID_ARG, "scale must be finite");
+    AVQ_REQUIRE(tile == 32 || tile == 64 || tile == 128 || tile == 256, AVQ_ERR_UNSUPPORTED,
+                "tile must be 32, 64, 128 or 256");
+    return hip_status(avq::launch_capture(Q, K, leaf, sel, B, H, N, d, M0, C, P, tile, scale, dtype, capture_out,
+                                          (hipStream_t)stream));
+}
+
 int avq_exact_attention_fwd(const void *Q, const void *K, const void *V, int B, int H, int N, int d,
                             float scale, int dtype, void *Y_out, void *stream)
 {

@@ -123,6 +123,18 @@ hipError_t launch_attention_fwd(const void *Q, const void *parents, const void *
 // 0 if the shape does not fit its LDS budget
 int attention_child_chunk(int d, int M0, int C, int P, int tile, int dtype);
 
+// codebook diagnostics: commitment loss (needs K, the tree and leaf ids) and
+// active ratio (needs counts); workspace of diagnostics_workspace_bytes
+size_t diagnostics_workspace_bytes(int B, int H, int N);
+hipError_t launch_codebook_diagnostics(const void *K, const void *parents, const void *children,
+                                       const int32_t *leaf, const int32_t *count, int B, int H, int N, int d,
+                                       int M0, int C, int dtype, float *commit_out, float *active_out,
+                                       void *workspace, hipStream_t stream);
+// per-query capture of the exact softmax weight by the tiles' selections
+hipError_t launch_capture(const void *Q, const void *K, const int32_t *leaf, const int32_t *sel, int B, int H,
+                          int N, int d, int M0, int C, int P, int tile, float scale, int dtype, float *capture,
+                          hipStream_t stream);
+
 hipError_t launch_exact_attention(const void *Q, const void *K, const void *V, int B, int H, int N,
                                   int d, float scale, int dtype, void *Y, hipStream_t stream);
 

@@ -397,7 +397,19 @@ def main():
     else:
         y0 = Y0.cpu().double().numpy()
     g0 = dict(leaf=lf0.cpu().numpy(), count=cn0.cpu().numpy(), sel=sel0.cpu().numpy(), Y=y0)
-    del vs0, Y0, imp0
+    # the codebook measures the pages report (Table 7 commitment loss, Table 9
+    # active ratio, Table 6 capture) on the same inputs, off the timed region
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record()
+    cm, ac = avq.codebook_diagnostics(K, parents, ch, lf0, cn0)
+    d1.record()
+    cap = avq.capture(Q, K, ch, lf0, sel0, inp.T, inp.scale)
+    torch.cuda.synchronize()
+    out_diag = {"commitment_loss": round(float(cm.mean()), 6), "active_ratio": round(float(ac.mean()), 6),
+                "capture": round(float(cap.mean()), 6), "P": P,
+                "codebook_diagnostics_ms": round(d0.elapsed_time(d1), 4),
+                "sample": "input set 0, every (b, h) and query; means over them"}
+    del vs0, Y0, imp0, cap
 
     if not args.no_exact_context:
         Q, K, V = sets[0]
@@ -420,6 +432,7 @@ def main():
     if args.copy_probe:
         out["copy_probe"] = copy_probe(torch, dev)
 
+    out["diagnostics"] = out_diag
     if args.peaks:
         out["measured_peaks"] = measure_peaks(torch, dev)
 

@@ -236,6 +236,51 @@ int avq_attention_fwd(const void *Q, const void *parents, const void *children,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * avq_diagnostics_workspace_size -- bytes of device workspace that
+ * avq_codebook_diagnostics needs for the commitment loss (0 if invalid).
+ */
+size_t avq_diagnostics_workspace_size(int B, int H, int N);
+
+/*
+ * avq_codebook_diagnostics -- the codebook measures the pages report next
+ * to the method (appendix "Per-layer codebook analysis", Table 7, and
+ * "Codebook utilization", Table 9).  Off the hot path; either output may
+ * be NULL, not both.
+ *   commit_out [B][H] fp32  commitment loss E ||k - k_hat||^2: the mean
+ *              over the head's N keys of the squared distance between the
+ *              key and its leaf codeword (leaf ids from avq_assign_aggregate's
+ *              leaf_out); independent of P.  Needs K [B][H][N][d], parents,
+ *              children (the flat codebook when C = 0), leaf [B][H][N] and a
+ *              workspace of avq_diagnostics_workspace_size bytes (256-byte
+ *              aligned).
+ *   active_out [B][H] fp32  active ratio: the fraction of the head's
+ *              M0 (1 + C) codewords whose count (avq_assign_aggregate's
+ *              count_out [B][H][S_tot]) exceeds 1 % of the fair share
+ *              N / (M0 (1 + C)).
+ *   Sums run in a fixed order: repeated calls give identical bits.
+ */
+int avq_codebook_diagnostics(const void *K, const void *parents, const void *children,
+                             const int32_t *leaf, const int32_t *count, int B, int H, int N,
+                             int d, int M0, int C, int dtype, float *commit_out,
+                             float *active_out, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * avq_capture -- capture (Sec. 5.2, Table 6): for every query, the fraction
+ * of its exact softmax attention weight (scale * q.k over all N keys) that
+ * falls on keys whose parent is among the P parents its query tile
+ * selected.  O(N^2 d) like exact attention; a diagnostic, off the hot path.
+ *   Q, K       [B][H][N][d]   dtype
+ *   leaf       [B][H][N]      int32  leaf ids from avq_assign_aggregate
+ *   sel        [B][H][ceil(N/tile)][P] int32  selections from
+ *              avq_attention_fwd's sel_out (NULL allowed when P = 0)
+ *   capture_out [B][H][N]     fp32
+ */
+int avq_capture(const void *Q, const void *K, const int32_t *leaf, const int32_t *sel,
+                int B, int H, int N, int d, int M0, int C, int P, int tile, float scale,
+                int dtype, float *capture_out, void *stream);
+
+/*
  * avq_exact_attention_fwd -- exact softmax attention, non-causal
  * (Sec. 3.1), computed flash-attention style (Sec. 3.3).  Used as the
  * timing context next to AVQ and to check the one-key-per-leaf limit.
