@@ -21,6 +21,7 @@ __all__ = [
     "build_tree", "assign_aggregate", "attention_fwd", "exact_attention_fwd",
     "assign_aggregate_workspace_size", "attention_workspace_size", "forward",
     "assign_aggregate_noalloc", "NOALLOC_SCRATCH_BYTES", "codebook_diagnostics", "capture",
+    "gilbert_order", "permute_tokens",
     "AVQ_FLAG_FORCE_CHILD", "AVQ_FLAG_UNFUSED",
 ]
 
@@ -77,6 +78,10 @@ def load_library():
                                              vp, vp, vp, sz, vp]
     lib.avq_capture.restype = i32
     lib.avq_capture.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.avq_gilbert_order.restype = i32
+    lib.avq_gilbert_order.argtypes = [i32, i32, vp]
+    lib.avq_permute_tokens.restype = i32
+    lib.avq_permute_tokens.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.avq_exact_attention_fwd.restype = i32
     lib.avq_exact_attention_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
     _lib = lib
@@ -327,6 +332,33 @@ def capture(Q, K, children, leaf, sel, tile: int, scale: float):
         _check(load_library().avq_capture(_ptr(Q), _ptr(K), _ptr(leaf), _ptr(sel) if P > 0 else None, B, H, N,
                                           d, M0, C, P, tile, float(scale), _dt(Q), _ptr(out), _stream(dev)))
     return out
+
+
+def gilbert_order(W: int, H: int) -> torch.Tensor:
+    """Row-major cell indices of a W x H grid along the Gilbert curve, as a
+    CPU int32 tensor (host computation in the library)."""
+    out = torch.empty(W * H, dtype=torch.int32)
+    _check(load_library().avq_gilbert_order(W, H, _ptr(out)))
+    return out
+
+
+def permute_tokens(x: torch.Tensor, order: torch.Tensor, inverse: bool = False,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [B][H][N][d] -> rows moved into the order (out[:, :, i] =
+    x[:, :, order[i]]) or, with inverse, back out of it."""
+    _need(x, "x", 4)
+    _need(order, "order", 1, torch.int32, x.device)
+    B, H, N, d = x.shape
+    if order.numel() != N:
+        raise AvqError("order must have N entries")
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", 4, x.dtype, x.device)
+    if y.shape != x.shape:
+        raise AvqError("out must have x's shape")
+    with _on(x.device):
+        _check(load_library().avq_permute_tokens(_ptr(x), _ptr(order), B, H, N, d, _dt(x), 1 if inverse else 0,
+                                                 _ptr(y), _stream(x.device)))
+    return y
 
 
 def exact_attention_fwd(Q, K, V, scale: float, out: Optional[torch.Tensor] = None):

@@ -277,6 +277,30 @@ int avq_capture(const void *Q, const void *K, const int32_t *leaf, const int32_t
                                           (hipStream_t)stream));
 }
 
+int avq_gilbert_order(int W, int H, int32_t *order_out)
+{
+    AVQ_REQUIRE(order_out, AVQ_ERR_INVALID_ARG, "null pointer argument");
+    AVQ_REQUIRE(W >= 1 && H >= 1, AVQ_ERR_INVALID_ARG, "W and H must be >= 1");
+    AVQ_REQUIRE((int64_t)W * H <= kMaxN, AVQ_ERR_UNSUPPORTED, "W * H must be <= 1048576");
+    avq::gilbert_cells(W, H, order_out);
+    return AVQ_OK;
+}
+
+int avq_permute_tokens(const void *src, const int32_t *order, int B, int H, int N, int d, int dtype, int inverse,
+                       void *dst, void *stream)
+{
+    AVQ_REQUIRE(src && order && dst, AVQ_ERR_INVALID_ARG, "null pointer argument");
+    AVQ_REQUIRE(src != dst, AVQ_ERR_INVALID_ARG, "src and dst must not alias");
+    AVQ_REQUIRE(H >= 1 && d >= 1, AVQ_ERR_INVALID_ARG, "H and d must be >= 1");
+    AVQ_REQUIRE(valid_dtype(dtype), AVQ_ERR_INVALID_ARG, "dtype must be AVQ_F32 or AVQ_BF16");
+    int st = check_seq(B, N);
+    if (st != AVQ_OK) return st;
+    const int row_bytes = d * (dtype == AVQ_BF16 ? 2 : 4);
+    AVQ_REQUIRE(row_bytes % 16 == 0, AVQ_ERR_UNSUPPORTED, "rows must be a multiple of 16 bytes");
+    return hip_status(avq::launch_permute_rows(src, order, (int64_t)B * H * N, N, row_bytes, inverse ? 1 : 0, dst,
+                                               (hipStream_t)stream));
+}
+
 int avq_exact_attention_fwd(const void *Q, const void *K, const void *V, int B, int H, int N, int d,
                             float scale, int dtype, void *Y_out, void *stream)
 {

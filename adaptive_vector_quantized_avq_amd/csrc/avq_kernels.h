@@ -135,6 +135,12 @@ hipError_t launch_capture(const void *Q, const void *K, const int32_t *leaf, con
                           int N, int d, int M0, int C, int P, int tile, float scale, int dtype, float *capture,
                           hipStream_t stream);
 
+// Gilbert-curve order of a W x H grid's cells (host), and row gather /
+// scatter of [rows][row_bytes] tensors by a permutation of N rows per (b, h)
+void gilbert_cells(int W, int H, int32_t *out);
+hipError_t launch_permute_rows(const void *src, const int32_t *order, int64_t rows, int N, int row_bytes,
+                               int inverse, void *dst, hipStream_t stream);
+
 hipError_t launch_exact_attention(const void *Q, const void *K, const void *V, int B, int H, int N,
                                   int d, float scale, int dtype, void *Y, hipStream_t stream);
 

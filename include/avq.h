@@ -281,6 +281,32 @@ int avq_capture(const void *Q, const void *K, const int32_t *leaf, const int32_t
                 int dtype, float *capture_out, void *stream);
 
 /*
+ * avq_gilbert_order -- the token order of the pages' spatial reordering
+ *   (Sec. 4.2, Table 8; ref. [4]): the cells of a W x H token grid along the
+ *   generalized Hilbert ("Gilbert") curve, which starts at cell (0, 0) and
+ *   ends at the far corner of the longer side, so that consecutive tokens,
+ *   and therefore query tiles of any size, form compact 2D regions.
+ *   order_out  HOST buffer of W*H int32: order_out[i] = y*W + x of the i-th
+ *              cell on the curve (a permutation of the row-major indices).
+ *   Host code only, once per grid shape; 1 <= W*H <= 1048576.
+ */
+int avq_gilbert_order(int W, int H, int32_t *order_out);
+
+/*
+ * avq_permute_tokens -- move tokens into (inverse = 0: dst row i = src row
+ *   order[i]) or out of (inverse != 0: dst row order[i] = src row i) an
+ *   order, for every (b, h): Q, K and V before the forward pass, Y after it.
+ *   src, dst   [B][H][N][d] dtype, device, must not alias
+ *   order      [N] int32, device: a permutation of 0..N-1 (entries outside
+ *              that range are skipped; with repeated entries the scatter's
+ *              result is unspecified).  A grid with extra tokens (a class
+ *              token, say) uses the Gilbert order offset past them.
+ *   Rows must be a multiple of 16 bytes (d*sizeof(dtype)).
+ */
+int avq_permute_tokens(const void *src, const int32_t *order, int B, int H, int N, int d,
+                       int dtype, int inverse, void *dst, void *stream);
+
+/*
  * avq_exact_attention_fwd -- exact softmax attention, non-causal
  * (Sec. 3.1), computed flash-attention style (Sec. 3.3).  Used as the
  * timing context next to AVQ and to check the one-key-per-leaf limit.

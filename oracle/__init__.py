@@ -81,6 +81,7 @@ def _load():
             lib.avqo_capture.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int, _i32p, _i32p,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                          _dp]
+            lib.avqo_gilbert_order.argtypes = [ctypes.c_int, ctypes.c_int, _i32p]
             _lib = lib
     return _lib
 
@@ -285,6 +286,15 @@ def capture(Q, K, pstar, sel, T: int, scale: float, M0: int, threads: Optional[i
             raise MemoryError("oracle capture allocation failed")
 
     _run(unit, [(b, h) for b in range(B) for h in range(H)], threads)
+    return out
+
+
+def gilbert_order(W: int, H: int) -> np.ndarray:
+    """Row-major cell indices y*W + x of a W x H grid in the order of the
+    generalized Hilbert curve (the pages' token reordering, ref. [4])."""
+    lib = _load()
+    out = np.empty(W * H, dtype=np.int32)
+    lib.avqo_gilbert_order(W, H, _p(out, _i32p))
     return out
 
 

@@ -369,3 +369,55 @@ int avqo_capture(const double *Q /*[N][d]*/, const double *K /*[N][d]*/, int64_t
     free(chosen);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Token order along the generalized Hilbert ("Gilbert") curve of a W x H */
+/* grid (Sec. 4.2: tokens are reordered so that contiguous query tiles   */
+/* are compact 2D regions; ref. [4]).  The curve covers a rectangle      */
+/* spanned by a major axis vector a and a minor axis vector b, starting  */
+/* at its corner (x, y) and ending at the far end of a:                  */
+/*  - a rectangle one cell thick is walked straight;                     */
+/*  - a rectangle much longer than wide (2|a| > 3|b|) is cut across a     */
+/*    into two halves (the first kept even), each walked the same way;   */
+/*  - otherwise it is cut into three: a first piece along half of b      */
+/*    (axes swapped), a middle piece over the rest of b with the full a, */
+/*    and a last piece walked back along -b towards the end of a, so the */
+/*    three join end to start.                                           */
+/* order[i] receives y*W + x of the i-th cell.                            */
+/* ------------------------------------------------------------------ */
+static int sgn(int v) { return (v > 0) - (v < 0); }
+static int fdiv2(int v) { return v >= 0 ? v / 2 : -((-v + 1) / 2); }   /* floor(v / 2) */
+
+static void gilbert_walk(int x, int y, int ax, int ay, int bx, int by, int W, int32_t *order, int64_t *n)
+{
+    const int w = abs(ax + ay), h = abs(bx + by);
+    const int dax = sgn(ax), day = sgn(ay), dbx = sgn(bx), dby = sgn(by);
+    if (h == 1) {
+        for (int i = 0; i < w; ++i) order[(*n)++] = (y + i * day) * W + (x + i * dax);
+        return;
+    }
+    if (w == 1) {
+        for (int i = 0; i < h; ++i) order[(*n)++] = (y + i * dby) * W + (x + i * dbx);
+        return;
+    }
+    int ax2 = fdiv2(ax), ay2 = fdiv2(ay), bx2 = fdiv2(bx), by2 = fdiv2(by);
+    const int w2 = abs(ax2 + ay2), h2 = abs(bx2 + by2);
+    if (2 * w > 3 * h) {
+        if ((w2 & 1) && w > 2) { ax2 += dax; ay2 += day; }
+        gilbert_walk(x, y, ax2, ay2, bx, by, W, order, n);
+        gilbert_walk(x + ax2, y + ay2, ax - ax2, ay - ay2, bx, by, W, order, n);
+    } else {
+        if ((h2 & 1) && h > 2) { bx2 += dbx; by2 += dby; }
+        gilbert_walk(x, y, bx2, by2, ax2, ay2, W, order, n);
+        gilbert_walk(x + bx2, y + by2, ax, ay, bx - bx2, by - by2, W, order, n);
+        gilbert_walk(x + (ax - dax) + (bx2 - dbx), y + (ay - day) + (by2 - dby), -bx2, -by2,
+                     -(ax - ax2), -(ay - ay2), W, order, n);
+    }
+}
+
+void avqo_gilbert_order(int W, int H, int32_t *order /*[W*H]*/)
+{
+    int64_t n = 0;
+    if (W >= H) gilbert_walk(0, 0, W, 0, 0, H, W, order, &n);
+    else gilbert_walk(0, 0, 0, H, W, 0, W, order, &n);
+}

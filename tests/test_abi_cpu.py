@@ -145,3 +145,23 @@ def test_invalid_arguments_are_rejected_before_launch(lib):
     assert lib.avq_build_tree(p, 1, 4, 4, 64, 1, p, p, None, None) == -1
     assert lib.avq_build_tree(p, 1, 4, 4, 64, 5, p, p, p, None) == -1
     assert lib.avq_exact_attention_fwd(p, p, p, 1, 1, 16, 80, 1.0, 1, p, None) == -2
+
+
+@pytest.mark.parametrize("W,H", [(1, 1), (1, 9), (7, 1), (4, 4), (5, 3), (3, 5), (28, 28), (64, 64),
+                                 (13, 40), (256, 256), (33, 18), (100, 7)])
+def test_gilbert_order_matches_the_oracle(lib, W, H):
+    # host code of the library (no GPU call) against the oracle's own
+    # implementation of the curve
+    import numpy as np
+    import oracle
+    import adaptive_vector_quantized_avq_amd as avq
+    np.testing.assert_array_equal(avq.gilbert_order(W, H).numpy(), oracle.gilbert_order(W, H))
+
+
+def test_gilbert_order_rejects_bad_grids(lib):
+    import adaptive_vector_quantized_avq_amd as avq
+    buf = ctypes.create_string_buffer(64)
+    assert lib.avq_gilbert_order(0, 4, buf) == -1
+    assert lib.avq_gilbert_order(2048, 1024, buf) == -2
+    assert lib.avq_gilbert_order(4, 4, None) == -1
+    assert avq.gilbert_order(2, 3).numel() == 6

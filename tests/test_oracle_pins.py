@@ -491,3 +491,57 @@ def test_capture_limits_and_softmax_reformulation():
     assert np.abs(oracle.capture(Q, K, r["pstar"], all_sel, inp.T, inp.scale, inp.M0) - 1).max() < 1e-12
     none = np.zeros((1, 2, inp.ntiles, 0), dtype=np.int32)
     assert (oracle.capture(Q, K, r["pstar"], none, inp.T, inp.scale, inp.M0) == 0).all()
+
+
+# ---------------------------------------------------------------- Gilbert order
+
+def _hilbert_d2xy(n, dist):
+    """Classical Hilbert curve on an n x n grid (n a power of two), index ->
+    (x, y), by the textbook quadrant-rotation recursion written iteratively."""
+    x = y = 0
+    t = dist
+    s = 1
+    while s < n:
+        rx = 1 & (t // 2)
+        ry = 1 & (t ^ rx)
+        if ry == 0:
+            if rx == 1:
+                x, y = s - 1 - x, s - 1 - y
+            x, y = y, x
+        x += s * rx
+        y += s * ry
+        t //= 4
+        s *= 2
+    return x, y
+
+
+@pytest.mark.parametrize("W,H", [(1, 1), (1, 7), (9, 1), (2, 2), (4, 4), (3, 5), (5, 3), (6, 4), (7, 7),
+                                 (10, 3), (28, 28), (30, 30), (64, 64), (13, 40), (256, 256), (33, 18)])
+def test_gilbert_order_is_a_path_over_the_grid(W, H):
+    o = oracle.gilbert_order(W, H)
+    assert sorted(o.tolist()) == list(range(W * H))               # a permutation of the cells
+    x, y = o % W, o // W
+    step = np.abs(np.diff(x)) + np.abs(np.diff(y))
+    cheb = np.maximum(np.abs(np.diff(x)), np.abs(np.diff(y)))
+    assert (cheb == 1).all() if W * H > 1 else True               # every step to a touching cell
+    assert (step == 2).sum() <= 1                                 # at most one diagonal step
+    if W * H > 1:                                                 # corner to corner along the long side
+        assert (x[0], y[0]) == (0, 0)
+        assert ((x[-1], y[-1]) == (W - 1, 0)) if W >= H else ((x[-1], y[-1]) == (0, H - 1))
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 32])
+def test_gilbert_on_power_of_two_squares_is_the_hilbert_curve(n):
+    o = oracle.gilbert_order(n, n)
+    ref = [_hilbert_d2xy(n, i) for i in range(n * n)]
+    assert [(int(v % n), int(v // n)) for v in o] == ref
+
+
+def test_gilbert_tiles_are_compact():
+    # 64 x 64 grid in tiles of 128 cells: every tile's bounding box is far
+    # smaller than a raster tile's (2 rows x 64 columns)
+    o = oracle.gilbert_order(64, 64)
+    x, y = o % 64, o // 64
+    spans = [(x[t:t + 128].max() - x[t:t + 128].min() + 1) * (y[t:t + 128].max() - y[t:t + 128].min() + 1)
+             for t in range(0, 64 * 64, 128)]
+    assert max(spans) <= 256
