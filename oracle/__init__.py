@@ -82,6 +82,19 @@ def _load():
                                          ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                          _dp]
             lib.avqo_gilbert_order.argtypes = [ctypes.c_int, ctypes.c_int, _i32p]
+            lib.avqo_build_tree3.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, _dp, _dp]
+            lib.avqo_assign3.argtypes = [_dp, ctypes.c_int64, ctypes.c_int, _dp, _dp, _dp,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         _i32p, _i32p, _dp, _dp, _dp]
+            lib.avqo_aggregate3.argtypes = [_dp, ctypes.c_int64, ctypes.c_int, _i32p,
+                                            ctypes.c_int, ctypes.c_int, _dp, _i64p]
+            lib.avqo_attention3.restype = ctypes.c_int
+            lib.avqo_attention3.argtypes = [_dp, ctypes.c_int64, ctypes.c_int, _dp, _dp, _dp,
+                                            ctypes.c_int, ctypes.c_int, _dp, _i64p,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                            _i32p, _i32p, ctypes.c_int64, ctypes.c_int64,
+                                            _dp, _dp, _i32p, _dp, _i32p]
             _lib = lib
     return _lib
 
@@ -296,6 +309,131 @@ def gilbert_order(W: int, H: int) -> np.ndarray:
     out = np.empty(W * H, dtype=np.int32)
     lib.avqo_gilbert_order(W, H, _p(out, _i32p))
     return out
+
+
+# ---------------------------------------------------------------------------
+# three-level tree (roots -> children -> leaves)
+
+def build_tree3(leaves, dtype: str):
+    """leaves [H][M0][C][C][d] float64 -> (level0 [H][M0][d], level1
+    [H][M0][C][d], sqnorm [H][M0(1+C+C^2)]: roots, children, leaves), the two
+    upper levels rounded to dtype."""
+    lib = _load()
+    leaves = _f64(leaves)
+    H, M0, C, _, d = leaves.shape
+    l0 = np.empty((H, M0, d))
+    l1 = np.empty((H, M0, C, d))
+    n1 = M0 * C
+    sq = np.empty((H, M0 + n1 + n1 * C))
+    for h in range(H):
+        lib.avqo_build_tree3(_p(leaves[h], _dp), M0, C, d, 1 if dtype == "bf16" else 0,
+                             _p(l1[h], _dp), _p(l0[h], _dp))
+        for lo, rows, n in ((0, l0[h], M0), (M0, l1[h], n1), (M0 + n1, leaves[h], n1 * C)):
+            tmp = np.empty(n)
+            lib.avqo_sqnorm(_p(np.ascontiguousarray(rows), _dp), n, d, _p(tmp, _dp))
+            sq[h, lo:lo + n] = tmp
+    return l0, l1, sq
+
+
+def assign3(K, level0, level1, leaves, force_child: bool = False, threads: Optional[int] = None):
+    """K [B][H][N][d] -> dict of [B][H][N] arrays: pstar, leaf (int32, slot
+    in the three-level layout), gap0, gap1, gap2 (relative top-2 gaps at
+    each level; gap2 is +inf for keys that stayed at their root)."""
+    lib = _load()
+    K, level0, level1, leaves = _f64(K), _f64(level0), _f64(level1), _f64(leaves)
+    B, H, N, d = K.shape
+    M0, C = leaves.shape[1], leaves.shape[2]
+    out = {k: np.empty((B, H, N), dtype=np.int32) for k in ("pstar", "leaf")}
+    out.update({k: np.empty((B, H, N)) for k in ("gap0", "gap1", "gap2")})
+
+    def unit(bh):
+        b, h = bh
+        lib.avqo_assign3(_p(K[b, h], _dp), N, d, _p(level0[h], _dp), _p(level1[h], _dp),
+                         _p(leaves[h], _dp), M0, C, 1 if force_child else 0,
+                         _p(out["pstar"][b, h], _i32p), _p(out["leaf"][b, h], _i32p),
+                         _p(out["gap0"][b, h], _dp), _p(out["gap1"][b, h], _dp),
+                         _p(out["gap2"][b, h], _dp))
+
+    _run(unit, [(b, h) for b in range(B) for h in range(H)], threads)
+    return out
+
+
+def aggregate3(V, leaf, M0: int, C: int, threads: Optional[int] = None):
+    """V [B][H][N][d], leaf [B][H][N] (three-level slots) -> (vsum
+    [B][H][S3][d], count [B][H][S3]) with every slot holding its whole cell."""
+    lib = _load()
+    V = _f64(V)
+    leaf = np.ascontiguousarray(leaf, dtype=np.int32)
+    B, H, N, d = V.shape
+    S = M0 * (1 + C + C * C)
+    vsum = np.empty((B, H, S, d))
+    count = np.empty((B, H, S), dtype=np.int64)
+
+    def unit(bh):
+        b, h = bh
+        lib.avqo_aggregate3(_p(V[b, h], _dp), N, d, _p(leaf[b, h], _i32p), M0, C,
+                            _p(vsum[b, h], _dp), _p(count[b, h], _i64p))
+
+    _run(unit, [(b, h) for b in range(B) for h in range(H)], threads)
+    return vsum, count
+
+
+def attention3(Q, level0, level1, leaves, vsum, count, P: int, T: int, scale: float,
+               forced_sel0=None, forced_sel1=None, tiles=None, threads: Optional[int] = None):
+    """Q [B][H][N][d] -> dict: Y [B][H][N][d]; imp0 [B][H][ntiles][M0] and
+    sel0 [B][H][ntiles][P] (roots, sel0 in importance order); imp1
+    [B][H][ntiles][P*C] (children of the selected roots by ascending index)
+    and sel1 [B][H][ntiles][P] (selected children p*C + a, ascending).
+    `tiles` = (t_begin, t_end) restricts the work (other rows of Y are NaN)."""
+    lib = _load()
+    Q, level0, level1, leaves, vsum = _f64(Q), _f64(level0), _f64(level1), _f64(leaves), _f64(vsum)
+    count = np.ascontiguousarray(count, dtype=np.int64)
+    B, H, N, d = Q.shape
+    M0, C = leaves.shape[1], leaves.shape[2]
+    nt = -(-N // T)
+    t0, t1 = tiles if tiles is not None else (0, nt)
+    Y = np.full((B, H, N, d), np.nan)
+    imp0 = np.zeros((B, H, nt, M0))
+    sel0 = np.zeros((B, H, nt, P), dtype=np.int32)
+    imp1 = np.zeros((B, H, nt, P * C))
+    sel1 = np.zeros((B, H, nt, P), dtype=np.int32)
+    f0 = None if forced_sel0 is None else np.ascontiguousarray(forced_sel0, dtype=np.int32)
+    f1 = None if forced_sel1 is None else np.ascontiguousarray(forced_sel1, dtype=np.int32)
+    threads = threads or default_threads()
+    per = max(1, -(-(t1 - t0) * B * H // (4 * threads)))
+    units = [(b, h, a, min(a + per, t1)) for b in range(B) for h in range(H)
+             for a in range(t0, t1, per)]
+
+    def unit(u):
+        b, h, a, e = u
+        rc = lib.avqo_attention3(_p(Q[b, h], _dp), N, d, _p(level0[h], _dp), _p(level1[h], _dp),
+                                 _p(leaves[h], _dp), M0, C, _p(vsum[b, h], _dp),
+                                 _p(count[b, h], _i64p), P, T, float(scale),
+                                 _p(f0[b, h] if f0 is not None else None, _i32p),
+                                 _p(f1[b, h] if f1 is not None else None, _i32p),
+                                 a, e, _p(Y[b, h], _dp), _p(imp0[b, h], _dp), _p(sel0[b, h], _i32p),
+                                 _p(imp1[b, h], _dp), _p(sel1[b, h], _i32p))
+        if rc != 0:
+            raise MemoryError("oracle attention allocation failed")
+
+    _run(unit, units, threads)
+    return dict(Y=Y, imp0=imp0, sel0=sel0, imp1=imp1, sel1=sel1)
+
+
+def forward3(inp, P: Optional[int] = None, T: Optional[int] = None, force_child=False,
+             threads: Optional[int] = None, tiles=None):
+    """Whole three-level forward pass on a `synth.Inputs` workload whose
+    `children` holds the leaves [H][M0][C][C][d]."""
+    from synth import storage_to_f64
+    lv = storage_to_f64(inp.children, inp.dtype)
+    l0, l1, sq = build_tree3(lv, inp.dtype)
+    P = inp.P if P is None else P
+    T = inp.T if T is None else T
+    a = assign3(storage_to_f64(inp.K, inp.dtype), l0, l1, lv, force_child, threads)
+    vsum, count = aggregate3(storage_to_f64(inp.V, inp.dtype), a["leaf"], inp.M0, inp.C, threads)
+    att = attention3(storage_to_f64(inp.Q, inp.dtype), l0, l1, lv, vsum, count, P, T, inp.scale,
+                     tiles=tiles, threads=threads)
+    return dict(level0=l0, level1=l1, sqnorm=sq, vsum=vsum, count=count, **a, **att)
 
 
 def forward(inp, P: Optional[int] = None, T: Optional[int] = None, force_child=False,

@@ -421,3 +421,278 @@ void avqo_gilbert_order(int W, int H, int32_t *order /*[W*H]*/)
     if (W >= H) gilbert_walk(0, 0, W, 0, 0, H, W, order, &n);
     else gilbert_walk(0, 0, 0, H, W, 0, W, order, &n);
 }
+
+/* ------------------------------------------------------------------ */
+/* Three-level tree (Sec. 6 "Discussion and Conclusion": a deeper       */
+/* hierarchy adds P*C codes per extra level).  The pages propose it and */
+/* give no algorithm; the readings taken here (each in the design doc):      */
+/*  - leaves L[p][a][b] are given; level 1 c[p][a] is the mean of its C  */
+/*    leaves and the root r[p] the mean of its C*C leaves (the mean      */
+/*    constraint at every level), each rounded once to the storage type; */
+/*  - assignment descends one level at a time: nearest root, then that   */
+/*    root's children (taken if strictly closer than the root), then     */
+/*    that child's leaves (taken if strictly closer than the child);     */
+/*  - every slot holds its whole cell: root p all keys under p, child    */
+/*    (p, a) all keys that reached it (including those that went on to a */
+/*    leaf), leaf slots the keys assigned there;                         */
+/*  - stage 2 repeats importance, top-P and correction once per level:   */
+/*    level-1 importance w_c = n_c sum_i exp(S_ic)/Z1_i over the P*C      */
+/*    children of the selected roots, Z1 the denominator after the       */
+/*    level-1 correction; the top P children (ties to the lower child     */
+/*    index) have their logits recovered as the mean of their leaves'   */
+/*    logits and are replaced by their leaves as in O7.                  */
+/* Slot layout per head: [0, M0) roots, [M0, M0 + M0*C) children         */
+/* (p*C + a), [M0 + M0*C, M0 + M0*C + M0*C*C) leaves ((p*C + a)*C + b).   */
+/* ------------------------------------------------------------------ */
+void avqo_build_tree3(const double *leaves /*[M0][C][C][d]*/, int M0, int C, int d, int dtype,
+                      double *level1 /*[M0][C][d]*/, double *level0 /*[M0][d]*/)
+{
+    for (int p = 0; p < M0; ++p)
+        for (int t = 0; t < d; ++t) {
+            double all = 0.0;
+            for (int a = 0; a < C; ++a) {
+                double s = 0.0;
+                for (int b = 0; b < C; ++b) s += leaves[(((int64_t)p * C + a) * C + b) * d + t];
+                all += s;
+                double mean = s / C;
+                level1[((int64_t)p * C + a) * d + t] = dtype == 1 ? avqo_round_bf16(mean) : (double)(float)mean;
+            }
+            double mean = all / ((double)C * C);
+            level0[(int64_t)p * d + t] = dtype == 1 ? avqo_round_bf16(mean) : (double)(float)mean;
+        }
+}
+
+/* gap0: relative top-2 gap over the roots; gap1: over {p*} U children(p*);
+ * gap2: over {(p*, a*)} U leaves(p*, a*) when the key reached a child,
+ * +infinity otherwise.  force_child != 0 treats the distance to the level
+ * above as +infinity at both steps. */
+void avqo_assign3(const double *K /*[N][d]*/, int64_t N, int d, const double *level0 /*[M0][d]*/,
+                  const double *level1 /*[M0][C][d]*/, const double *leaves /*[M0][C][C][d]*/,
+                  int M0, int C, int force_child, int32_t *pstar, int32_t *leaf,
+                  double *gap0, double *gap1, double *gap2)
+{
+    double *Dp = (double *)malloc(sizeof(double) * (size_t)M0);
+    double *Dl = (double *)malloc(sizeof(double) * (size_t)(C + 1));
+    double *Dg = (double *)malloc(sizeof(double) * (size_t)(C + 1));
+    for (int64_t k = 0; k < N; ++k) {
+        const double *key = K + k * d;
+        int best = 0;
+        for (int p = 0; p < M0; ++p) {
+            Dp[p] = sqdist(key, level0 + (int64_t)p * d, d);
+            if (Dp[p] < Dp[best]) best = p;
+        }
+        pstar[k] = best;
+        if (gap0) gap0[k] = rel_gap(Dp, M0);
+        int a = 0;
+        for (int c = 0; c < C; ++c) {
+            Dl[c] = sqdist(key, level1 + ((int64_t)best * C + c) * d, d);
+            if (Dl[c] < Dl[a]) a = c;
+        }
+        const int to_child = force_child || Dl[a] < Dp[best];
+        if (gap1) {
+            Dl[C] = Dp[best];
+            gap1[k] = rel_gap(Dl, force_child ? C : C + 1);
+        }
+        if (!to_child) {
+            leaf[k] = best;
+            if (gap2) gap2[k] = INFINITY;
+            continue;
+        }
+        const int64_t ci = (int64_t)best * C + a;   /* child index */
+        int b = 0;
+        for (int g = 0; g < C; ++g) {
+            Dg[g] = sqdist(key, leaves + (ci * C + g) * d, d);
+            if (Dg[g] < Dg[b]) b = g;
+        }
+        const int to_leaf = force_child || Dg[b] < Dl[a];
+        leaf[k] = to_leaf ? (int32_t)(M0 + (int64_t)M0 * C + ci * C + b) : (int32_t)(M0 + ci);
+        if (gap2) {
+            Dg[C] = Dl[a];
+            gap2[k] = rel_gap(Dg, force_child ? C : C + 1);
+        }
+    }
+    free(Dp);
+    free(Dl);
+    free(Dg);
+}
+
+void avqo_aggregate3(const double *V /*[N][d]*/, int64_t N, int d, const int32_t *leaf, int M0, int C,
+                     double *vsum /*[S3][d]*/, int64_t *count /*[S3]*/)
+{
+    const int64_t n1 = (int64_t)M0 * C, S = M0 + n1 + n1 * C;
+    memset(vsum, 0, sizeof(double) * (size_t)(S * d));
+    memset(count, 0, sizeof(int64_t) * (size_t)S);
+    for (int64_t k = 0; k < N; ++k) {
+        const int64_t l = leaf[k];
+        int64_t slots[3];
+        int ns = 0;
+        if (l < M0) {
+            slots[ns++] = l;
+        } else if (l < M0 + n1) {
+            slots[ns++] = (l - M0) / C;
+            slots[ns++] = l;
+        } else {
+            const int64_t ci = (l - M0 - n1) / C;
+            slots[ns++] = ci / C;
+            slots[ns++] = M0 + ci;
+            slots[ns++] = l;
+        }
+        for (int s = 0; s < ns; ++s) {
+            for (int t = 0; t < d; ++t) vsum[slots[s] * d + t] += V[k * d + t];
+            count[slots[s]] += 1;
+        }
+    }
+}
+
+/* one refinement level for query row q: the `nsel` codewords `sel` of the
+ * level above (codeword j's C children at rows j*C .. j*C+C-1 of `kids`,
+ * their slots at slot0 + j*C + c) are replaced by their children, the
+ * parent logit recovered as the mean of the children's logits (O7).
+ * Child logits are written to s_out[k*C + c] when s_out is not null. */
+static void correct_level(const double *q, int d, double scale, const int32_t *sel, int nsel,
+                          const double *kids, int C, int64_t slot0, const double *vsum,
+                          const int64_t *count, double *x, double *Z, double *m, double *s,
+                          double *s_out)
+{
+    for (int k = 0; k < nsel; ++k) {
+        const int64_t j = sel[k];
+        double mean = 0.0, smax = -INFINITY;
+        for (int c = 0; c < C; ++c) {
+            const double *cw = kids + (j * C + c) * d;
+            double dot = 0.0;
+            for (int u = 0; u < d; ++u) dot += q[u] * cw[u];
+            s[c] = scale * dot;
+            mean += s[c];
+            if (s[c] > smax) smax = s[c];
+        }
+        mean /= C;
+        if (smax > *m) {
+            const double a = exp(*m - smax);
+            for (int u = 0; u < d; ++u) x[u] *= a;
+            *Z *= a;
+            *m = smax;
+        }
+        const double ep = exp(mean - *m);
+        for (int c = 0; c < C; ++c) {
+            const int64_t slot = slot0 + j * C + c;
+            const double dA = exp(s[c] - *m) - ep;
+            for (int u = 0; u < d; ++u) x[u] += dA * vsum[slot * d + u];
+            *Z += dA * (double)count[slot];
+            if (s_out) s_out[(int64_t)k * C + c] = s[c];
+        }
+    }
+}
+
+static int cmp_int32(const void *a, const void *b)
+{
+    const int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* Tiles [t_begin, t_end).  imp0 [ntiles][M0] and sel0 [ntiles][P] as in
+ * avqo_attention (sel0 in importance order); imp1 [ntiles][P*C] is the
+ * level-1 importance of the children of the selected roots listed by
+ * ascending child index, sel1 [ntiles][P] the selected children's indices
+ * (p*C + a) in ascending order.  forced_sel0 / forced_sel1 (nullable)
+ * replace the two choices.  Returns 0, or -1 on allocation failure. */
+int avqo_attention3(const double *Q /*[N][d]*/, int64_t N, int d, const double *level0 /*[M0][d]*/,
+                    const double *level1 /*[M0][C][d]*/, const double *leaves /*[M0][C][C][d]*/,
+                    int M0, int C, const double *vsum /*[S3][d]*/, const int64_t *count, int P, int T,
+                    double scale, const int32_t *forced_sel0, const int32_t *forced_sel1,
+                    int64_t t_begin, int64_t t_end, double *Y /*[N][d]*/, double *imp0, int32_t *sel0,
+                    double *imp1, int32_t *sel1)
+{
+    const int PC = P * C;
+    const int64_t n1 = (int64_t)M0 * C;
+    double *E = (double *)malloc(sizeof(double) * (size_t)T * M0);
+    double *m = (double *)malloc(sizeof(double) * (size_t)T);
+    double *Z = (double *)malloc(sizeof(double) * (size_t)T);
+    double *X = (double *)malloc(sizeof(double) * (size_t)T * d);
+    double *s = (double *)malloc(sizeof(double) * (size_t)(M0 > C ? M0 : C));
+    double *S1 = (double *)malloc(sizeof(double) * (size_t)T * (PC > 0 ? PC : 1));
+    double *w = (double *)malloc(sizeof(double) * (size_t)(M0 > PC ? M0 : (PC > 0 ? PC : 1)));
+    wi_pair *order = (wi_pair *)malloc(sizeof(wi_pair) * (size_t)(M0 > PC ? M0 : (PC > 0 ? PC : 1)));
+    int32_t *ch0 = (int32_t *)malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+    int32_t *ch1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+    if (!E || !m || !Z || !X || !s || !S1 || !w || !order || !ch0 || !ch1) {
+        free(E); free(m); free(Z); free(X); free(s); free(S1); free(w); free(order); free(ch0); free(ch1);
+        return -1;
+    }
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const int64_t i0 = t * T, i1 = i0 + T < N ? i0 + T : N;
+        const int nI = (int)(i1 - i0);
+
+        /* O4: parent pass over the roots */
+        for (int ii = 0; ii < nI; ++ii) {
+            const double *q = Q + (i0 + ii) * d;
+            double mx = -INFINITY;
+            for (int j = 0; j < M0; ++j) {
+                double dot = 0.0;
+                for (int u = 0; u < d; ++u) dot += q[u] * level0[(int64_t)j * d + u];
+                s[j] = scale * dot;
+                if (s[j] > mx) mx = s[j];
+            }
+            m[ii] = mx;
+            double z = 0.0, *x = X + (int64_t)ii * d;
+            for (int u = 0; u < d; ++u) x[u] = 0.0;
+            for (int j = 0; j < M0; ++j) {
+                const double e = exp(s[j] - mx);
+                E[(int64_t)ii * M0 + j] = e;
+                z += e * (double)count[j];
+                for (int u = 0; u < d; ++u) x[u] += e * vsum[(int64_t)j * d + u];
+            }
+            Z[ii] = z;
+        }
+        /* O5, O6 at the roots */
+        for (int j = 0; j < M0; ++j) {
+            double acc = 0.0;
+            for (int ii = 0; ii < nI; ++ii) acc += E[(int64_t)ii * M0 + j] * (double)count[j] / Z[ii];
+            w[j] = acc;
+            if (imp0) imp0[t * M0 + j] = acc;
+        }
+        if (forced_sel0) {
+            for (int k = 0; k < P; ++k) ch0[k] = forced_sel0[t * P + k];
+        } else {
+            for (int j = 0; j < M0; ++j) { order[j].w = w[j]; order[j].idx = j; }
+            qsort(order, (size_t)M0, sizeof(wi_pair), cmp_pair);
+            for (int k = 0; k < P; ++k) ch0[k] = order[k].idx;
+        }
+        if (sel0) for (int k = 0; k < P; ++k) sel0[t * P + k] = ch0[k];
+        /* candidates of level 1: children of the selected roots by ascending index */
+        qsort(ch0, (size_t)P, sizeof(int32_t), cmp_int32);
+
+        /* O7 at level 1 (roots -> children), child logits kept */
+        for (int ii = 0; ii < nI; ++ii)
+            correct_level(Q + (i0 + ii) * d, d, scale, ch0, P, level1, C, M0, vsum, count,
+                          X + (int64_t)ii * d, &Z[ii], &m[ii], s, S1 + (int64_t)ii * PC);
+
+        /* level-1 importance over the P*C candidates, then top-P */
+        for (int k = 0; k < PC; ++k) {
+            const int64_t ci = (int64_t)ch0[k / C] * C + k % C;
+            double acc = 0.0;
+            for (int ii = 0; ii < nI; ++ii)
+                acc += exp(S1[(int64_t)ii * PC + k] - m[ii]) * (double)count[M0 + ci] / Z[ii];
+            w[k] = acc;
+            if (imp1) imp1[t * PC + k] = acc;
+        }
+        if (forced_sel1) {
+            for (int k = 0; k < P; ++k) ch1[k] = forced_sel1[t * P + k];
+        } else {
+            for (int k = 0; k < PC; ++k) { order[k].w = w[k]; order[k].idx = (int)((int64_t)ch0[k / C] * C + k % C); }
+            qsort(order, (size_t)PC, sizeof(wi_pair), cmp_pair);
+            for (int k = 0; k < P; ++k) ch1[k] = order[k].idx;
+        }
+        qsort(ch1, (size_t)P, sizeof(int32_t), cmp_int32);
+        if (sel1) for (int k = 0; k < P; ++k) sel1[t * P + k] = ch1[k];
+
+        /* O7 at level 2 (children -> leaves), then O8 */
+        for (int ii = 0; ii < nI; ++ii) {
+            double *x = X + (int64_t)ii * d;
+            correct_level(Q + (i0 + ii) * d, d, scale, ch1, P, leaves, C, M0 + n1, vsum, count, x,
+                          &Z[ii], &m[ii], s, NULL);
+            for (int u = 0; u < d; ++u) Y[(i0 + ii) * d + u] = x[u] / Z[ii];
+        }
+    }
+    free(E); free(m); free(Z); free(X); free(s); free(S1); free(w); free(order); free(ch0); free(ch1);
+    return 0;
+}

@@ -12,6 +12,7 @@ from .generators import (  # noqa: F401
     Inputs,
     generate,
     generate_dyadic,
+    generate_dyadic3,
     generate_one_key_per_leaf,
     f64_to_bf16_bits,
     bf16_bits_to_f64,

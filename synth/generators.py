@@ -51,12 +51,19 @@ WORKLOADS = {
     # pages' fixed-codebook baseline with M = 256 codewords (Table 2).
     "flat-64k": dict(B=1, H=8, N=65536, d=64, M0=256, C=0, P=0, T=128,
                      dtype="bf16", keys="uniform", queries="clustered"),
+    # Three-level tree (roots -> children -> leaves, the deeper hierarchy
+    # the pages propose as the next step, Sec. 6) at the long-sequence
+    # shape, with the pages' 64/16/8 root configuration: 64 roots, 512
+    # children, 4096 leaves per head; P = 16 refinements at each level.
+    "deep-64k": dict(B=1, H=8, N=65536, d=64, M0=64, C=8, P=16, T=128,
+                     dtype="bf16", keys="uniform", queries="clustered", levels=3),
 }
 WORKLOAD_ORDER = ["tiny-f32", "vit-b", "seg-zipf", "long-64k", "wide-d128"]
 # further workloads (not among the five the parity suite sweeps by name)
-EXTRA_WORKLOADS = ["flat-64k"]
+EXTRA_WORKLOADS = ["flat-64k", "deep-64k"]
 
 CHILD_SPREAD = 0.3      # std of child offsets around their parent
+LEAF_SPREAD = 0.15      # std of leaf offsets around their child (three-level trees)
 KEY_SPREAD = 0.1        # std of key noise around its generating leaf
 QUERY_SPREAD = 0.5      # std of query noise around its parent
 ZIPF_EXPONENT = 1.1
@@ -118,14 +125,19 @@ class Inputs:
     dtype: str
     scale: float
     seed: int
-    children: np.ndarray      # [H][M0][C][d] storage dtype ([H][M0][d] for a flat codebook, C = 0)
+    children: np.ndarray      # [H][M0][C][d] storage dtype ([H][M0][d] for a flat codebook, C = 0;
+                              # the leaves [H][M0][C][C][d] of a three-level tree)
     Q: np.ndarray             # [B][H][N][d]
     K: np.ndarray
     V: np.ndarray
-    true_leaf: np.ndarray     # [B][H][N] int32: slot of the generating leaf (M0 + p*C + c; p if C = 0)
+    true_leaf: np.ndarray     # [B][H][N] int32: slot of the generating leaf (M0 + p*C + c; p if C = 0;
+                              # M0 + M0*C + (p*C + a)*C + b for a three-level tree)
+    levels: int = 2
 
     @property
     def S_tot(self) -> int:
+        if self.levels == 3:
+            return self.M0 * (1 + self.C + self.C * self.C)
         return self.M0 * (1 + self.C)
 
     @property
@@ -163,12 +175,17 @@ def generate(name: str, seed: Optional[int] = None, **overrides) -> Inputs:
     B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]
     M0, C, P, T = spec["M0"], spec["C"], spec["P"], spec["T"]
     dtype = spec["dtype"]
+    levels = spec.get("levels", 2)
     rng = np.random.Generator(np.random.PCG64(seed))
     flat_vq = C == 0          # a flat codebook: the M0 codewords are the leaves
-    L = M0 if flat_vq else M0 * C
+    deep = levels == 3        # roots -> children -> leaves
+    if deep and flat_vq:
+        raise ValueError("a three-level tree needs C > 0")
+    L = M0 if flat_vq else M0 * C * (C if deep else 1)
 
     parents64 = np.empty((H, M0, d))
     children64 = np.empty((H, M0, C, d))
+    leaves64 = np.empty((H, M0, C, C, d)) if deep else None
     zipf_perm = [None] * H
     aniso = [None] * H
     for h in range(H):
@@ -178,6 +195,10 @@ def generate(name: str, seed: Optional[int] = None, **overrides) -> Inputs:
             off = rng.normal(0.0, CHILD_SPREAD, size=(M0, C, d))
             off -= off.mean(axis=1, keepdims=True)
             children64[h] = par[:, None, :] + off
+        if deep:
+            off2 = rng.normal(0.0, LEAF_SPREAD, size=(M0, C, C, d))
+            off2 -= off2.mean(axis=2, keepdims=True)
+            leaves64[h] = children64[h][:, :, None, :] + off2
         if spec["keys"] == "zipf":
             zipf_perm[h] = rng.permutation(L)
         elif spec["keys"] == "anisotropic":
@@ -192,7 +213,8 @@ def generate(name: str, seed: Optional[int] = None, **overrides) -> Inputs:
 
     for b in range(B):
         for h in range(H):
-            flat = parents64[h] if flat_vq else children64[h].reshape(L, d)
+            flat = (parents64[h] if flat_vq else
+                    leaves64[h].reshape(L, d) if deep else children64[h].reshape(L, d))
             if spec["keys"] == "zipf":
                 rank = rng.choice(L, size=N, p=zp)
                 leaf = zipf_perm[h][rank]
@@ -212,14 +234,16 @@ def generate(name: str, seed: Optional[int] = None, **overrides) -> Inputs:
             K[b, h] = to_storage(k64, dtype)
             Q[b, h] = to_storage(q64, dtype)
             V[b, h] = to_storage(v64, dtype)
-            true_leaf[b, h] = leaf if flat_vq else M0 + leaf
+            true_leaf[b, h] = (leaf if flat_vq else
+                               M0 + M0 * C + leaf if deep else M0 + leaf)
 
-    # a flat codebook is passed as [H][M0][d]: its codewords are the parents
-    codebook = parents64 if flat_vq else children64
+    # a flat codebook is passed as [H][M0][d]: its codewords are the parents;
+    # a three-level tree as its leaves [H][M0][C][C][d]
+    codebook = parents64 if flat_vq else leaves64 if deep else children64
     return Inputs(name=name, B=B, H=H, N=N, d=d, M0=M0, C=C, P=P, T=T,
                   dtype=dtype, scale=1.0 / math.sqrt(d), seed=seed,
                   children=to_storage(codebook, dtype), Q=Q, K=K, V=V,
-                  true_leaf=true_leaf)
+                  true_leaf=true_leaf, levels=levels)
 
 
 def generate_dyadic(seed: int, B=1, H=1, N=256, d=64, M0=8, C=4, P=2, T=64,
@@ -278,3 +302,63 @@ def generate_one_key_per_leaf(seed: int, B=1, H=1, d=64, M0=8, C=4, T=64,
             base.true_leaf[b, h] = M0 + np.arange(L, dtype=np.int32)
     base.name = "one-key-per-leaf"
     return base
+
+
+def generate_dyadic3(seed: int, B=1, H=1, N=256, d=64, M0=4, C=4, P=2, T=64,
+                     dtype="bf16", one_key_per_leaf=False, upper_share=0.25) -> Inputs:
+    """Three-level tree whose coordinates are multiples of 1/8 with |x| < 32:
+    the last child of every root and the last leaf of every child are chosen
+    so that each level averages exactly to the one above.  Every coordinate,
+    and every mean, is then exact in bf16 and fp32.  Keys are drawn around
+    uniformly chosen leaves, except that a share `upper_share` of them is
+    drawn around a random root or a random child (half each), so that some
+    keys stay above the leaf level (or, with one_key_per_leaf, N = M0*C*C
+    keys are placed exactly on the leaves in leaf order); queries around a
+    random root; values standard normal."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    L = M0 * C * C
+    leaves64 = np.empty((H, M0, C, C, d))
+    mids64 = np.empty((H, M0, C, d))
+    roots64 = np.empty((H, M0, d))
+    for h in range(H):
+        root = np.clip(np.round(rng.standard_normal((M0, d)) * 8) / 8, -4, 4)
+        off = np.clip(np.round(rng.normal(0, CHILD_SPREAD, (M0, C, d)) * 8) / 8, -1, 1)
+        off[:, C - 1, :] = -off[:, : C - 1, :].sum(axis=1)
+        off2 = np.clip(np.round(rng.normal(0, LEAF_SPREAD, (M0, C, C, d)) * 8) / 8, -1, 1)
+        off2[:, :, C - 1, :] = -off2[:, :, : C - 1, :].sum(axis=2)
+        roots64[h] = root
+        mids64[h] = root[:, None, :] + off
+        leaves64[h] = mids64[h][:, :, None, :] + off2
+    if one_key_per_leaf:
+        N = L
+    st = np.uint16 if dtype == "bf16" else np.float32
+    Q = np.empty((B, H, N, d), dtype=st)
+    K = np.empty_like(Q)
+    V = np.empty_like(Q)
+    true_leaf = np.empty((B, H, N), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            flat = leaves64[h].reshape(L, d)
+            if one_key_per_leaf:
+                leaf = np.arange(L)
+                k64 = flat.copy()
+            else:
+                leaf = rng.integers(0, L, size=N)
+                centre = flat[leaf]
+                kind = rng.random(N)
+                up_root = kind < upper_share / 2
+                up_child = (kind >= upper_share / 2) & (kind < upper_share)
+                centre[up_root] = roots64[h][leaf[up_root] // (C * C)]
+                centre[up_child] = mids64[h].reshape(M0 * C, d)[leaf[up_child] // C]
+                k64 = centre + KEY_SPREAD * rng.standard_normal((N, d))
+            qp = rng.integers(0, M0, size=N)
+            q64 = roots64[h][qp] + QUERY_SPREAD * rng.standard_normal((N, d))
+            v64 = rng.standard_normal((N, d))
+            K[b, h] = to_storage(k64, dtype)
+            Q[b, h] = to_storage(q64, dtype)
+            V[b, h] = to_storage(v64, dtype)
+            true_leaf[b, h] = M0 + M0 * C + leaf
+    return Inputs(name="dyadic3", B=B, H=H, N=N, d=d, M0=M0, C=C, P=P, T=T,
+                  dtype=dtype, scale=1.0 / math.sqrt(d), seed=seed,
+                  children=to_storage(leaves64, dtype), Q=Q, K=K, V=V,
+                  true_leaf=true_leaf, levels=3)
