@@ -18,6 +18,8 @@ import torch
 
 __all__ = [
     "AvqError", "library_path", "load_library", "abi_version",
+    "build_tree3", "assign_aggregate3", "attention3_fwd", "attention3_workspace_size",
+    "assign_aggregate3_workspace_size",
     "build_tree", "assign_aggregate", "attention_fwd", "exact_attention_fwd",
     "assign_aggregate_workspace_size", "attention_workspace_size", "forward",
     "assign_aggregate_noalloc", "NOALLOC_SCRATCH_BYTES", "codebook_diagnostics", "capture",
@@ -84,6 +86,18 @@ def load_library():
     lib.avq_permute_tokens.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.avq_exact_attention_fwd.restype = i32
     lib.avq_exact_attention_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.avq_build_tree3.restype = i32
+    lib.avq_build_tree3.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.avq_assign_aggregate3_workspace_size.restype = sz
+    lib.avq_assign_aggregate3_workspace_size.argtypes = [i32] * 6
+    lib.avq_assign_aggregate3.restype = i32
+    lib.avq_assign_aggregate3.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, u32,
+                                          vp, vp, vp, vp, sz, vp]
+    lib.avq_attention3_workspace_size.restype = sz
+    lib.avq_attention3_workspace_size.argtypes = [i32] * 6
+    lib.avq_attention3_fwd.restype = i32
+    lib.avq_attention3_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                       vp, vp, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -377,6 +391,118 @@ def exact_attention_fwd(Q, K, V, scale: float, out: Optional[torch.Tensor] = Non
         _check(load_library().avq_exact_attention_fwd(_ptr(Q), _ptr(K), _ptr(V), B, H, N, d, float(scale),
                                                       _dt(Q), _ptr(Y), _stream(Q.device)))
     return Y
+
+
+# ---------------------------------------------------------------------------
+# three-level tree (roots -> children -> leaves)
+
+def _tree3_dims(leaves: torch.Tensor):
+    if not isinstance(leaves, torch.Tensor) or leaves.dim() != 5 or leaves.shape[2] != leaves.shape[3]:
+        raise AvqError("leaves must be [H][M0][C][C][d]")
+    H, M0, C, _, d = leaves.shape
+    return H, M0, C, d
+
+
+def build_tree3(leaves: torch.Tensor):
+    """leaves [H][M0][C][C][d] -> (level0 [H][M0][d], level1 [H][M0][C][d],
+    sqnorm [H][M0(1+C+C^2)] fp32, frame [H][d] fp32)."""
+    H, M0, C, d = _tree3_dims(leaves)
+    _need(leaves, "leaves", 5)
+    dev = leaves.device
+    l0 = torch.empty((H, M0, d), dtype=leaves.dtype, device=dev)
+    l1 = torch.empty((H, M0, C, d), dtype=leaves.dtype, device=dev)
+    sq = torch.empty((H, M0 * (1 + C + C * C)), dtype=torch.float32, device=dev)
+    fr = torch.empty((H, d), dtype=torch.float32, device=dev)
+    with _on(dev):
+        _check(load_library().avq_build_tree3(_ptr(leaves), H, M0, C, d, _dt(leaves), _ptr(l0), _ptr(l1),
+                                              _ptr(sq), _ptr(fr), _stream(dev)))
+    return l0, l1, sq, fr
+
+
+def assign_aggregate3_workspace_size(B, H, N, M0, C, d) -> int:
+    return int(load_library().avq_assign_aggregate3_workspace_size(B, H, N, M0, C, d))
+
+
+def assign_aggregate3(K, V, level0, level1, leaves, sqnorm, frame, force_child: bool = False,
+                      want_leaf: bool = False, workspace: Optional[torch.Tensor] = None,
+                      out: Optional[tuple] = None):
+    """Stage 1 on a three-level tree: (vsum [B][H][S3][d] fp32, count
+    [B][H][S3] int32, leaf [B][H][N] int32 or None); `out` = (vsum, count)
+    buffers to write into."""
+    _need(K, "K", 4)
+    dev, dt = K.device, K.dtype
+    _need(V, "V", 4, dt, dev)
+    H, M0, C, d = _tree3_dims(leaves)
+    _need(leaves, "leaves", 5, dt, dev)
+    _need(level0, "level0", 3, dt, dev)
+    _need(level1, "level1", 4, dt, dev)
+    _need(sqnorm, "sqnorm", 2, torch.float32, dev)
+    _need(frame, "frame", 2, torch.float32, dev)
+    B, Hk, N, dk = K.shape
+    S = M0 * (1 + C + C * C)
+    if V.shape != K.shape or Hk != H or dk != d or level0.shape != (H, M0, d) or \
+            level1.shape != (H, M0, C, d) or sqnorm.shape != (H, S) or frame.shape != (H, d):
+        raise AvqError("inconsistent shapes")
+    lib = load_library()
+    workspace = _workspace(workspace, int(lib.avq_assign_aggregate3_workspace_size(B, H, N, M0, C, d)),
+                           dev, "workspace")
+    if out is None:
+        vsum = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
+        count = torch.empty((B, H, S), dtype=torch.int32, device=dev)
+    else:
+        vsum, count = out
+        _need(vsum, "vsum", 4, torch.float32, dev)
+        _need(count, "count", 3, torch.int32, dev)
+        if vsum.shape != (B, H, S, d) or count.shape != (B, H, S):
+            raise AvqError("output buffers do not match the shape")
+    leaf = torch.empty((B, H, N), dtype=torch.int32, device=dev) if want_leaf else None
+    with _on(dev):
+        _check(lib.avq_assign_aggregate3(
+            _ptr(K), _ptr(V), _ptr(level0), _ptr(level1), _ptr(leaves), _ptr(sqnorm), _ptr(frame), B, H, N, d,
+            M0, C, _dt(K), AVQ_FLAG_FORCE_CHILD if force_child else 0, _ptr(vsum), _ptr(count), _ptr(leaf),
+            _ptr(workspace), workspace.numel(), _stream(dev)))
+    return vsum, count, leaf
+
+
+def attention3_workspace_size(B, H, M0, C, d, dtype) -> int:
+    return int(load_library().avq_attention3_workspace_size(B, H, M0, C, d, _DTYPES[dtype]))
+
+
+def attention3_fwd(Q, level0, level1, leaves, vsum, count, P: int, tile: int, scale: float,
+                   want_sel: bool = False, workspace: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None):
+    """Stage 2 on a three-level tree -> (Y, sel0 [B][H][ntiles][P] or None,
+    sel1 [B][H][ntiles][P] or None: selected roots and children, ascending)."""
+    _need(Q, "Q", 4)
+    dev, dt = Q.device, Q.dtype
+    H, M0, C, d = _tree3_dims(leaves)
+    _need(leaves, "leaves", 5, dt, dev)
+    _need(level0, "level0", 3, dt, dev)
+    _need(level1, "level1", 4, dt, dev)
+    _need(vsum, "vsum", 4, torch.float32, dev)
+    _need(count, "count", 3, torch.int32, dev)
+    B, Hq, N, dq = Q.shape
+    S = M0 * (1 + C + C * C)
+    if Hq != H or dq != d or level0.shape != (H, M0, d) or level1.shape != (H, M0, C, d):
+        raise AvqError("inconsistent shapes")
+    if vsum.shape != (B, H, S, d) or count.shape != (B, H, S):
+        raise AvqError("vsum / count do not match the shape")
+    lib = load_library()
+    workspace = _workspace(workspace, int(lib.avq_attention3_workspace_size(B, H, M0, C, d, _dt(Q))),
+                           dev, "workspace")
+    nt = -(-N // tile) if tile > 0 else 0
+    Y = torch.empty_like(Q) if out is None else out
+    _need(Y, "out", 4, dt, dev)
+    if Y.shape != Q.shape:
+        raise AvqError("out must have Q's shape")
+    s0 = torch.empty((B, H, nt, P), dtype=torch.int32, device=dev) if want_sel else None
+    s1 = torch.empty((B, H, nt, P), dtype=torch.int32, device=dev) if want_sel else None
+    with _on(dev):
+        _check(lib.avq_attention3_fwd(
+            _ptr(Q), _ptr(level0), _ptr(level1), _ptr(leaves), _ptr(vsum), _ptr(count), B, H, N, d, M0, C, P,
+            tile, float(scale), _dt(Q), _ptr(Y), _ptr(s0), _ptr(s1), _ptr(workspace), workspace.numel(),
+            _stream(dev)))
+    return Y, s0, s1
 
 
 def forward(Q, K, V, children, P: int, tile: int, scale: float, tree=None, force_child=False):

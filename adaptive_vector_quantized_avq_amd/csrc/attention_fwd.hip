@@ -56,11 +56,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQPW = 32;   // queries per wave
 
 struct AttnLds {
-    size_t ps, vt, np, wp, sel, total;
+    size_t ps, vt, np, wp, sel, wp2, sel2, total;
+    bool wp2_shared;   // level-1 importance partials in the idle half of wp
 };
 
+// level-1 candidates of a three-level tree (the children of the P selected
+// roots), rounded up to whole chunks of 32
+__host__ __device__ inline int attn_cands(int P, int C) { return (P * C + 31) & ~31; }
+
 template <typename T, int D, bool VT_LDS>
-__host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave)
+__host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave, int C = 0, bool three_level = false)
 {
     const int M0p = padded_parents(M0);
     AttnLds L;
@@ -70,6 +75,17 @@ __host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave)
     L.np = o;  o += (size_t)M0p * 4;
     L.wp = o;  o += (size_t)2 * nwave * M0p * 4;
     L.sel = o; o += (size_t)nwave * ((P + 3) & ~3) * 4;
+    L.wp2 = L.wp;
+    L.sel2 = o;
+    L.wp2_shared = true;
+    if (three_level) {
+        o += (size_t)nwave * ((P + 3) & ~3) * 4;
+        L.wp2_shared = attn_cands(P, C) <= M0p;
+        if (!L.wp2_shared) {
+            L.wp2 = o;
+            o += (size_t)nwave * attn_cands(P, C) * 4;
+        }
+    }
     L.total = o;
     return L;
 }
@@ -208,12 +224,16 @@ template <typename T, int D> constexpr int attn_super_chunks()
 // NRB = number of 16-row parent blocks (padded_parents(M0) / 16).
 // sl2 = |scale| * log2(e); neg != 0 flips the sign of Q (scale < 0), so the
 // softmax shift is always a maximum.
-template <typename T, int D, bool VT_LDS, int NRB, int CC, int NWV>
+// L3: three-level tree -- `children` is the middle level and `leaves` the
+// C leaves of every child; after the children's correction the tile's
+// level-1 importance picks P children, whose leaves correct them in turn.
+template <typename T, int D, bool VT_LDS, int NRB, int CC, int NWV, bool L3>
 __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const T *__restrict__ Q, const T *__restrict__ parents, const T *__restrict__ children,
     const unsigned char *__restrict__ pack, int H, int N, int M0, int P, int ltile, float sl2,
     int neg, int ntiles, int nsteps, int per_bh, int nbh, T *__restrict__ Y,
-    int32_t *__restrict__ sel_out, float *__restrict__ imp_out)
+    int32_t *__restrict__ sel_out, float *__restrict__ imp_out, const T *__restrict__ leaves,
+    int32_t *__restrict__ sel1_out)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int KS = D / 32;
@@ -225,7 +245,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     constexpr int LC = CC == 2 ? 1 : CC == 4 ? 2 : CC == 8 ? 3 : 4;
     constexpr int SCH = attn_super_chunks<T, D>();
     const int selStride = (P + 3) & ~3;
-    const AttnLds L = attn_lds<T, D, VT_LDS>(M0, P, NWV);
+    const AttnLds L = attn_lds<T, D, VT_LDS>(M0, P, NWV, CC, L3);
     T *Ps = reinterpret_cast<T *>(smem + L.ps);
     T *Vt = reinterpret_cast<T *>(smem + L.vt);
     float *nP = reinterpret_cast<float *>(smem + L.np);
@@ -241,7 +261,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, i16 = lane & 15;
-    const PackLayout PL = pack_layout(M0, CC, D, (int)sizeof(T));
+    const PackLayout PL = pack_layout(M0, CC, D, (int)sizeof(T), L3);
     const unsigned char *pk = pack + (size_t)bh * PL.bytes;
     const T *pvt = reinterpret_cast<const T *>(pk + PL.pvt);
     const float *pnp = reinterpret_cast<const float *>(pk + PL.pn);
@@ -250,6 +270,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const T *Qh = Q + (size_t)bh * N * D;
     T *Yh = Y + (size_t)bh * N * D;
     const T *Ch = children + (size_t)h * M0 * CC * D;
+    const T *Lh = L3 ? leaves + (size_t)h * M0 * CC * CC * D : nullptr;
+    const T *gvt = reinterpret_cast<const T *>(pk + PL.gvt);
+    const float *gnp = reinterpret_cast<const float *>(pk + PL.gn);
 
     // ---- stage the head's parents, parent value sums and counts once.
     // Padding rows (M0 <= j < M0p) repeat parent 0: their logit is one of the
@@ -269,7 +292,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const int wpt = (1 << ltile) / kQPW;         // waves per tile
     const int tw0 = (w / wpt) * wpt;             // first wave of this wave's tile
     int *mysel = selS + (w / wpt) * selStride;   // the tile's selection
+    int *mysel2 = reinterpret_cast<int *>(smem + L.sel2) + (w / wpt) * selStride;   // its children's (L3)
     const int PC = P * CC;
+    const int PCr = attn_cands(P, CC);
 
     int buf = 0;
     for (int st = slice; st < nsteps; st += per_bh, buf ^= 1) {
@@ -460,8 +485,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
         // A position ph >= P*C (padding of the last chunks) takes the
         // codeword of child 0 of the first selected parent, whose logit is
         // already among the real ones (so the shift is unchanged), and the
-        // all-zero count and value-sum entry M0 (so it adds nothing); every
-        // chunk is therefore processed the same way, without guards.
+        // all-zero count and value-sum entry of the level (so it adds
+        // nothing); every chunk is therefore processed the same way, without
+        // guards.  A level is described by the selected parents' indices,
+        // the children's codewords, and their value sums and counts in the
+        // pack; a three-level tree runs it once more one level down.
         // (at d = 128 the query fragments are read again here rather than
         // held through the weights, value sums and selection, which keeps
         // the parent pass out of scratch)
@@ -474,21 +502,28 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
         const float sl2c = sl2 * (1.0f / (float)CC);   // mean over CC children, scaled
         constexpr int SC = 32 * SCH;                    // children per super-chunk
 
+        struct Level {
+            const int *sel;     // selected parents of the level (LDS)
+            const T *cw;        // children's codewords, parent-major
+            const T *vt;        // children's value sums [np + 1][D][CC]
+            const float *cn;    // children's counts [np + 1][CC]
+            int zero;           // the all-zero entry (np)
+        };
         // codeword fragments of the super-chunk starting at c0: output row
         // 4g+r of tile A is child 8g+r of a chunk, of tile B child 8g+4+r
         struct CwBuf {
             Frag<T> a[SCH][KS], b[SCH][KS];
         };
-        auto load_cw = [&](int c0, CwBuf &cw) {
+        auto load_cw = [&](const Level &lv, int c0, CwBuf &cw) {
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
                 const int phA = c0 + 32 * q + 8 * (i16 >> 2) + (i16 & 3), phB = phA + 4;
                 // (indices clamped so that the LDS reads are unconditional)
-                const int sa = mysel[phA < PC ? phA >> LC : 0], sb = mysel[phB < PC ? phB >> LC : 0];
+                const int sa = lv.sel[phA < PC ? phA >> LC : 0], sb = lv.sel[phB < PC ? phB >> LC : 0];
                 const int ia = sa * CC + (phA < PC ? (phA & (CC - 1)) : 0);
                 const int ib = sb * CC + (phB < PC ? (phB & (CC - 1)) : 0);
-                const T *ra = Ch + (size_t)ia * D + 8 * g;
-                const T *rb_ = Ch + (size_t)ib * D + 8 * g;
+                const T *ra = lv.cw + (size_t)ia * D + 8 * g;
+                const T *rb_ = lv.cw + (size_t)ib * D + 8 * g;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     cw.a[q][ks] = load_frag(ra + 32 * ks);
@@ -496,61 +531,67 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                 }
             }
         };
+        // child logits of a super-chunk (rows as in load_cw)
+        auto child_logits = [&](const CwBuf &cw, int q, f32x4 &a0, f32x4 &b0, f32x4 &a1, f32x4 &b1) {
+            a0 = f32x4{0.f, 0.f, 0.f, 0.f};
+            b0 = a0; a1 = a0; b1 = a0;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                a0 = mma(cw.a[q][ks], qa[ks], a0);
+                b0 = mma(cw.b[q][ks], qa[ks], b0);
+                a1 = mma(cw.a[q][ks], qb[ks], a1);
+                b1 = mma(cw.b[q][ks], qb[ks], b1);
+            }
+        };
         // one super-chunk: its counts and value sums are loaded first (they
         // are needed last), the next super-chunk's codewords are loaded into
         // `nxt` while this one computes
-        auto super_chunk = [&](int c0, const CwBuf &cw, CwBuf &nxt, bool more) {
+        auto super_chunk = [&](const Level &lv, int c0, const CwBuf &cw, CwBuf &nxt, bool more) {
             f32x4 nA[SCH], nB[SCH];
             Frag<T> vc[SCH][DB];
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
                 const int ph0 = c0 + 32 * q + 8 * g;
                 if constexpr (CC >= 8) {   // the 8 children share one parent
-                    const int ps = mysel[ph0 < PC ? ph0 >> LC : 0];
-                    const int pp = ph0 < PC ? ps : M0;
-                    const float *cp = cnp + pp * CC + (ph0 & (CC - 1));
+                    const int ps = lv.sel[ph0 < PC ? ph0 >> LC : 0];
+                    const int pp = ph0 < PC ? ps : lv.zero;
+                    const float *cp = lv.cn + (size_t)pp * CC + (ph0 & (CC - 1));
                     nA[q] = *reinterpret_cast<const f32x4 *>(cp);
                     nB[q] = *reinterpret_cast<const f32x4 *>(cp + 4);
-                    const T *vp = cvt + ((size_t)pp * D + i16) * CC + (ph0 & (CC - 1));
+                    const T *vp = lv.vt + ((size_t)pp * D + i16) * CC + (ph0 & (CC - 1));
 #pragma unroll
                     for (int db = 0; db < DB; ++db) vc[q][db] = load_frag(vp + (size_t)16 * db * CC);
                 } else {
-                    int pk8[8];   // slot (parent index, or the zero entry M0) of children ph0..ph0+7
+                    int pk8[8];   // slot (parent index, or the zero entry) of children ph0..ph0+7
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
                         const int ph = ph0 + k;
-                        const int ps = mysel[ph < PC ? ph >> LC : 0];
-                        pk8[k] = ph < PC ? ps : M0;
+                        const int ps = lv.sel[ph < PC ? ph >> LC : 0];
+                        pk8[k] = ph < PC ? ps : lv.zero;
                     }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        nA[q][r] = cnp[pk8[r] * CC + ((ph0 + r) & (CC - 1))];
-                        nB[q][r] = cnp[pk8[4 + r] * CC + ((ph0 + 4 + r) & (CC - 1))];
+                        nA[q][r] = lv.cn[(size_t)pk8[r] * CC + ((ph0 + r) & (CC - 1))];
+                        nB[q][r] = lv.cn[(size_t)pk8[4 + r] * CC + ((ph0 + 4 + r) & (CC - 1))];
                     }
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
                         float v[8];
 #pragma unroll
                         for (int k = 0; k < 8; ++k)
-                            v[k] = to_float(cvt[((size_t)pk8[k] * D + 16 * db + i16) * CC + ((ph0 + k) & (CC - 1))]);
+                            v[k] = to_float(lv.vt[((size_t)pk8[k] * D + 16 * db + i16) * CC + ((ph0 + k) & (CC - 1))]);
                         vc[q][db] = frag_from8<T>(v);
                     }
                 }
             }
-            if (more) load_cw(c0 + SC, nxt);
+            if (more) load_cw(lv, c0 + SC, nxt);
             // child logits and their maximum
             f32x4 SA0[SCH], SB0[SCH], SA1[SCH], SB1[SCH];
             float c0m = -INFINITY, c1m = -INFINITY;
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
-                f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, b0 = a0, a1 = a0, b1 = a0;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    a0 = mma(cw.a[q][ks], qa[ks], a0);
-                    b0 = mma(cw.b[q][ks], qa[ks], b0);
-                    a1 = mma(cw.a[q][ks], qb[ks], a1);
-                    b1 = mma(cw.b[q][ks], qb[ks], b1);
-                }
+                f32x4 a0, b0, a1, b1;
+                child_logits(cw, q, a0, b0, a1, b1);
                 SA0[q] = a0; SB0[q] = b0; SA1[q] = a1; SB1[q] = b1;
                 c0m = max3f(c0m, max3f(a0[0], a0[1], a0[2]), max3f(a0[3], b0[0], b0[1]));
                 c0m = max3f(c0m, b0[2], b0[3]);
@@ -622,14 +663,73 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                 }
             }
         };
-        if (PC > 0) {
-            CwBuf cwA, cwB;
-            load_cw(0, cwA);
-            for (int c0 = 0; c0 < PC; c0 += 2 * SC) {
-                super_chunk(c0, cwA, cwB, c0 + SC < PC);
-                if (c0 + SC >= PC) break;
-                super_chunk(c0 + SC, cwB, cwA, c0 + 2 * SC < PC);
+        auto correct_level = [&](const Level &lv) {
+            if (PC > 0) {
+                CwBuf cwA, cwB;
+                load_cw(lv, 0, cwA);
+                for (int c0 = 0; c0 < PC; c0 += 2 * SC) {
+                    super_chunk(lv, c0, cwA, cwB, c0 + SC < PC);
+                    if (c0 + SC >= PC) break;
+                    super_chunk(lv, c0 + SC, cwB, cwA, c0 + 2 * SC < PC);
+                }
             }
+        };
+        correct_level(Level{mysel, Ch, cvt, cnp, M0});
+
+        if constexpr (L3) {
+            // ---- level 1 of a three-level tree: importance of the P*C
+            // children just added, w_c = n_c sum_i exp(S_ic - m_i) / Z_i with
+            // Z after their correction (the logits are formed again: a
+            // second pass over the same codewords, from L2), top-P children,
+            // then the same correction one level down
+            const float Z10 = Zf0 + xgroup_sum(dz0), Z11 = Zf1 + xgroup_sum(dz1);
+            const float u0 = v0 ? __builtin_amdgcn_rcpf(Z10) : 0.f, u1 = v1 ? __builtin_amdgcn_rcpf(Z11) : 0.f;
+            float *W2 = L.wp2_shared ? Wp + (buf ^ 1) * NWV * M0p : reinterpret_cast<float *>(smem + L.wp2);
+            const Level lv1{mysel, Ch, cvt, cnp, M0};
+            for (int c0 = 0; c0 < PC; c0 += 32) {
+                CwBuf cw;
+                load_cw(lv1, c0, cw);
+                f32x4 a0, b0, a1, b1;
+                child_logits(cw, 0, a0, b0, a1, b1);
+                f32x4 t[2];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    t[0][r] = __builtin_amdgcn_exp2f(fmaf(a0[r], sl2, -m0)) * u0 +
+                              __builtin_amdgcn_exp2f(fmaf(a1[r], sl2, -m1)) * u1;
+                    t[1][r] = __builtin_amdgcn_exp2f(fmaf(b0[r], sl2, -m0)) * u0 +
+                              __builtin_amdgcn_exp2f(fmaf(b1[r], sl2, -m1)) * u1;
+                }
+                // summed over the 16 queries of each row: children
+                // c0 + 8g + 4 (i16 >> 3) + r
+                const f32x4 part = row16_reduce_scatter<2>(t, i16);
+                if ((i16 & 7) == 0) *reinterpret_cast<f32x4 *>(W2 + w * PCr + c0 + 8 * g + 4 * (i16 >> 3)) = part;
+            }
+            __syncthreads();   // every wave's level-1 partials are in W2
+            if (w == tw0) {
+                float wv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = lane + 64 * i, jc = j < PC ? j : 0;
+                    float a = 0.f;
+#pragma unroll
+                    for (int ww = 0; ww < NWV; ++ww) {
+                        const float x = W2[((tw0 + ww) & (NWV - 1)) * PCr + jc];
+                        a += ww < wpt ? x : 0.f;
+                    }
+                    const float nc = cnp[(size_t)mysel[jc >> LC] * CC + (jc & (CC - 1))];
+                    wv[i] = j < PC ? a * nc : 0.f;
+                }
+                // positions among the candidates (ascending), then child ids
+                select_top_p_regs(wv, PC, P, mysel2, nullptr);
+                for (int k = lane; k < P; k += 64) {
+                    const int pos = mysel2[k];
+                    const int child = mysel[pos >> LC] * CC + (pos & (CC - 1));
+                    mysel2[k] = child;
+                    if (sel1_out && tg < ntiles) sel1_out[((size_t)bh * ntiles + tg) * P + k] = child;
+                }
+            }
+            __syncthreads();   // the children's selection is in LDS
+            correct_level(Level{mysel2, Lh, gvt, gnp, M0 * CC});
         }
         }   // CC > 0
 
@@ -647,17 +747,16 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
 // its CU alone)
 template <int D, bool VT> static int attn_waves(int tile) { return tile >= 256 || (VT && D == 128) ? 8 : 4; }
 
-int attention_child_chunk(int d, int M0, int C, int P, int tile, int dtype)
+int attention_child_chunk(int d, int M0, int C, int P, int tile, int dtype, bool three_level)
 {
-    (void)C;
     if (tile != 32 && tile != 64 && tile != 128 && tile != 256) return 0;
     size_t lds;
     if (dtype == 1)
-        lds = d == 64 ? attn_lds<bf16, 64, true>(M0, P, attn_waves<64, true>(tile)).total
-                      : attn_lds<bf16, 128, true>(M0, P, attn_waves<128, true>(tile)).total;
+        lds = d == 64 ? attn_lds<bf16, 64, true>(M0, P, attn_waves<64, true>(tile), C, three_level).total
+                      : attn_lds<bf16, 128, true>(M0, P, attn_waves<128, true>(tile), C, three_level).total;
     else
-        lds = d == 64 ? attn_lds<float, 64, true>(M0, P, attn_waves<64, true>(tile)).total
-                      : attn_lds<float, 128, false>(M0, P, attn_waves<128, false>(tile)).total;
+        lds = d == 64 ? attn_lds<float, 64, true>(M0, P, attn_waves<64, true>(tile), C, three_level).total
+                      : attn_lds<float, 128, false>(M0, P, attn_waves<128, false>(tile), C, three_level).total;
     return lds <= 160 * 1024 ? 32 : 0;
 }
 
@@ -682,16 +781,23 @@ static int device_cus()
     return cus[dev];
 }
 
-template <typename T, int D, bool VT, int NRB, int CC, int NWV>
-static hipError_t launch_attn_k(const void *Q, const void *parents, const void *children,
-                                const void *pack, int B, int H, int N, int M0, int P, int tile,
-                                float scale, void *Y, int32_t *sel, float *imp, hipStream_t stream)
+struct AttnArgs {
+    const void *Q, *parents, *children, *pack, *leaves;
+    int B, H, N, M0, C, P, tile;
+    float scale;
+    void *Y;
+    int32_t *sel, *sel1;
+    float *imp;
+};
+
+template <typename T, int D, bool VT, int NRB, int CC, int NWV, bool L3>
+static hipError_t launch_attn_k(const AttnArgs &a, hipStream_t stream)
 {
-    allow_full_lds<attention_kernel<T, D, VT, NRB, CC, NWV>>();
-    const size_t lds = attn_lds<T, D, VT>(M0, P, NWV).total;
-    const int ntiles = (N + tile - 1) / tile;
-    const int nsteps = (N + NWV * kQPW - 1) / (NWV * kQPW);
-    const int BH = B * H;
+    allow_full_lds<attention_kernel<T, D, VT, NRB, CC, NWV, L3>>();
+    const size_t lds = attn_lds<T, D, VT>(a.M0, a.P, NWV, CC, L3).total;
+    const int ntiles = (a.N + a.tile - 1) / a.tile;
+    const int nsteps = (a.N + NWV * kQPW - 1) / (NWV * kQPW);
+    const int BH = a.B * a.H;
     // two work-groups per CU when LDS and registers allow (an 8-wave
     // work-group takes both of a SIMD's two wave slots), each a slice of one
     // head's steps; rounded down, so that every work-group is resident from
@@ -700,67 +806,62 @@ static hipError_t launch_attn_k(const void *Q, const void *parents, const void *
     const int per_cu = NWV == 4 && lds * 2 <= 160 * 1024 ? 2 : 1;
     const int per_bh = max(1, min(nsteps, per_cu * device_cus() / BH));
     const int grid = (BH * per_bh + 7) & ~7;
-    hipLaunchKernelGGL((attention_kernel<T, D, VT, NRB, CC, NWV>), dim3(grid), dim3(64 * NWV), lds, stream,
-                       (const T *)Q, (const T *)parents, (const T *)children, (const unsigned char *)pack,
-                       H, N, M0, P, ilog2(tile), fabsf(scale) * kLog2e, scale < 0.f ? 1 : 0, ntiles,
-                       nsteps, per_bh, BH, (T *)Y, sel, imp);
+    hipLaunchKernelGGL((attention_kernel<T, D, VT, NRB, CC, NWV, L3>), dim3(grid), dim3(64 * NWV), lds, stream,
+                       (const T *)a.Q, (const T *)a.parents, (const T *)a.children, (const unsigned char *)a.pack,
+                       a.H, a.N, a.M0, a.P, ilog2(a.tile), fabsf(a.scale) * kLog2e, a.scale < 0.f ? 1 : 0, ntiles,
+                       nsteps, per_bh, BH, (T *)a.Y, a.sel, a.imp, (const T *)a.leaves, a.sel1);
     return hipGetLastError();
 }
 
-template <typename T, int D, bool VT, int NRB, int CC>
-static hipError_t launch_attn_w(const void *Q, const void *parents, const void *children,
-                                const void *pack, int B, int H, int N, int M0, int P, int tile,
-                                float scale, void *Y, int32_t *sel, float *imp, hipStream_t stream)
+template <typename T, int D, bool VT, int NRB, int CC, bool L3>
+static hipError_t launch_attn_w(const AttnArgs &a, hipStream_t stream)
 {
-    if (attn_waves<D, VT>(tile) == 8)
-        return launch_attn_k<T, D, VT, NRB, CC, 8>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
-    if constexpr (!(VT && D == 128))
-        return launch_attn_k<T, D, VT, NRB, CC, 4>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
+    if (attn_waves<D, VT>(a.tile) == 8) return launch_attn_k<T, D, VT, NRB, CC, 8, L3>(a, stream);
+    if constexpr (!(VT && D == 128)) return launch_attn_k<T, D, VT, NRB, CC, 4, L3>(a, stream);
     return hipErrorInvalidConfiguration;
 }
 
 template <typename T, int D, bool VT, int NRB>
-static hipError_t launch_attn_nrb(const void *Q, const void *parents, const void *children,
-                                  const void *pack, int B, int H, int N, int M0, int C, int P,
-                                  int tile, float scale, void *Y, int32_t *sel, float *imp,
-                                  hipStream_t stream)
+static hipError_t launch_attn_nrb(const AttnArgs &a, hipStream_t stream)
 {
-    switch (C) {
-    case 0: return launch_attn_w<T, D, VT, NRB, 0>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
-    case 2: return launch_attn_w<T, D, VT, NRB, 2>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
-    case 4: return launch_attn_w<T, D, VT, NRB, 4>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
-    case 8: return launch_attn_w<T, D, VT, NRB, 8>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
-    default: return launch_attn_w<T, D, VT, NRB, 16>(Q, parents, children, pack, B, H, N, M0, P, tile, scale, Y, sel, imp, stream);
+    if (a.leaves) {
+        switch (a.C) {
+        case 2: return launch_attn_w<T, D, VT, NRB, 2, true>(a, stream);
+        case 4: return launch_attn_w<T, D, VT, NRB, 4, true>(a, stream);
+        case 8: return launch_attn_w<T, D, VT, NRB, 8, true>(a, stream);
+        default: return launch_attn_w<T, D, VT, NRB, 16, true>(a, stream);
+        }
+    }
+    switch (a.C) {
+    case 0: return launch_attn_w<T, D, VT, NRB, 0, false>(a, stream);
+    case 2: return launch_attn_w<T, D, VT, NRB, 2, false>(a, stream);
+    case 4: return launch_attn_w<T, D, VT, NRB, 4, false>(a, stream);
+    case 8: return launch_attn_w<T, D, VT, NRB, 8, false>(a, stream);
+    default: return launch_attn_w<T, D, VT, NRB, 16, false>(a, stream);
     }
 }
 
 template <typename T, int D, bool VT>
-static hipError_t launch_attn_t(const void *Q, const void *parents, const void *children,
-                                const void *pack, int B, int H, int N, int M0, int C, int P, int tile,
-                                float scale, void *Y, int32_t *sel, float *imp, hipStream_t stream)
+static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t stream)
 {
-    if (attn_lds<T, D, VT>(M0, P, attn_waves<D, VT>(tile)).total > 160 * 1024) return hipErrorInvalidConfiguration;
-    switch (padded_parents(M0)) {
-    case 32: return launch_attn_nrb<T, D, VT, 2>(Q, parents, children, pack, B, H, N, M0, C, P, tile, scale, Y, sel, imp, stream);
-    case 64: return launch_attn_nrb<T, D, VT, 4>(Q, parents, children, pack, B, H, N, M0, C, P, tile, scale, Y, sel, imp, stream);
-    case 128: return launch_attn_nrb<T, D, VT, 8>(Q, parents, children, pack, B, H, N, M0, C, P, tile, scale, Y, sel, imp, stream);
-    default: return launch_attn_nrb<T, D, VT, 16>(Q, parents, children, pack, B, H, N, M0, C, P, tile, scale, Y, sel, imp, stream);
+    if (attn_lds<T, D, VT>(a.M0, a.P, attn_waves<D, VT>(a.tile), a.C, a.leaves != nullptr).total > 160 * 1024)
+        return hipErrorInvalidConfiguration;
+    switch (padded_parents(a.M0)) {
+    case 32: return launch_attn_nrb<T, D, VT, 2>(a, stream);
+    case 64: return launch_attn_nrb<T, D, VT, 4>(a, stream);
+    case 128: return launch_attn_nrb<T, D, VT, 8>(a, stream);
+    default: return launch_attn_nrb<T, D, VT, 16>(a, stream);
     }
 }
 
 hipError_t launch_attention_fwd(const void *Q, const void *parents, const void *children,
                                 const void *pack, int B, int H, int N, int d, int M0, int C, int P,
                                 int tile, float scale, int dtype, void *Y, int32_t *sel,
-                                float *importance, hipStream_t stream)
+                                float *importance, hipStream_t stream, const void *leaves, int32_t *sel1)
 {
-    if (dtype == 1) {
-        if (d == 64)
-            return launch_attn_t<bf16, 64, true>(Q, parents, children, pack, B, H, N, M0, C, P, tile, scale, Y, sel, importance, stream);
-        return launch_attn_t<bf16, 128, true>(Q, parents, children, pack, B, H, N, M0, C, P, tile, scale, Y, sel, importance, stream);
-    }
-    if (d == 64)
-        return launch_attn_t<float, 64, true>(Q, parents, children, pack, B, H, N, M0, C, P, tile, scale, Y, sel, importance, stream);
-    return launch_attn_t<float, 128, false>(Q, parents, children, pack, B, H, N, M0, C, P, tile, scale, Y, sel, importance, stream);
+    const AttnArgs a{Q, parents, children, pack, leaves, B, H, N, M0, C, P, tile, scale, Y, sel, sel1, importance};
+    if (dtype == 1) return d == 64 ? launch_attn_t<bf16, 64, true>(a, stream) : launch_attn_t<bf16, 128, true>(a, stream);
+    return d == 64 ? launch_attn_t<float, 64, true>(a, stream) : launch_attn_t<float, 128, false>(a, stream);
 }
 
 }  // namespace avq

@@ -46,6 +46,15 @@ int check_tree(int H, int M0, int C, int d, int dtype)
     return AVQ_OK;
 }
 
+// a three-level tree (roots -> children -> leaves) needs children
+int check_tree3(int H, int M0, int C, int d, int dtype)
+{
+    int st = check_tree(H, M0, C, d, dtype);
+    if (st != AVQ_OK) return st;
+    AVQ_REQUIRE(C > 0, AVQ_ERR_INVALID_ARG, "a three-level tree needs C > 0");
+    return AVQ_OK;
+}
+
 int check_seq(int B, int N)
 {
     AVQ_REQUIRE(B >= 1, AVQ_ERR_INVALID_ARG, "B must be >= 1");
@@ -231,6 +240,80 @@ int avq_attention_fwd(const void *Q, const void *parents, const void *children, 
     return hip_status(avq::launch_attention_fwd(Q, parents, children, workspace, B, H, N, d, M0, C, P, tile,
                                                 scale, dtype, Y_out, sel_out, importance_out,
                                                 (hipStream_t)stream));
+}
+
+int avq_build_tree3(const void *leaves, int H, int M0, int C, int d, int dtype, void *level0_out, void *level1_out,
+                    float *sqnorm_out, float *frame_out, void *stream)
+{
+    AVQ_REQUIRE(leaves && level0_out && level1_out && sqnorm_out && frame_out, AVQ_ERR_INVALID_ARG,
+                "null pointer argument");
+    int st = check_tree3(H, M0, C, d, dtype);
+    if (st != AVQ_OK) return st;
+    return hip_status(avq::launch_build_tree3(leaves, H, M0, C, d, dtype, level0_out, level1_out, sqnorm_out,
+                                              frame_out, (hipStream_t)stream));
+}
+
+size_t avq_assign_aggregate3_workspace_size(int B, int H, int N, int M0, int C, int d)
+{
+    if (check_tree3(H, M0, C, d, AVQ_BF16) != AVQ_OK || check_seq(B, N) != AVQ_OK) return 0;
+    return avq::assign3_workspace_bytes(B, H, N, M0, C, d);
+}
+
+int avq_assign_aggregate3(const void *K, const void *V, const void *level0, const void *level1, const void *leaves,
+                          const float *sqnorm, const float *frame, int B, int H, int N, int d, int M0, int C,
+                          int dtype, unsigned flags, float *vsum_out, int32_t *count_out, int32_t *leaf_out,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    AVQ_REQUIRE(K && V && level0 && level1 && leaves && sqnorm && frame && vsum_out && count_out && workspace,
+                AVQ_ERR_INVALID_ARG, "null pointer argument");
+    int st = check_tree3(H, M0, C, d, dtype);
+    if (st != AVQ_OK) return st;
+    st = check_seq(B, N);
+    if (st != AVQ_OK) return st;
+    AVQ_REQUIRE((flags & ~(unsigned)AVQ_FLAG_FORCE_CHILD) == 0, AVQ_ERR_INVALID_ARG,
+                "only AVQ_FLAG_FORCE_CHILD applies to a three-level tree");
+    AVQ_REQUIRE(workspace_bytes >= avq::assign3_workspace_bytes(B, H, N, M0, C, d), AVQ_ERR_INVALID_ARG,
+                "workspace too small");
+    AVQ_REQUIRE(((uintptr_t)workspace & 255u) == 0, AVQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    return hip_status(avq::launch_assign_aggregate3(K, V, level0, level1, leaves, sqnorm, frame, B, H, N, d, M0, C,
+                                                    dtype, flags, vsum_out, count_out, leaf_out, workspace,
+                                                    (hipStream_t)stream));
+}
+
+size_t avq_attention3_workspace_size(int B, int H, int M0, int C, int d, int dtype)
+{
+    if (check_tree3(H, M0, C, d, dtype) != AVQ_OK || B < 1) return 0;
+    return (size_t)B * H * avq::pack_layout(M0, C, d, dtype == AVQ_BF16 ? 2 : 4, true).bytes;
+}
+
+int avq_attention3_fwd(const void *Q, const void *level0, const void *level1, const void *leaves, const float *vsum,
+                       const int32_t *count, int B, int H, int N, int d, int M0, int C, int P, int tile, float scale,
+                       int dtype, void *Y_out, int32_t *sel0_out, int32_t *sel1_out, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    AVQ_REQUIRE(Q && level0 && level1 && leaves && vsum && count && Y_out && workspace, AVQ_ERR_INVALID_ARG,
+                "null pointer argument");
+    int st = check_tree3(H, M0, C, d, dtype);
+    if (st != AVQ_OK) return st;
+    st = check_seq(B, N);
+    if (st != AVQ_OK) return st;
+    AVQ_REQUIRE(P >= 0 && P <= M0, AVQ_ERR_INVALID_ARG, "P must satisfy 0 <= P <= M0");
+    AVQ_REQUIRE(tile >= 1, AVQ_ERR_INVALID_ARG, "tile must be >= 1");
+    AVQ_REQUIRE(isfinite(scale), AVQ_ERR_INVALID_ARG, "scale must be finite");
+    AVQ_REQUIRE(tile == 32 || tile == 64 || tile == 128 || tile == 256, AVQ_ERR_UNSUPPORTED,
+                "tile must be 32, 64, 128 or 256");
+    AVQ_REQUIRE(P * C <= 256, AVQ_ERR_UNSUPPORTED, "P * C must be <= 256 (the level-1 candidates of a tile)");
+    AVQ_REQUIRE(avq::attention_child_chunk(d, M0, C, P, tile, dtype, true) > 0, AVQ_ERR_UNSUPPORTED,
+                "codebook does not fit in LDS for this dtype/d/M0/P");
+    const size_t need = (size_t)B * H * avq::pack_layout(M0, C, d, dtype == AVQ_BF16 ? 2 : 4, true).bytes;
+    AVQ_REQUIRE(workspace_bytes >= need, AVQ_ERR_INVALID_ARG, "workspace too small");
+    AVQ_REQUIRE(((uintptr_t)workspace & 255u) == 0, AVQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    hipError_t e = avq::launch_pack_aggregates(vsum, count, B, H, d, M0, C, dtype, workspace, (hipStream_t)stream,
+                                               true);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(avq::launch_attention_fwd(Q, level0, level1, workspace, B, H, N, d, M0, C, P, tile, scale,
+                                                dtype, Y_out, sel0_out, nullptr, (hipStream_t)stream, leaves,
+                                                sel1_out));
 }
 
 size_t avq_diagnostics_workspace_size(int B, int H, int N)

@@ -57,9 +57,12 @@ struct AssignWorkspace {
 //                        all zero (read for the padding children of a
 //                        partly filled chunk)
 //   cn  [M0+1][C] float  child counts; entry M0 is all zero
+// and, for a three-level tree, the same two sections one level down (the
+// M0*C children as parents of their C leaves):
+//   gvt [M0*C+1][D][C] T, gn [M0*C+1][C] float (entry M0*C all zero)
 // with M0p = padded_parents(M0).
 struct PackLayout {
-    size_t pvt, pn, cvt, cn, bytes;
+    size_t pvt, pn, cvt, cn, gvt, gn, bytes;
 };
 // parents padded to a power of two >= 32, so that the stage-2 kernel can be
 // specialised on the number of 16-row MFMA blocks
@@ -68,7 +71,7 @@ __host__ __device__ inline int padded_parents(int M0)
     return M0 <= 32 ? 32 : M0 <= 64 ? 64 : M0 <= 128 ? 128 : 256;
 }
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-__host__ __device__ inline PackLayout pack_layout(int M0, int C, int D, int esize)
+__host__ __device__ inline PackLayout pack_layout(int M0, int C, int D, int esize, bool three_level = false)
 {
     const int M0p = padded_parents(M0);
     PackLayout L;
@@ -77,6 +80,12 @@ __host__ __device__ inline PackLayout pack_layout(int M0, int C, int D, int esiz
     L.pn = o;  o = align256(o + (size_t)M0p * 4);
     L.cvt = o; o = align256(o + (size_t)(M0 + 1) * D * C * esize);
     L.cn = o;  o = align256(o + (size_t)(M0 + 1) * C * 4);
+    L.gvt = o; L.gn = o;
+    if (three_level) {
+        const size_t n1 = (size_t)M0 * C;
+        L.gvt = o; o = align256(o + (n1 + 1) * D * C * esize);
+        L.gn = o;  o = align256(o + (n1 + 1) * C * 4);
+    }
     L.bytes = o;
     return L;
 }
@@ -109,19 +118,41 @@ hipError_t launch_assign_aggregate(const void *K, const void *V, const void *par
                                    int32_t *count, int32_t *leaf, const AssignWorkspace &ws,
                                    hipStream_t stream);
 
+// second stage-1 kernel alone on caller-built lists: slot_stride = slots
+// (and norms) per head, leaf_base added to every leaf id written
+hipError_t launch_refine_slots(const void *K, const void *V, const void *parents, const void *children,
+                               const float *sqnorm, const float *frame, int B, int H, int N, int d, int M0,
+                               int C, int dtype, unsigned flags, float *vsum, int32_t *count, int32_t *leaf,
+                               const AssignWorkspace &ws, int slot_stride, int leaf_base, hipStream_t stream);
+
+// three-level tree (roots -> children -> leaves): the two upper levels from
+// the leaves, frame and norms over all three (slot order)
+hipError_t launch_build_tree3(const void *leaves, int H, int M0, int C, int d, int dtype, void *level0,
+                              void *level1, float *sqnorm, float *frame, hipStream_t stream);
+size_t assign3_workspace_bytes(int B, int H, int N, int M0, int C, int D);
+// stage 1 of a three-level tree; leaf may be null (the workspace then holds
+// the leaf ids the second descent needs)
+hipError_t launch_assign_aggregate3(const void *K, const void *V, const void *level0, const void *level1,
+                                    const void *leaves, const float *sqnorm, const float *frame, int B, int H,
+                                    int N, int d, int M0, int C, int dtype, unsigned flags, float *vsum,
+                                    int32_t *count, int32_t *leaf, void *workspace, hipStream_t stream);
+
 // stage-2 operand pack (PackLayout, B*H blocks) from fp32 sums and int32 counts
+// (three_level: slots in the three-level layout, grandchild sections filled)
 hipError_t launch_pack_aggregates(const float *vsum, const int32_t *count, int B, int H, int d, int M0, int C,
-                                  int dtype, void *pack, hipStream_t stream);
+                                  int dtype, void *pack, hipStream_t stream, bool three_level = false);
 
 // returns hipErrorInvalidConfiguration when the shape does not fit the
-// kernel's on-chip budget
+// kernel's on-chip budget.  leaves != nullptr: three-level tree (children
+// are the middle level), sel1 receives the selected children
 hipError_t launch_attention_fwd(const void *Q, const void *parents, const void *children,
                                 const void *pack, int B, int H, int N, int d, int M0, int C, int P,
                                 int tile, float scale, int dtype, void *Y, int32_t *sel,
-                                float *importance, hipStream_t stream);
+                                float *importance, hipStream_t stream, const void *leaves = nullptr,
+                                int32_t *sel1 = nullptr);
 // rows of children staged per tile and per step by the attention kernel, or
 // 0 if the shape does not fit its LDS budget
-int attention_child_chunk(int d, int M0, int C, int P, int tile, int dtype);
+int attention_child_chunk(int d, int M0, int C, int P, int tile, int dtype, bool three_level = false);
 
 // codebook diagnostics: commitment loss (needs K, the tree and leaf ids) and
 // active ratio (needs counts); workspace of diagnostics_workspace_bytes

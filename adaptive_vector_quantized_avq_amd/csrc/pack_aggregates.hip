@@ -15,7 +15,9 @@
 //   cvt  item (p, t, group of 8 children): the children's sums of dimension
 //        t, children innermost; entry M0 is all zero;
 //   pn   parent counts as fp32 (zero past M0);
-//   cn   child counts as fp32; entry M0 is all zero.
+//   cn   child counts as fp32; entry M0 is all zero;
+//   and for a three-level tree the same two sections for the children as
+//   parents of the leaves (gvt, gn).
 // The grid is 1-D, with the (b, h) units spread over the XCDs in contiguous
 // ranges the way the attention kernel spreads them, so that a head's operands
 // are written from the XCD whose L2 then reads them.
@@ -39,14 +41,35 @@ template <> __device__ __forceinline__ void store8<float>(float *dst, const floa
     *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
-template <int D, int CC> __host__ __device__ inline int pack_items(int M0)
+template <int D, int CC, bool L3> __host__ __device__ inline int pack_items(int M0)
 {
     const int NG = CC >= 8 ? CC / 8 : 1;
+    const int n1 = M0 * CC;
     return D * (padded_parents(M0) / 8) + (CC > 0 ? (M0 + 1) * D * NG : 0) + padded_parents(M0) +
-           (M0 + 1) * CC;
+           (M0 + 1) * CC + (L3 ? (n1 + 1) * D * NG + (n1 + 1) * CC : 0);
 }
 
+// child sums of one level: item (p, t, group of 8 children) of `np1` parents
+// (entry np1 - 1 all zero), children of parent p at slots c0 + p*CC + k
 template <typename T, int D, int CC>
+__device__ __forceinline__ void pack_child_item(int a, const float *vs, int c0, int np, T *cvt)
+{
+    constexpr int CG = CC >= 8 ? 8 : CC;   // children per item
+    constexpr int NG = CC / CG;
+    const int t = a % D, r = a / D, cg = r % NG, p = r / NG;
+    T *dst = cvt + ((size_t)p * D + t) * CC + CG * cg;
+    if constexpr (CG == 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = p < np ? vs[((size_t)c0 + (size_t)p * CC + 8 * cg + k) * D + t] : 0.f;
+        store8<T>(dst, v);
+    } else {
+#pragma unroll
+        for (int k = 0; k < CG; ++k) dst[k] = from_float<T>(p < np ? vs[((size_t)c0 + (size_t)p * CC + k) * D + t] : 0.f);
+    }
+}
+
+template <typename T, int D, int CC, bool L3>
 __global__ __launch_bounds__(kPackThreads) void pack_aggregates_kernel(
     const float *__restrict__ vsum, const int32_t *__restrict__ count, int M0, int nbh, int parts,
     unsigned char *__restrict__ pack)
@@ -56,8 +79,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_aggregates_kernel(
     const int bh = unit / parts, part = unit - bh * parts;
     if (bh >= nbh) return;
     const int M0p = padded_parents(M0);
-    const int S = M0 * (1 + CC);
-    const PackLayout PL = pack_layout(M0, CC, D, (int)sizeof(T));
+    const int n1 = M0 * CC;
+    const int S = M0 + n1 + (L3 ? n1 * CC : 0);
+    const PackLayout PL = pack_layout(M0, CC, D, (int)sizeof(T), L3);
     unsigned char *pk = pack + (size_t)bh * PL.bytes;
     const float *vs = vsum + (size_t)bh * S * D;
     const int32_t *cs = count + (size_t)bh * S;
@@ -78,24 +102,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_aggregates_kernel(
         return;
     }
     a -= n_pvt;
+    constexpr int NG = CC >= 8 ? CC / 8 : 1;
     if constexpr (CC > 0) {
-        constexpr int CG = CC >= 8 ? 8 : CC;   // children per item
-        constexpr int NG = CC / CG;
         const int n_cvt = (M0 + 1) * D * NG;
         if (a < n_cvt) {
-            const int t = a % D, r = a / D, cg = r % NG, p = r / NG;
-            T *dst = reinterpret_cast<T *>(pk + PL.cvt) + ((size_t)p * D + t) * CC + CG * cg;
-            if constexpr (CG == 8) {
-                float v[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    v[k] = p < M0 ? vs[((size_t)M0 + (size_t)p * CC + 8 * cg + k) * D + t] : 0.f;
-                store8<T>(dst, v);
-            } else {
-#pragma unroll
-                for (int k = 0; k < CG; ++k)
-                    dst[k] = from_float<T>(p < M0 ? vs[((size_t)M0 + (size_t)p * CC + k) * D + t] : 0.f);
-            }
+            pack_child_item<T, D, CC>(a, vs, M0, M0, reinterpret_cast<T *>(pk + PL.cvt));
             return;
         }
         a -= n_cvt;
@@ -105,42 +116,63 @@ __global__ __launch_bounds__(kPackThreads) void pack_aggregates_kernel(
         return;
     }
     a -= M0p;
-    if (a < (M0 + 1) * CC)
+    if (a < (M0 + 1) * CC) {
         reinterpret_cast<float *>(pk + PL.cn)[a] = a < M0 * CC ? (float)cs[M0 + a] : 0.f;
+        return;
+    }
+    a -= (M0 + 1) * CC;
+    if constexpr (L3) {   // the leaves' sums and counts, the children as parents
+        const int n_gvt = (n1 + 1) * D * NG;
+        if (a < n_gvt) {
+            pack_child_item<T, D, CC>(a, vs, M0 + n1, n1, reinterpret_cast<T *>(pk + PL.gvt));
+            return;
+        }
+        a -= n_gvt;
+        if (a < (n1 + 1) * CC)
+            reinterpret_cast<float *>(pk + PL.gn)[a] = a < n1 * CC ? (float)cs[M0 + n1 + a] : 0.f;
+    }
 }
 
-template <typename T, int D, int CC>
+template <typename T, int D, int CC, bool L3>
 static hipError_t launch_pack_k(const float *vsum, const int32_t *count, int BH, int M0, void *pack,
                                 hipStream_t stream)
 {
-    const int parts = (pack_items<D, CC>(M0) + kPackThreads - 1) / kPackThreads;
+    const int parts = (pack_items<D, CC, L3>(M0) + kPackThreads - 1) / kPackThreads;
     const int grid = (BH * parts + 7) & ~7;
-    hipLaunchKernelGGL((pack_aggregates_kernel<T, D, CC>), dim3(grid), dim3(kPackThreads), 0, stream, vsum,
+    hipLaunchKernelGGL((pack_aggregates_kernel<T, D, CC, L3>), dim3(grid), dim3(kPackThreads), 0, stream, vsum,
                        count, M0, BH, parts, (unsigned char *)pack);
     return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_pack_t(const float *vsum, const int32_t *count, int BH, int M0, int C, void *pack,
-                                hipStream_t stream)
+                                hipStream_t stream, bool l3)
 {
+    if (l3) {
+        switch (C) {
+        case 2: return launch_pack_k<T, D, 2, true>(vsum, count, BH, M0, pack, stream);
+        case 4: return launch_pack_k<T, D, 4, true>(vsum, count, BH, M0, pack, stream);
+        case 8: return launch_pack_k<T, D, 8, true>(vsum, count, BH, M0, pack, stream);
+        default: return launch_pack_k<T, D, 16, true>(vsum, count, BH, M0, pack, stream);
+        }
+    }
     switch (C) {
-    case 0: return launch_pack_k<T, D, 0>(vsum, count, BH, M0, pack, stream);
-    case 2: return launch_pack_k<T, D, 2>(vsum, count, BH, M0, pack, stream);
-    case 4: return launch_pack_k<T, D, 4>(vsum, count, BH, M0, pack, stream);
-    case 8: return launch_pack_k<T, D, 8>(vsum, count, BH, M0, pack, stream);
-    default: return launch_pack_k<T, D, 16>(vsum, count, BH, M0, pack, stream);
+    case 0: return launch_pack_k<T, D, 0, false>(vsum, count, BH, M0, pack, stream);
+    case 2: return launch_pack_k<T, D, 2, false>(vsum, count, BH, M0, pack, stream);
+    case 4: return launch_pack_k<T, D, 4, false>(vsum, count, BH, M0, pack, stream);
+    case 8: return launch_pack_k<T, D, 8, false>(vsum, count, BH, M0, pack, stream);
+    default: return launch_pack_k<T, D, 16, false>(vsum, count, BH, M0, pack, stream);
     }
 }
 
 hipError_t launch_pack_aggregates(const float *vsum, const int32_t *count, int B, int H, int d, int M0, int C,
-                                  int dtype, void *pack, hipStream_t stream)
+                                  int dtype, void *pack, hipStream_t stream, bool three_level)
 {
     if (dtype == 1)
-        return d == 64 ? launch_pack_t<bf16, 64>(vsum, count, B * H, M0, C, pack, stream)
-                       : launch_pack_t<bf16, 128>(vsum, count, B * H, M0, C, pack, stream);
-    return d == 64 ? launch_pack_t<float, 64>(vsum, count, B * H, M0, C, pack, stream)
-                   : launch_pack_t<float, 128>(vsum, count, B * H, M0, C, pack, stream);
+        return d == 64 ? launch_pack_t<bf16, 64>(vsum, count, B * H, M0, C, pack, stream, three_level)
+                       : launch_pack_t<bf16, 128>(vsum, count, B * H, M0, C, pack, stream, three_level);
+    return d == 64 ? launch_pack_t<float, 64>(vsum, count, B * H, M0, C, pack, stream, three_level)
+                   : launch_pack_t<float, 128>(vsum, count, B * H, M0, C, pack, stream, three_level);
 }
 
 }  // namespace avq

@@ -136,7 +136,7 @@ void refine_aggregate_kernel(
     int H, int N, int M0,
     int nchunks, int force_child, const int32_t *__restrict__ sorted,
     const int2 *__restrict__ seg, float *__restrict__ vsum, int32_t *__restrict__ count,
-    int32_t *__restrict__ leaf)
+    int32_t *__restrict__ leaf, int slot_stride, int leaf_base)
 {
     using Cfg = RefineCfg<T, D, CC>;
     constexpr int G = Cfg::G, NW = Cfg::NW, BR = Cfg::BR, BRB = Cfg::BRB, NRB = Cfg::NRB;
@@ -155,7 +155,10 @@ void refine_aggregate_kernel(
     const int Gv = min(G, M0 - p0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, i16 = lane & 15;
-    const int S = M0 * (1 + CC);
+    // slots (and norms) per head: M0 * (1 + CC) for a two-level tree; the
+    // second descent of a three-level tree passes the whole tree's stride
+    // with the arrays offset to its children
+    const int S = slot_stride;
     const int64_t head = (int64_t)bh * N;
     // this wave's transposed-V tile and slot bytes
     T *VT = reinterpret_cast<T *>(un + (size_t)wave * (D * LDK * sizeof(T) + KEYS));
@@ -280,7 +283,7 @@ void refine_aggregate_kernel(
         for (int kb = 0; kb < KB; ++kb) {
             const unsigned ek = (unsigned)__shfl((int)e, 16 * kb + i16);
             key[kb] = (int)(ek & 0xFFFFFFu);
-            lp[kb] = (int)(ek >> 24) - p0;
+            lp[kb] = (int)(((ek >> 24) - (unsigned)p0) & 0xFFu);   // (entries carry parent mod 256)
         }
         // distances to every codeword row; keep the key's own parent block
         f32x4 own[KB][BRB];
@@ -334,7 +337,7 @@ void refine_aggregate_kernel(
             if (g == 0) {
                 SL[16 * kb + i16] = valid ? (unsigned char)(lp[kb] * (CC + 1) + j) : (unsigned char)0xFF;
                 if (valid && leaf)
-                    leaf[head + key[kb]] = to_child ? M0 + (p0 + lp[kb]) * CC + crow : p0 + lp[kb];
+                    leaf[head + key[kb]] = leaf_base + (to_child ? M0 + (p0 + lp[kb]) * CC + crow : p0 + lp[kb]);
             }
             // transpose this column block's values into VT[dim][key]
 #pragma unroll
@@ -462,7 +465,7 @@ template <typename T, int D, int CC>
 static hipError_t launch_refine(const void *K, const void *V, const void *parents,
                                 const void *children, const float *sqnorm, const float *frame, int B, int H,
                                 int N, int M0, unsigned flags, float *vsum, int32_t *count, int32_t *leaf,
-                                const AssignWorkspace &ws, hipStream_t stream)
+                                const AssignWorkspace &ws, int slot_stride, int leaf_base, hipStream_t stream)
 {
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     const size_t lds = RefineCfg<T, D, CC>::lds(nchunks);
@@ -471,7 +474,7 @@ static hipError_t launch_refine(const void *K, const void *V, const void *parent
     hipLaunchKernelGGL((refine_aggregate_kernel<T, D, CC>), dim3(ngroups, B * H), dim3(kRefineThreads),
                        lds, stream, (const T *)K, (const T *)V, (const T *)parents,
                        (const T *)children, sqnorm, frame, H, N, M0, nchunks, (flags & 1u) ? 1 : 0,
-                       ws.sorted, ws.seg, vsum, count, leaf);
+                       ws.sorted, ws.seg, vsum, count, leaf, slot_stride, leaf_base);
     return hipGetLastError();
 }
 
@@ -480,10 +483,11 @@ static hipError_t launch_refine_t(const void *K, const void *V, const void *pare
                                   const float *sqnorm, const float *frame, int B, int H, int N, int M0, int C,
                                   unsigned flags,
                                   float *vsum, int32_t *count, int32_t *leaf,
-                                  const AssignWorkspace &ws, hipStream_t stream)
+                                  const AssignWorkspace &ws, int slot_stride, int leaf_base, hipStream_t stream)
 {
-#define AVQ_REFINE(CCV) \
-    launch_refine<T, D, CCV>(K, V, parents, children, sqnorm, frame, B, H, N, M0, flags, vsum, count, leaf, ws, stream)
+#define AVQ_REFINE(CCV)                                                                                     \
+    launch_refine<T, D, CCV>(K, V, parents, children, sqnorm, frame, B, H, N, M0, flags, vsum, count, leaf, ws, \
+                             slot_stride, leaf_base, stream)
     switch (C) {
     case 0: return AVQ_REFINE(0);
     case 2: return AVQ_REFINE(2);
@@ -492,6 +496,20 @@ static hipError_t launch_refine_t(const void *K, const void *V, const void *pare
     default: return AVQ_REFINE(16);
     }
 #undef AVQ_REFINE
+}
+
+hipError_t launch_refine_slots(const void *K, const void *V, const void *parents, const void *children,
+                                    const float *sqnorm, const float *frame, int B, int H, int N, int d, int M0,
+                                    int C, int dtype, unsigned flags, float *vsum, int32_t *count,
+                                    int32_t *leaf, const AssignWorkspace &ws, int slot_stride, int leaf_base,
+                                    hipStream_t stream)
+{
+#define AVQ_REFINE_ARGS K, V, parents, children, sqnorm, frame, B, H, N, M0, C, flags, vsum, count, leaf, ws, \
+                        slot_stride, leaf_base, stream
+    if (dtype == 1)
+        return d == 64 ? launch_refine_t<bf16, 64>(AVQ_REFINE_ARGS) : launch_refine_t<bf16, 128>(AVQ_REFINE_ARGS);
+    return d == 64 ? launch_refine_t<float, 64>(AVQ_REFINE_ARGS) : launch_refine_t<float, 128>(AVQ_REFINE_ARGS);
+#undef AVQ_REFINE_ARGS
 }
 
 hipError_t launch_assign_aggregate(const void *K, const void *V, const void *parents,
@@ -503,14 +521,8 @@ hipError_t launch_assign_aggregate(const void *K, const void *V, const void *par
 {
     hipError_t err = launch_assign_parent(K, parents, sqnorm, frame, B, H, N, d, M0, C, dtype, ws, nullptr, stream);
     if (err != hipSuccess) return err;
-    if (dtype == 1) {
-        if (d == 64)
-            return launch_refine_t<bf16, 64>(K, V, parents, children, sqnorm, frame, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
-        return launch_refine_t<bf16, 128>(K, V, parents, children, sqnorm, frame, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
-    }
-    if (d == 64)
-        return launch_refine_t<float, 64>(K, V, parents, children, sqnorm, frame, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
-    return launch_refine_t<float, 128>(K, V, parents, children, sqnorm, frame, B, H, N, M0, C, flags, vsum, count, leaf, ws, stream);
+    return launch_refine_slots(K, V, parents, children, sqnorm, frame, B, H, N, d, M0, C, dtype, flags, vsum, count,
+                             leaf, ws, M0 * (1 + C), 0, stream);
 }
 
 }  // namespace avq

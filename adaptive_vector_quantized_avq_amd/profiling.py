@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
     "assign_parent_kernel": ["adaptive_vector_quantized_avq_amd/csrc/assign_parent.hip", *_HDRS],
     "refine_aggregate_kernel": ["adaptive_vector_quantized_avq_amd/csrc/refine_aggregate.hip", *_HDRS],
     "exact_attention_kernel": ["adaptive_vector_quantized_avq_amd/csrc/exact_attention.hip", *_HDRS],
+    "bucket_children_kernel": ["adaptive_vector_quantized_avq_amd/csrc/tree3_stage1.hip", *_HDRS],
 }
 COPY_KERNEL = "probe_copy_kernel"   # the calibration copy (bench.py --copy-probe)
 COPY_BYTES = 256 << 20        # bytes read and bytes written per copy launch

@@ -42,15 +42,18 @@ def log(*a):
 
 
 def algorithmic(inp, P):
-    """Algorithmic bytes and flops per launch ('Roofline')."""
+    """Algorithmic bytes and flops per launch ('Roofline').
+    A three-level tree refines once more: C more distances per key in stage
+    1, P*C more codes per query in stage 2."""
     e = 2 if inp.dtype == "bf16" else 4
     BH, N, d, M0, C = inp.B * inp.H, inp.N, inp.d, inp.M0, inp.C
-    S = M0 * (1 + C)
+    deep = inp.levels == 3
+    S = inp.S_tot
     s1_bytes = BH * (N * 2 * d * e + S * (4 * d + 4))
-    s1_flops = BH * N * 2 * d * (M0 + C)
+    s1_flops = BH * N * 2 * d * (M0 + C * (2 if deep else 1))
     s2_bytes = BH * (N * 2 * d * e + S * (4 * d + 4 + d * e))
-    s2_flops = BH * N * 4 * d * (M0 + P * C)
-    s2_exps = BH * N * (M0 + P * (C + 1))
+    s2_flops = BH * N * 4 * d * (M0 + P * C * (2 if deep else 1))
+    s2_exps = BH * N * (M0 + P * (C + 1) * (2 if deep else 1))
     return dict(s1_bytes=s1_bytes, s1_flops=s1_flops, s2_bytes=s2_bytes, s2_flops=s2_flops,
                 s2_exps=s2_exps)
 
@@ -76,6 +79,8 @@ def cpu_baseline(inp, P, heads):
     """The CPU oracle, as it stands, on the first `heads` heads of batch 0 of
     the workload: stage 1 on all their keys, stage 2 on all their query
     tiles.  Returns the timing record and the oracle's outputs."""
+    import numpy as np
+
     import oracle
     import synth
 
@@ -86,6 +91,22 @@ def cpu_baseline(inp, P, heads):
     ch = sub.f64("children")
     K64, V64, Q64 = sub.f64("K"), sub.f64("V"), sub.f64("Q")
     threads = oracle.default_threads()
+    if inp.levels == 3:
+        oracle.build_tree3(ch[:1], inp.dtype)
+        t0 = time.perf_counter()
+        l0, l1, _ = oracle.build_tree3(ch, inp.dtype)
+        a = oracle.assign3(K64, l0, l1, ch, threads=threads)
+        vsum, count = oracle.aggregate3(V64, a["leaf"], inp.M0, inp.C, threads=threads)
+        t1 = time.perf_counter()
+        r = oracle.attention3(Q64, l0, l1, ch, vsum, count, P, inp.T, inp.scale, threads=threads)
+        t2 = time.perf_counter()
+        rec = dict(value=heads * inp.N / (t2 - t0), unit="tokens/s/head", cores=threads, kind="oracle",
+                   sample=f"{heads} of {inp.B * inp.H} (b,h) units of {inp.name} (three-level tree): stage 1 "
+                          f"on all {inp.N} keys and stage 2 on all {inp.ntiles} query tiles of each, fp64",
+                   stage1_s=round(t1 - t0, 3), stage2_s=round(t2 - t1, 3))
+        a = dict(a, gap_parent=a["gap0"], gap_leaf=np.minimum(a["gap1"], a["gap2"]))
+        return rec, dict(a=a, count=count, Y=r["Y"], imp=r["imp0"], sel=r["sel0"], imp1=r["imp1"],
+                         sel1=r["sel1"])
     oracle.build_tree(ch[:1], inp.dtype)   # loads/compiles outside the timing
     t0 = time.perf_counter()
     par, _ = oracle.build_tree(ch, inp.dtype)
@@ -126,6 +147,8 @@ def oracle_comparison(inp, P, ref, g):
     else:
         amb_tiles = np.zeros(w.shape[:-1], dtype=bool)
     same = (np.sort(g["sel"][:1, :heads], axis=-1) == np.sort(ref["sel"], axis=-1)).all(axis=-1)
+    if "sel1" in ref:   # three-level tree: the children's selection must agree too
+        same = same & (g["sel1"][:1, :heads] == ref["sel1"]).all(axis=-1)
     rows = np.repeat(same, inp.T, axis=-1)[..., :inp.N]
     dY = np.abs(g["Y"][:1, :heads] - ref["Y"])
     return dict(
@@ -139,7 +162,8 @@ def oracle_comparison(inp, P, ref, g):
         selection_mismatch_tiles=int((~same).sum()),
         selection_mismatch_outside_band=int((~same & ~amb_tiles).sum()),
         # keys that stayed at their parent (none is possible without children)
-        sum_residual=None if inp.C == 0 else int(g["count"][..., :M0].sum() - g["count"][..., M0:].sum()),
+        sum_residual=None if inp.C == 0 else
+        int(g["count"][..., :M0].sum() - g["count"][..., M0:M0 + M0 * inp.C].sum()),
     )
 
 
@@ -263,24 +287,45 @@ def main():
         sh = s * 7 * inp.T % inp.N
         sets.append(tuple(torch.roll(x, shifts=sh, dims=2).contiguous() for x in (Q0, K0, V0)))
     del Q0, K0, V0
-    parents, sq, fr = avq.build_tree(ch)
+    deep = inp.levels == 3   # three-level tree: `ch` holds the leaves
     B, H, N, d, S = inp.B, inp.H, inp.N, inp.d, inp.S_tot
+    if deep:
+        parents, mid, sq, fr = avq.build_tree3(ch)
+        ws1_bytes = avq.assign_aggregate3_workspace_size(B, H, N, inp.M0, inp.C, d)
+        ws2_bytes = avq.attention3_workspace_size(B, H, inp.M0, inp.C, d, sets[0][0].dtype)
+    else:
+        parents, sq, fr = avq.build_tree(ch)
+        ws1_bytes = avq.assign_aggregate_workspace_size(B, H, N, inp.M0, inp.C, d)
+        ws2_bytes = avq.attention_workspace_size(B, H, inp.M0, inp.C, d, sets[0][0].dtype)
     vsum = torch.empty((B, H, S, d), dtype=torch.float32, device=dev)
     count = torch.empty((B, H, S), dtype=torch.int32, device=dev)
-    ws1 = torch.empty(avq.assign_aggregate_workspace_size(B, H, N, inp.M0, inp.C, d),
-                      dtype=torch.uint8, device=dev)
-    ws2 = torch.empty(avq.attention_workspace_size(B, H, inp.M0, inp.C, d, sets[0][0].dtype),
-                      dtype=torch.uint8, device=dev)
+    ws1 = torch.empty(ws1_bytes, dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(ws2_bytes, dtype=torch.uint8, device=dev)
     Y = torch.empty_like(sets[0][0])
+
+    def stage1(K, V, want_leaf=False, ws=None, out=None):
+        if deep:
+            return avq.assign_aggregate3(K, V, parents, mid, ch, sq, fr, want_leaf=want_leaf, workspace=ws,
+                                         out=out)
+        return avq.assign_aggregate(K, V, parents, ch, sq, fr, want_leaf=want_leaf, workspace=ws, out=out,
+                                    unfused=args.unfused)
+
+    def stage2(Q, vs, cn, want_sel=False, ws=None, out=None):
+        """-> (Y, sel, sel1 (three-level) or importance (two-level))"""
+        if deep:
+            return avq.attention3_fwd(Q, parents, mid, ch, vs, cn, P, inp.T, inp.scale, want_sel=want_sel,
+                                      workspace=ws, out=out)
+        return avq.attention_fwd(Q, parents, ch, vs, cn, P, inp.T, inp.scale, want_sel=want_sel,
+                                 want_importance=want_sel, workspace=ws, out=out)
 
     def step(i, ev=None):
         Q, K, V = sets[i % len(sets)]
         if ev is not None:
             ev[0].record()
-        avq.assign_aggregate(K, V, parents, ch, sq, fr, workspace=ws1, out=(vsum, count), unfused=args.unfused)
+        stage1(K, V, ws=ws1, out=(vsum, count))
         if ev is not None:
             ev[1].record()
-        avq.attention_fwd(Q, parents, ch, vsum, count, P, inp.T, inp.scale, workspace=ws2, out=Y)
+        stage2(Q, vsum, count, ws=ws2, out=Y)
         if ev is not None:
             ev[2].record()
 
@@ -321,13 +366,16 @@ def main():
     s2_tfs = alg["s2_flops"] / (s2_ms * 1e-3) / 1e12
     s2_gbs = alg["s2_bytes"] / (s2_ms * 1e-3) / 1e9
     s2_bound = "mfma" if alg["s2_flops"] / (peak_mf * 1e12) >= alg["s2_bytes"] / (HBM_PEAK_GBS * 1e9) else "hbm"
+    s1_kernels = ("assign_parent_kernel", "refine_aggregate_kernel") + (("bucket_children_kernel",) if deep else ())
     tr = {k: measured_traffic(k, inp.name) for k in
-          ("assign_parent_kernel", "refine_aggregate_kernel", "pack_aggregates_kernel", "attention_kernel")}
+          s1_kernels + ("pack_aggregates_kernel", "attention_kernel")}
+    # launches per step (a three-level stage 1 runs the refinement twice)
+    per_step = {"refine_aggregate_kernel": 2 if deep else 1}
 
     def total(*ks):
-        return None if any(tr[k] is None for k in ks) else sum(tr[k] for k in ks)
+        return None if any(tr[k] is None for k in ks) else sum(tr[k] * per_step.get(k, 1) for k in ks)
 
-    s1_traffic = total("assign_parent_kernel", "refine_aggregate_kernel")
+    s1_traffic = total(*s1_kernels)
     s2_traffic = total("pack_aggregates_kernel", "attention_kernel")
     if s2_ms >= s1_ms:
         # avq_attention_fwd is two kernels: the operand pack, then attention
@@ -342,7 +390,7 @@ def main():
         roof["traffic_unit"] = "bytes per launch"
         roof["launch_ms"] = round(s2_ms, 5)
     else:
-        roof = dict(kernel="assign_aggregate (assign_parent_kernel + refine_aggregate_kernel)", bound="hbm",
+        roof = dict(kernel="assign_aggregate (" + " + ".join(s1_kernels) + ")", bound="hbm",
                     achieved=round(s1_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(s1_gbs / HBM_PEAK_GBS, 4), traffic=s1_traffic,
                     traffic_unit="bytes per launch", launch_ms=round(s1_ms, 5))
@@ -361,7 +409,7 @@ def main():
         "dtype": inp.dtype,
         "data": "synthetic (seeded PCG64; shapes of the pages' long-sequence timing sweep)",
         "config": {"workload": inp.name, "B": B, "H": H, "N": N, "d": d, "M0": inp.M0,
-                   "C": inp.C, "P": P, "tile": inp.T, "input_sets": args.sets,
+                   "C": inp.C, "P": P, "tile": inp.T, "input_sets": args.sets, "levels": inp.levels,
                    "stage1": "unfused" if args.unfused else "fused"},
         "roofline": roof,
         "stages": {
@@ -388,28 +436,33 @@ def main():
 
     # outputs on input set 0 (the unrotated workload) for the oracle check
     Q, K, V = sets[0]
-    vs0, cn0, lf0 = avq.assign_aggregate(K, V, parents, ch, sq, fr, want_leaf=True, unfused=args.unfused)
-    Y0, sel0, imp0 = avq.attention_fwd(Q, parents, ch, vs0, cn0, P, inp.T, inp.scale,
-                                       want_sel=True, want_importance=True)
+    vs0, cn0, lf0 = stage1(K, V, want_leaf=True)
+    Y0, sel0, extra0 = stage2(Q, vs0, cn0, want_sel=True)
     torch.cuda.synchronize()
     if inp.dtype == "bf16":
         y0 = synth.bf16_bits_to_f64(Y0.cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
     else:
         y0 = Y0.cpu().double().numpy()
     g0 = dict(leaf=lf0.cpu().numpy(), count=cn0.cpu().numpy(), sel=sel0.cpu().numpy(), Y=y0)
-    # the codebook measures the pages report (Table 7 commitment loss, Table 9
-    # active ratio, Table 6 capture) on the same inputs, off the timed region
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record()
-    cm, ac = avq.codebook_diagnostics(K, parents, ch, lf0, cn0)
-    d1.record()
-    cap = avq.capture(Q, K, ch, lf0, sel0, inp.T, inp.scale)
-    torch.cuda.synchronize()
-    out_diag = {"commitment_loss": round(float(cm.mean()), 6), "active_ratio": round(float(ac.mean()), 6),
-                "capture": round(float(cap.mean()), 6), "P": P,
-                "codebook_diagnostics_ms": round(d0.elapsed_time(d1), 4),
-                "sample": "input set 0, every (b, h) and query; means over them"}
-    del vs0, Y0, imp0, cap
+    if deep:
+        g0["sel1"] = extra0.cpu().numpy()
+        out_diag = None   # the diagnostics are defined on the two-level tree
+    else:
+        # the codebook measures the pages report (Table 7 commitment loss,
+        # Table 9 active ratio, Table 6 capture) on the same inputs, off the
+        # timed region
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        cm, ac = avq.codebook_diagnostics(K, parents, ch, lf0, cn0)
+        d1.record()
+        cap = avq.capture(Q, K, ch, lf0, sel0, inp.T, inp.scale)
+        torch.cuda.synchronize()
+        out_diag = {"commitment_loss": round(float(cm.mean()), 6), "active_ratio": round(float(ac.mean()), 6),
+                    "capture": round(float(cap.mean()), 6), "P": P,
+                    "codebook_diagnostics_ms": round(d0.elapsed_time(d1), 4),
+                    "sample": "input set 0, every (b, h) and query; means over them"}
+        del cap
+    del vs0, Y0, extra0
 
     if not args.no_exact_context:
         Q, K, V = sets[0]

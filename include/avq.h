@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define AVQ_ABI_VERSION 2
+#define AVQ_ABI_VERSION 3
 
 enum avq_status {
     AVQ_OK = 0,
@@ -234,6 +234,85 @@ int avq_attention_fwd(const void *Q, const void *parents, const void *children,
                       int d, int M0, int C, int P, int tile, float scale, int dtype,
                       void *Y_out, int32_t *sel_out, float *importance_out,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Three-level tree (roots -> children -> leaves): the deeper hierarchy the
+ * pages propose as the next step (Sec. 6 "Discussion and Conclusion": each
+ * extra level multiplies the codebook's resolution by C and adds P*C codes
+ * per query).  The pages give no algorithm for it; these calls repeat the
+ * two-level rules one level down:
+ *  - tree: a child is the mean of its C leaves, a root the mean of its C*C
+ *    leaves (the Sec. 4.1 constraint at every level);
+ *  - stage 1: nearest root, then that root's C children (taken if strictly
+ *    closer than the root), then that child's C leaves (taken if strictly
+ *    closer than the child); every slot holds its whole cell;
+ *  - stage 2: parent pass, importance and top-P over the roots, correction
+ *    by their children (as avq_attention_fwd); then the level-1 importance
+ *    w_c(I) = sum_{i in I} exp(S_ic - m_i) n_c / Z_i over the P*C children
+ *    just added, with Z after their correction, top-P children (ties ->
+ *    lower child index), and the same correction by their leaves, a child's
+ *    logit recovered as the mean of its leaves' logits.
+ * Slots per head: [0, M0) roots; M0 + p*C + a children; M0 + M0*C +
+ * (p*C + a)*C + b leaves; S3 = M0 (1 + C + C*C).  C in {2, 4, 8, 16}.
+ */
+
+/*
+ * avq_build_tree3 -- the two upper levels, frame and norms of a frozen
+ * three-level tree (once per codebook).
+ *   leaves     [H][M0][C][C][d] dtype  input
+ *   level0_out [H][M0][d]       dtype  roots: mean of each root's C*C leaves
+ *   level1_out [H][M0][C][d]    dtype  children: mean of each child's C leaves
+ *              (both accumulated in fp64 and rounded once to dtype)
+ *   sqnorm_out [H][S3]          fp32   ||c - r||^2 of every codeword, slot order
+ *   frame_out  [H][d]           fp32   reference point r as in avq_build_tree,
+ *                                      over the codewords of all three levels
+ */
+int avq_build_tree3(const void *leaves, int H, int M0, int C, int d, int dtype, void *level0_out,
+                    void *level1_out, float *sqnorm_out, float *frame_out, void *stream);
+
+/* bytes of device workspace avq_assign_aggregate3 needs (0 if invalid) */
+size_t avq_assign_aggregate3_workspace_size(int B, int H, int N, int M0, int C, int d);
+
+/*
+ * avq_assign_aggregate3 -- stage 1 on a three-level tree (rule above).
+ *   K, V       [B][H][N][d]       dtype
+ *   level0, level1, sqnorm, frame from avq_build_tree3; leaves [H][M0][C][C][d]
+ *   flags      0 or AVQ_FLAG_FORCE_CHILD (descend at both steps regardless
+ *              of the distance to the level above)
+ *   vsum_out   [B][H][S3][d] fp32, count_out [B][H][S3] int32: whole cells
+ *              (every slot written)
+ *   leaf_out   [B][H][N] int32 optional: each key's final slot
+ *   workspace  at least avq_assign_aggregate3_workspace_size(...) bytes,
+ *              256-byte aligned, caller-owned, not shared with a concurrent
+ *              call.  Repeated calls give identical bits.
+ */
+int avq_assign_aggregate3(const void *K, const void *V, const void *level0, const void *level1,
+                          const void *leaves, const float *sqnorm, const float *frame, int B, int H,
+                          int N, int d, int M0, int C, int dtype, unsigned flags, float *vsum_out,
+                          int32_t *count_out, int32_t *leaf_out, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* bytes of device workspace avq_attention3_fwd needs (0 if invalid) */
+size_t avq_attention3_workspace_size(int B, int H, int M0, int C, int d, int dtype);
+
+/*
+ * avq_attention3_fwd -- stage 2 on a three-level tree (rule above).
+ *   Q          [B][H][N][d] dtype
+ *   level0, level1, leaves   the tree (avq_build_tree3)
+ *   vsum, count [B][H][S3]   whole-cell aggregates (avq_assign_aggregate3 or
+ *              any caller-built sums in that layout); read, never written
+ *   P          0 <= P <= M0 and P*C <= 256: refinements per tile at each level
+ *   tile, scale, Y_out, workspace as in avq_attention_fwd (workspace of
+ *              avq_attention3_workspace_size bytes)
+ *   sel0_out   [B][H][ceil(N/tile)][P] int32 optional: selected roots, ascending
+ *   sel1_out   [B][H][ceil(N/tile)][P] int32 optional: selected children
+ *              p*C + a, ascending
+ */
+int avq_attention3_fwd(const void *Q, const void *level0, const void *level1, const void *leaves,
+                       const float *vsum, const int32_t *count, int B, int H, int N, int d, int M0,
+                       int C, int P, int tile, float scale, int dtype, void *Y_out,
+                       int32_t *sel0_out, int32_t *sel1_out, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /*
  * avq_diagnostics_workspace_size -- bytes of device workspace that

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.avq_abi_version() == 2
+    assert lib.avq_abi_version() == 3
     assert lib.avq_status_string(0) == b"AVQ_OK"
     assert lib.avq_status_string(-1) == b"AVQ_ERR_INVALID_ARG"
     assert lib.avq_status_string(-2) == b"AVQ_ERR_UNSUPPORTED"
@@ -165,3 +165,38 @@ def test_gilbert_order_rejects_bad_grids(lib):
     assert lib.avq_gilbert_order(2048, 1024, buf) == -2
     assert lib.avq_gilbert_order(4, 4, None) == -1
     assert avq.gilbert_order(2, 3).numel() == 6
+
+
+def test_three_level_workspace_sizes(lib):
+    al = lambda x: (x + 255) // 256 * 256
+    # per (b,h): the two-level pack of 64 roots with 8 children, then the
+    # children's leaf sums [513][d][8] and counts [513][8]
+    per = (al(64 * 64 * 2) + al(64 * 4) + al(65 * 64 * 8 * 2) + al(65 * 8 * 4)
+           + al(513 * 64 * 8 * 2) + al(513 * 8 * 4))
+    assert lib.avq_attention3_workspace_size(1, 8, 64, 8, 64, 1) == 8 * per
+    assert lib.avq_attention3_workspace_size(1, 8, 64, 0, 64, 1) == 0
+    # lists + segment table of the second descent (512 children in groups of
+    # 4, 64 chunks of 1024 keys) + leaf ids
+    bhn = 8 * 65536
+    want = al(bhn * 4) + al(8 * 128 * 64 * 8) + al(bhn * 4)
+    assert lib.avq_assign_aggregate3_workspace_size(1, 8, 65536, 64, 8, 64) == want
+    assert lib.avq_assign_aggregate3_workspace_size(1, 8, 65536, 64, 0, 64) == 0
+
+
+def test_three_level_rejects_bad_arguments(lib):
+    p = ctypes.c_void_p(16)
+    lib.avq_build_tree3.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p] * 5
+    assert lib.avq_build_tree3(p, 1, 4, 0, 64, 1, p, p, p, p, None) == -1        # needs children
+    assert lib.avq_build_tree3(p, 1, 4, 3, 64, 1, p, p, p, p, None) == -2        # C = 3
+    assert lib.avq_build_tree3(None, 1, 4, 4, 64, 1, p, p, p, p, None) == -1
+    f = lib.avq_attention3_fwd
+    f.argtypes = ([ctypes.c_void_p] * 6 + [ctypes.c_int] * 8 + [ctypes.c_float, ctypes.c_int]
+                  + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p])
+    big = 1 << 40
+    # P*C = 272 level-1 candidates: more than a tile's selection handles
+    assert f(p, p, p, p, p, p, 1, 1, 256, 64, 64, 16, 17, 128, 1.0, 1, p, None, None, p, big, None) == -2
+    assert f(p, p, p, p, p, p, 1, 1, 256, 64, 64, 8, 65, 128, 1.0, 1, p, None, None, p, big, None) == -1
+    g = lib.avq_assign_aggregate3
+    g.argtypes = ([ctypes.c_void_p] * 7 + [ctypes.c_int] * 7 + [ctypes.c_uint]
+                  + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p])
+    assert g(p, p, p, p, p, p, p, 1, 1, 256, 64, 8, 4, 1, 2, p, p, None, p, big, None) == -1   # unfused flag
