@@ -23,26 +23,55 @@
 
 namespace avq {
 
-size_t assign_workspace_bytes(int B, int H, int N, int M0, int C, int D)
+// workspace regions: key lists, segment tables, split groups' partial sums
+// and their flags (each 256-byte aligned)
+static void assign_regions(int B, int H, int N, int M0, int C, int D, size_t (&sz)[5])
 {
     const int64_t nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     const int group = refine_group(C, D);
     const int64_t ngroups = (M0 + group - 1) / group;
-    size_t a = (size_t)B * H * N * sizeof(int32_t);
-    a = (a + 255) & ~(size_t)255;
-    size_t b = (size_t)B * H * ngroups * nchunks * sizeof(int2);
-    return a + ((b + 255) & ~(size_t)255);
+    const size_t bh = (size_t)B * H;
+    const RefinePlan pl = refine_plan(N, M0, C, D);
+    sz[0] = align256(bh * N * sizeof(int32_t));
+    sz[1] = align256(bh * ngroups * nchunks * sizeof(int2));
+    sz[2] = align256(bh * nchunks * 2 * sizeof(int32_t));
+    sz[3] = align256(bh * pl.max_partials * refine_partial_words(C, D) * sizeof(float));
+    sz[4] = align256(bh * pl.max_partials * sizeof(unsigned));
+}
+
+size_t assign_workspace_bytes(int B, int H, int N, int M0, int C, int D)
+{
+    size_t sz[5];
+    assign_regions(B, H, N, M0, C, D, sz);
+    return sz[0] + sz[1] + sz[2] + sz[3] + sz[4];
 }
 
 AssignWorkspace carve_assign_workspace(void *base, int B, int H, int N, int M0, int C, int D)
 {
+    size_t sz[5];
+    assign_regions(B, H, N, M0, C, D, sz);
     AssignWorkspace ws;
-    size_t a = (size_t)B * H * N * sizeof(int32_t);
-    a = (a + 255) & ~(size_t)255;
-    ws.sorted = (int32_t *)base;
-    ws.seg = (int2 *)((char *)base + a);
-    ws.bytes = assign_workspace_bytes(B, H, N, M0, C, D);
+    char *p = (char *)base;
+    ws.sorted = (int32_t *)p;
+    p += sz[0];
+    ws.seg = (int2 *)p;
+    p += sz[1];
+    ws.cmax = (int32_t *)p;
+    p += sz[2];
+    ws.partial = (float *)p;
+    p += sz[3];
+    ws.pflag = (unsigned *)p;
+    ws.bytes = sz[0] + sz[1] + sz[2] + sz[3] + sz[4];
     return ws;
+}
+
+unsigned next_call_tag()
+{
+    static std::atomic<unsigned> counter{0x9E3779B9u};
+    unsigned t;
+    do t = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    while (t == 0u);
+    return t;
 }
 
 // ---------------------------------------------------------------------------
@@ -76,7 +105,7 @@ template <typename T, int D, int NRB>
 __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(assign_waves_per_simd<T, D>()))) void assign_parent_kernel(
     const T *__restrict__ K, const T *__restrict__ parents, const float *__restrict__ sqnorm,
     const float *__restrict__ frame, int H, int N, int M0, int C, int nchunks, int32_t *__restrict__ sorted,
-    int2 *__restrict__ seg, int32_t *__restrict__ leaf_direct)
+    int2 *__restrict__ seg, int32_t *__restrict__ leaf_direct, int32_t *__restrict__ cmax)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NT = kAssignThreads;
@@ -318,9 +347,16 @@ __global__ __launch_bounds__(kAssignThreads) __attribute__((amdgpu_waves_per_eu(
     // p >= M0 equals nk: those parents have no keys)
     const int group = refine_group(C, D);
     const int ngroups = (M0 + group - 1) / group;
+    int most = 0;   // the largest group of this chunk (groups < 128: waves 0 and 1)
     for (int gr = tid; gr < ngroups; gr += NT) {
         const int a = hist[gr * group], b = hist[min((gr + 1) * group, M0)];
         seg[((int64_t)bh * ngroups + gr) * nchunks + chunk] = int2{a, b - a};
+        most = max(most, b - a);
+    }
+    if (wave < 2) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) most = max(most, __shfl_xor(most, off));
+        if (lane == 0) cmax[((int64_t)bh * nchunks + chunk) * 2 + wave] = most;
     }
     __syncthreads();
 #pragma unroll
@@ -349,7 +385,7 @@ static hipError_t launch_assign(const void *K, const void *parents, const float 
     allow_full_lds<assign_parent_kernel<T, D, NRB>>();
     hipLaunchKernelGGL((assign_parent_kernel<T, D, NRB>), dim3(nchunks, B * H), dim3(kAssignThreads), lds, stream,
                        (const T *)K, (const T *)parents, sqnorm, frame, H, N, M0, C, nchunks, ws.sorted,
-                       ws.seg, leaf_direct);
+                       ws.seg, leaf_direct, ws.cmax);
     return hipGetLastError();
 }
 

@@ -39,12 +39,50 @@ __host__ __device__ constexpr int refine_group(int C, int D)
     return C == 16 && D == 128 ? 2 : 4;
 }
 
+// How the refinement kernel splits its groups' key lists.  A (b, h) whose
+// per-chunk largest group counts sum to at most `quiet` (three times the
+// mean group length, at least 1024) cannot hold a group that long: no group
+// is split.  Otherwise a group longer than `target` keys (twice the mean,
+// at least 1024) becomes ceil(n / target) equal slices, one work-group
+// each; then at most max_items items and max_partials stored partial sums
+// per (b, h).
+struct RefinePlan {
+    int target, quiet, max_items, max_partials;
+};
+inline RefinePlan refine_plan(int N, int M0, int C, int D)
+{
+    const int ngroups = (M0 + refine_group(C, D) - 1) / refine_group(C, D);
+    const int mean = (N + ngroups - 1) / ngroups;
+    RefinePlan p;
+    p.target = 2 * mean < 1024 ? 1024 : 2 * mean;
+    p.quiet = 3 * mean < 1024 ? 1024 : 3 * mean;
+    p.max_partials = (N + p.target - 1) / p.target;
+    p.max_items = ngroups + p.max_partials;
+    return p;
+}
+// fp32 words of one stored partial: the slot rows of a group (padded to 16)
+// times (D value sums + 1 count)
+inline size_t refine_partial_words(int C, int D)
+{
+    const int rows = (refine_group(C, D) * (C + 1) + 15) / 16 * 16;
+    return (size_t)rows * (D + 1);
+}
+// a tag distinct for every refinement launch of the process (never 0): a
+// slice's "partial stored" flag is the tag of its launch, so flags left in
+// a workspace by earlier calls never match
+unsigned next_call_tag();
+
 struct AssignWorkspace {
     int32_t *sorted;      // [B*H][N]  key index | parent << 24, bucketed per chunk
     int2 *seg;            // [B*H][ceil(M0/refine_group)][nchunks] {start, length} of
                           // each refinement group's keys inside each chunk's list
+    int32_t *cmax;        // [B*H][nchunks][2] largest group's key count in each chunk (two
+                          // halves of the groups; a bound on every group's total)
+    float *partial;       // [B*H][max_partials][refine_partial_words] sums of split groups' slices
+    unsigned *pflag;      // [B*H][max_partials] launch tag once a slice's partial is stored
     size_t bytes;
 };
+
 
 // Aggregates rearranged as stage-2 MFMA operands (written into the stage-2
 // workspace from the caller's fp32 value sums and int32 counts by

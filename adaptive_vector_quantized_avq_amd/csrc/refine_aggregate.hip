@@ -4,8 +4,14 @@
 // to the nearest child (ties -> lowest index) if that child is strictly closer
 // than the parent.  Value sums and counts are accumulated at both levels: a
 // parent slot covers its whole cell, a child slot the keys that moved to it.
-// One work-group owns a group of parents and writes every output slot of
-// those parents exactly once (no global atomics, no pre-zeroing).
+// Work is split by group of parents: a group whose key list is longer than a
+// target (twice the mean, at least 1024 keys) is cut into equal slices of
+// its list, one work-group each, so that a skewed key distribution (a few
+// parents holding most keys) does not leave one work-group with most of the
+// work.  A group of one slice writes its output slots itself; for a split
+// group, every slice but the last stores its partial sums and the last one
+// adds them in slice order to its own and writes the slots, so the result
+// does not depend on timing (no float atomics, no pre-zeroing).
 #include "avq_kernels.h"
 
 namespace avq {
@@ -136,7 +142,9 @@ void refine_aggregate_kernel(
     int H, int N, int M0,
     int nchunks, int force_child, const int32_t *__restrict__ sorted,
     const int2 *__restrict__ seg, float *__restrict__ vsum, int32_t *__restrict__ count,
-    int32_t *__restrict__ leaf, int slot_stride, int leaf_base)
+    int32_t *__restrict__ leaf, int slot_stride, int leaf_base, int ngroups, int target, int quiet, int npmax,
+    unsigned tag, const int32_t *__restrict__ cmax, float *__restrict__ partial,
+    unsigned *__restrict__ pflag)
 {
     using Cfg = RefineCfg<T, D, CC>;
     constexpr int G = Cfg::G, NW = Cfg::NW, BR = Cfg::BR, BRB = Cfg::BRB, NRB = Cfg::NRB;
@@ -151,10 +159,85 @@ void refine_aggregate_kernel(
     int *pre = reinterpret_cast<int *>(un + ((Cfg::union_bytes + 15) & ~(size_t)15));   // [nchunks+1]
     int *segs = pre + nchunks + 1;                                         // [nchunks]
 
-    const int p0 = blockIdx.x * G, bh = blockIdx.y, h = bh % H;
-    const int Gv = min(G, M0 - p0);
+    const int bh = blockIdx.x, item = blockIdx.y, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, i16 = lane & 15;
+
+    // ---- this work-group's item.  The per-chunk largest group counts bound
+    // every group's total: when their sum stays within `quiet`, no group is
+    // split and item g is simply group g (one load per lane).  Otherwise
+    // the groups' totals are summed from the chunks' segment tables, the
+    // slices per group scanned, and the item's group and slice looked up.
+    // (The plan arrays live in the union region, before its use.)
+    int *gsz = reinterpret_cast<int *>(un);      // [ngroups]
+    int *ist = gsz + ngroups;                    // [ngroups + 1] first item of each group
+    int *pst = ist + ngroups + 1;                // [ngroups + 1] first partial slot of each group
+    int bound = 0;
+    for (int c = lane; c < nchunks; c += 64) {
+        const int2 m = *reinterpret_cast<const int2 *>(cmax + ((int64_t)bh * nchunks + c) * 2);
+        bound += max(m.x, m.y);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) bound += __shfl_xor(bound, off);
+    int gq, slice, nslices, gsize = -1, pslot = 0;
+    if (bound <= quiet) {
+        if (item >= ngroups) return;
+        gq = item;
+        slice = 0;
+        nslices = 1;
+    } else {
+        for (int gi = tid; gi < ngroups; gi += NT) gsz[gi] = 0;
+        __syncthreads();
+        // every (group, chunk) entry once, loads independent of each other
+        for (int e = tid; e < ngroups * nchunks; e += NT)
+            atomicAdd(gsz + e / nchunks, seg[(int64_t)bh * ngroups * nchunks + e].y);
+        __syncthreads();
+        if (wave == 0) {   // exclusive scans of the slice and partial-slot counts
+            int c1 = 0, c2 = 0;
+            for (int base = 0; base < ngroups; base += 64) {
+                const int gi = base + lane;
+                const int ns = gi < ngroups ? max(1, (gsz[gi] + target - 1) / target) : 0;
+                const int np = ns > 1 ? ns - 1 : 0;
+                int i1 = ns, i2 = np;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int t1 = __shfl_up(i1, off), t2 = __shfl_up(i2, off);
+                    if (lane >= off) {
+                        i1 += t1;
+                        i2 += t2;
+                    }
+                }
+                if (gi < ngroups) {
+                    ist[gi] = c1 + i1 - ns;
+                    pst[gi] = c2 + i2 - np;
+                }
+                c1 += __shfl(i1, 63);
+                c2 += __shfl(i2, 63);
+            }
+            if (lane == 0) {
+                ist[ngroups] = c1;
+                pst[ngroups] = c2;
+            }
+        }
+        __syncthreads();
+        if (item >= ist[ngroups]) return;    // past this (b, h)'s items (the same for the whole group)
+        int lo = 0, hi = ngroups;            // the group: last one whose first item is <= item
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            const bool right = ist[mid] <= item;
+            lo = right ? mid : lo;
+            hi = right ? hi : mid;
+        }
+        gq = lo;
+        slice = item - ist[gq];
+        nslices = ist[gq + 1] - ist[gq];
+        gsize = gsz[gq];
+        pslot = pst[gq];
+        __syncthreads();                     // the plan arrays are dead from here
+    }
+
+    const int p0 = gq * G;
+    const int Gv = min(G, M0 - p0);
     // slots (and norms) per head: M0 * (1 + CC) for a two-level tree; the
     // second descent of a three-level tree passes the whole tree's stride
     // with the arrays offset to its children
@@ -190,7 +273,7 @@ void refine_aggregate_kernel(
         }
     }
     for (int c = tid; c < nchunks; c += NT) {
-        const int2 sg = seg[((int64_t)bh * gridDim.x + blockIdx.x) * nchunks + c];
+        const int2 sg = seg[((int64_t)bh * ngroups + gq) * nchunks + c];
         pre[c] = sg.y;
         segs[c] = c * kAssignChunk + sg.x;
     }
@@ -229,6 +312,10 @@ void refine_aggregate_kernel(
     }
     __syncthreads();
     const int total = pre[nchunks];
+    // this work-group's list positions [xs, xe): the whole group, or its
+    // slice of equal parts
+    const int xs = gsize < 0 ? 0 : (int)((int64_t)gsize * slice / nslices);
+    const int xe = gsize < 0 ? total : (int)((int64_t)gsize * (slice + 1) / nslices);
 
     // raw list entry (key | parent << 24) at position x of the group's list;
     // positions past the end read the last entry (never used)
@@ -243,7 +330,7 @@ void refine_aggregate_kernel(
         }
         return (unsigned)sorted[head + segs[lo] + (x - pre[lo])];
     };
-    auto xpos = [&](int s) { return (s * NW + wave) * KEYS; };
+    auto xpos = [&](int s) { return xs + (s * NW + wave) * KEYS; };
     auto load_kv = [&](unsigned e, Frag<T> (&kf)[KB][KS], Frag<T> (&vf)[KB][KS]) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -333,7 +420,7 @@ void refine_aggregate_kernel(
             }
             const bool to_child = CC > 0 && (force_child || cbest < pe);
             const int j = to_child ? crow : CC;
-            const bool valid = x0 + 16 * kb + i16 < total;
+            const bool valid = x0 + 16 * kb + i16 < xe;
             if (g == 0) {
                 SL[16 * kb + i16] = valid ? (unsigned char)(lp[kb] * (CC + 1) + j) : (unsigned char)0xFF;
                 if (valid && leaf)
@@ -375,7 +462,8 @@ void refine_aggregate_kernel(
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    const int nsteps = total > wave * KEYS ? (total - wave * KEYS + NW * KEYS - 1) / (NW * KEYS) : 0;
+    const int span = xe - xs;   // this slice's list positions [xs, xe)
+    const int nsteps = span > wave * KEYS ? (span - wave * KEYS + NW * KEYS - 1) / (NW * KEYS) : 0;
     if (nsteps > 0) {
         Frag<T> kf[KB][KS], vf[KB][KS];
         unsigned e0 = entry(xpos(0) + lane), e1 = entry(xpos(1) + lane);
@@ -436,6 +524,43 @@ void refine_aggregate_kernel(
         __syncthreads();
     }
 
+    // ---- a split group: slices before the last store their sums for the
+    // last one, which adds them in slice order.  The stores and loads are
+    // agent-scope atomics (coherent across the XCDs' L2s); a slice's flag,
+    // the call's tag, is stored once all its sums have landed.
+    constexpr int PROWS = NSB * 16;
+    if (nslices > 1) {
+        const int64_t pbase = (int64_t)bh * npmax;
+        if (slice < nslices - 1) {
+            float *pp = partial + (pbase + pslot + slice) * (PROWS * (D + 1));
+            for (int e = tid; e < PROWS * D; e += NT)
+                __hip_atomic_store(pp + e, acc[(e / D) * LDA + e % D], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int e = tid; e < PROWS; e += NT)
+                __hip_atomic_store(pp + PROWS * D + e, cntf[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(pflag + pbase + pslot + slice, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        // the last slice: every earlier slice of the group has a lower item
+        // index, so it was dispatched earlier and finishes without waiting
+        for (int q = tid; q < nslices - 1; q += NT) {
+            const unsigned *f = pflag + pbase + pslot + q;
+            while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag) __builtin_amdgcn_s_sleep(2);
+        }
+        __syncthreads();
+        asm volatile("" ::: "memory");
+        for (int e = tid; e < PROWS * (D + 1); e += NT) {
+            float sum = 0.f;
+            for (int q = 0; q < nslices - 1; ++q)
+                sum += __hip_atomic_load(partial + (pbase + pslot + q) * (PROWS * (D + 1)) + e, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+            if (e < PROWS * D) acc[(e / D) * LDA + e % D] += sum;
+            else cntf[e - PROWS * D] += sum;
+        }
+        __syncthreads();
+    }
+
     // ---- outputs: child slots as accumulated; parent = stayed + children
     float *vs = vsum + (int64_t)bh * S * D;
     int32_t *cs = count + (int64_t)bh * S;
@@ -467,14 +592,22 @@ static hipError_t launch_refine(const void *K, const void *V, const void *parent
                                 int N, int M0, unsigned flags, float *vsum, int32_t *count, int32_t *leaf,
                                 const AssignWorkspace &ws, int slot_stride, int leaf_base, hipStream_t stream)
 {
+    using Cfg = RefineCfg<T, D, CC>;
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
-    const size_t lds = RefineCfg<T, D, CC>::lds(nchunks);
+    const int ngroups = (M0 + Cfg::G - 1) / Cfg::G;
+    const RefinePlan pl = refine_plan(N, M0, CC, D);
+    // the plan arrays share the union region when they fit in it
+    const size_t plan_bytes = (size_t)(3 * ngroups + 2) * 4;
+    const size_t lds = Cfg::lds(nchunks) + (plan_bytes > Cfg::union_bytes ? plan_bytes - Cfg::union_bytes + 16 : 0);
     allow_full_lds<refine_aggregate_kernel<T, D, CC>>();
-    const int ngroups = (M0 + RefineCfg<T, D, CC>::G - 1) / RefineCfg<T, D, CC>::G;
-    hipLaunchKernelGGL((refine_aggregate_kernel<T, D, CC>), dim3(ngroups, B * H), dim3(kRefineThreads),
+    // grid (b*h, items): consecutive work-groups take the same item of
+    // consecutive heads, so every head's real items come before any head's
+    // unused ones
+    hipLaunchKernelGGL((refine_aggregate_kernel<T, D, CC>), dim3(B * H, pl.max_items), dim3(kRefineThreads),
                        lds, stream, (const T *)K, (const T *)V, (const T *)parents,
                        (const T *)children, sqnorm, frame, H, N, M0, nchunks, (flags & 1u) ? 1 : 0,
-                       ws.sorted, ws.seg, vsum, count, leaf, slot_stride, leaf_base);
+                       ws.sorted, ws.seg, vsum, count, leaf, slot_stride, leaf_base, ngroups, pl.target,
+                       pl.quiet, pl.max_partials, next_call_tag(), ws.cmax, ws.partial, ws.pflag);
     return hipGetLastError();
 }
 
@@ -522,7 +655,7 @@ hipError_t launch_assign_aggregate(const void *K, const void *V, const void *par
     hipError_t err = launch_assign_parent(K, parents, sqnorm, frame, B, H, N, d, M0, C, dtype, ws, nullptr, stream);
     if (err != hipSuccess) return err;
     return launch_refine_slots(K, V, parents, children, sqnorm, frame, B, H, N, d, M0, C, dtype, flags, vsum, count,
-                             leaf, ws, M0 * (1 + C), 0, stream);
+                               leaf, ws, M0 * (1 + C), 0, stream);
 }
 
 }  // namespace avq

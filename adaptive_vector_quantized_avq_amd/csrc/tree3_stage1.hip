@@ -26,7 +26,8 @@ namespace avq {
 // (it needs the child only relative to its group's first child).
 __global__ __launch_bounds__(64) void bucket_children_kernel(const int32_t *__restrict__ leaf, int N, int M0,
                                                              int C, int group, int ngroups, int nbits, int nchunks,
-                                                             int32_t *__restrict__ sorted, int2 *__restrict__ seg)
+                                                             int32_t *__restrict__ sorted, int2 *__restrict__ seg,
+                                                             int32_t *__restrict__ cmax)
 {
     extern __shared__ int cnt[];   // [ngroups]: counts, then running positions
     const int chunk = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
@@ -61,10 +62,11 @@ __global__ __launch_bounds__(64) void bucket_children_kernel(const int32_t *__re
         if (v && mbcnt(m) == 0) cnt[gi] += __popcll(m);   // one lane per group
         __syncthreads();
     }
-    int carry = 0;   // exclusive scan -> the chunk's segment table
+    int carry = 0, most = 0;   // exclusive scan -> the chunk's segment table
     for (int base = 0; base < ngroups; base += 64) {
         const int g = base + lane;
         const int v = g < ngroups ? cnt[g] : 0;
+        most = max(most, v);
         int inc = v;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -78,6 +80,9 @@ __global__ __launch_bounds__(64) void bucket_children_kernel(const int32_t *__re
         }
         carry += __shfl(inc, 63);
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) most = max(most, __shfl_xor(most, off));
+    if (lane < 2) cmax[((int64_t)bh * nchunks + chunk) * 2 + lane] = lane == 0 ? most : 0;
     __syncthreads();
     for (int r = 0; r < rounds; ++r) {   // stable scatter in key order
         const int x = 64 * r + lane;
@@ -121,7 +126,7 @@ hipError_t launch_assign_aggregate3(const void *K, const void *V, const void *le
     while ((1 << nbits) < ngroups) ++nbits;
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
     hipLaunchKernelGGL(bucket_children_kernel, dim3(nchunks, B * H), dim3(64), (size_t)ngroups * sizeof(int), stream,
-                       (const int32_t *)lf, N, M0, C, group, ngroups, nbits, nchunks, ws.sorted, ws.seg);
+                       (const int32_t *)lf, N, M0, C, group, ngroups, nbits, nchunks, ws.sorted, ws.seg, ws.cmax);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     return launch_refine_slots(K, V, level1, leaves, sqnorm + M0, frame, B, H, N, d, n1, C, dtype, flags,

@@ -57,13 +57,33 @@ def test_attention_workspace_size(lib):
     assert f(0, 1, 16, 8, 64, 1) == 0
 
 
+def _assign_ws(B, H, N, M0, C, d):
+    """[B*H*N] int32 key list + [B*H][groups][ceil(N/1024) chunks] int2
+    segments + each chunk's largest group count [B*H][chunks][2] i32 + the split
+    groups' partial sums [B*H][ceil(N/target)][rows * (d + 1)] fp32 and their
+    flags [B*H][ceil(N/target)] u32, each 256-aligned;
+    groups of 4 parents (of 2 for C = 16 at d = 128), target = twice the
+    mean group length and at least 1024 keys, rows = the group's slots
+    rounded up to 16."""
+    al = lambda x: (x + 255) // 256 * 256
+    grp = 2 if (C == 16 and d == 128) else 4
+    ngroups = -(-M0 // grp)
+    target = max(1024, 2 * -(-N // ngroups))
+    npart = -(-N // target)
+    rows = -(-(grp * (C + 1)) // 16) * 16
+    bh = B * H
+    return (al(bh * N * 4) + al(bh * ngroups * -(-N // 1024) * 8) + al(bh * -(-N // 1024) * 8)
+            + al(bh * npart * rows * (d + 1) * 4) + al(bh * npart * 4))
+
+
 def test_workspace_size(lib):
     f = lib.avq_assign_aggregate_workspace_size
-    # [B*H*N] int32 key list + [B*H][ceil(M0/group) groups][ceil(N/1024) chunks]
-    # int2 segments, each 256-aligned; groups of 4 parents, of 2 for C = 16 at
-    # d = 128
-    assert f(1, 8, 65536, 256, 8, 64) == 8 * 65536 * 4 + ((8 * 64 * 64 * 8 + 255) // 256) * 256
-    assert f(2, 10, 32768, 256, 16, 128) == 20 * 32768 * 4 + ((20 * 128 * 32 * 8 + 255) // 256) * 256
+    assert f(1, 8, 65536, 256, 8, 64) == _assign_ws(1, 8, 65536, 256, 8, 64)
+    assert f(2, 10, 32768, 256, 16, 128) == _assign_ws(2, 10, 32768, 256, 16, 128)
+    assert f(2, 16, 16384, 128, 8, 64) == _assign_ws(2, 16, 16384, 128, 8, 64)
+    # long-64k: lists 2 MiB, segments 256 KiB, chunk maxima 4 KiB, 32 partial
+    # slots per head (target 2048 keys)
+    assert _assign_ws(1, 8, 65536, 256, 8, 64) == 8 * 65536 * 4 + 262144 + 4096 + 8 * 32 * 48 * 65 * 4 + 1024
     assert f(1, 1, 1, 1, 4, 64) > 0
     assert f(1, 1, 1, 300, 4, 64) == 0      # M0 > 256 unsupported
     assert f(1, 1, 1, 8, 3, 64) == 0        # C = 3 unsupported
@@ -175,10 +195,9 @@ def test_three_level_workspace_sizes(lib):
            + al(513 * 64 * 8 * 2) + al(513 * 8 * 4))
     assert lib.avq_attention3_workspace_size(1, 8, 64, 8, 64, 1) == 8 * per
     assert lib.avq_attention3_workspace_size(1, 8, 64, 0, 64, 1) == 0
-    # lists + segment table of the second descent (512 children in groups of
-    # 4, 64 chunks of 1024 keys) + leaf ids
-    bhn = 8 * 65536
-    want = al(bhn * 4) + al(8 * 128 * 64 * 8) + al(bhn * 4)
+    # the second descent's workspace (512 children as parents, in groups of
+    # 4) + leaf ids
+    want = _assign_ws(1, 8, 65536, 512, 8, 64) + al(8 * 65536 * 4)
     assert lib.avq_assign_aggregate3_workspace_size(1, 8, 65536, 64, 8, 64) == want
     assert lib.avq_assign_aggregate3_workspace_size(1, 8, 65536, 64, 0, 64) == 0
 
