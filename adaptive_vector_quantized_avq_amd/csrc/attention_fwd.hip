@@ -603,10 +603,13 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
             // up to 2^32 above it are harmless in fp32 and bf16, so it is
             // raised (and X, Z rescaled) only when a child logit exceeds it
             // by more than that, which takes extreme logit ranges.
-            {
+            // (any lane over the limit <=> some query's maximum is: the shift
+            // is the same in a query's four lanes; the cross-lane maximum is
+            // formed only then)
+            if (__ballot((fmaf(c0m, sl2, -m0) > 32.f) | (fmaf(c1m, sl2, -m1) > 32.f))) {
                 const float n0 = fmaxf(m0, sl2 * xgroup_max(c0m));
                 const float n1 = fmaxf(m1, sl2 * xgroup_max(c1m));
-                if (__ballot((n0 > m0 + 32.f) | (n1 > m1 + 32.f))) {
+                {
                     const float a0 = __builtin_amdgcn_exp2f(m0 - n0), a1 = __builtin_amdgcn_exp2f(m1 - n1);
                     m0 = n0; m1 = n1;
                     Zf0 *= a0; dz0 *= a0; Zf1 *= a1; dz1 *= a1;

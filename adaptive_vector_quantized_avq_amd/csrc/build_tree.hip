@@ -59,39 +59,60 @@ __device__ __forceinline__ const T *tree_row(const T *parents, const T *children
 // codeword (else r_t = 0).  Comparing distances as
 // ||c - r||^2 - 2 (k - r).(c - r) changes no distance but makes the fp32
 // rounding scale with the codebook's spread rather than its offset from the
-// origin.  One thread per (head, coordinate).
+// origin.  One 256-thread work-group per (head, coordinate); the fp64 sum is
+// taken in a fixed order (per-thread strided partials, then a tree), so the
+// frame is the same on every run.
+constexpr int kFrameThreads = 256;
 template <typename T>
-__global__ void tree_frame_kernel(const T *__restrict__ parents, const T *__restrict__ children,
-                                  const T *__restrict__ leaves, int H, int M0, int C, int d,
-                                  float *__restrict__ frame)
+__global__ __launch_bounds__(kFrameThreads) void tree_frame_kernel(const T *__restrict__ parents,
+                                                                   const T *__restrict__ children,
+                                                                   const T *__restrict__ leaves, int H, int M0,
+                                                                   int C, int d, float *__restrict__ frame)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (int64_t)H * d) return;
-    const int h = (int)(i / d), t = (int)(i % d);
+    __shared__ double rs[kFrameThreads];
+    __shared__ float rlo[kFrameThreads], rhi[kFrameThreads];
+    __shared__ int rok[kFrameThreads];
+    const int h = blockIdx.x / d, t = blockIdx.x % d, tid = threadIdx.x;
     const int S = M0 * (1 + C + (leaves ? C * C : 0));
     auto coord = [&](int j) -> float { return to_float(tree_row(parents, children, leaves, h, M0, C, d, j)[t]); };
     double s = 0.0;
     float lo = INFINITY, hi = -INFINITY;
-    for (int j = 0; j < S; ++j) {
+    for (int j = tid; j < S; j += kFrameThreads) {
         const float c = coord(j);
         s += (double)c;
         lo = fminf(lo, c);
         hi = fmaxf(hi, c);
     }
-    const float mu = (float)(s / (double)S);
-    const float spread = fmaxf(hi - mu, mu - lo);
-    float r = fabsf(mu) > 2.f * spread ? coarse3(mu) : 0.f;
+    rs[tid] = s;
+    rlo[tid] = lo;
+    rhi[tid] = hi;
+    __syncthreads();
+    for (int w = kFrameThreads / 2; w >= 1; w >>= 1) {
+        if (tid < w) {
+            rs[tid] += rs[tid + w];
+            rlo[tid] = fminf(rlo[tid], rlo[tid + w]);
+            rhi[tid] = fmaxf(rhi[tid], rhi[tid + w]);
+        }
+        __syncthreads();
+    }
+    const float mu = (float)(rs[0] / (double)S);
+    const float spread = fmaxf(rhi[0] - mu, mu - rlo[0]);
+    const float r = fabsf(mu) > 2.f * spread ? coarse3(mu) : 0.f;
+    int ok = 1;
     if (r != 0.f) {   // c - r must be exact in the storage type for every codeword
-        for (int j = 0; j < S; ++j) {
+        for (int j = tid; j < S; j += kFrameThreads) {
             const double dl = (double)coord(j) - (double)r;   // exact in fp64
             const float df = (float)dl;
-            if (!((double)df == dl && exact_in<T>(df))) {
-                r = 0.f;
-                break;
-            }
+            ok &= ((double)df == dl && exact_in<T>(df)) ? 1 : 0;
         }
     }
-    frame[i] = r;
+    rok[tid] = ok;
+    __syncthreads();
+    for (int w = kFrameThreads / 2; w >= 1; w >>= 1) {
+        if (tid < w) rok[tid] &= rok[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) frame[blockIdx.x] = rok[0] ? r : 0.f;
 }
 
 // one thread per stored codeword row, in slot order (tree_row); norms are
@@ -125,7 +146,7 @@ static hipError_t launch_tree_t(const void *children, int H, int M0, int C, int 
     hipLaunchKernelGGL(tree_parents_kernel<T>, dim3((unsigned)((np + threads - 1) / threads)),
                        dim3(threads), 0, stream, (const T *)children, H, M0, C, d, (T *)parents);
     const int64_t nf = (int64_t)H * d;
-    hipLaunchKernelGGL(tree_frame_kernel<T>, dim3((unsigned)((nf + 63) / 64)), dim3(64), 0, stream,
+    hipLaunchKernelGGL(tree_frame_kernel<T>, dim3((unsigned)nf), dim3(kFrameThreads), 0, stream,
                        (const T *)parents, (const T *)children, (const T *)nullptr, H, M0, C, d, frame);
     const int64_t nr = (int64_t)H * M0 * (1 + C);
     hipLaunchKernelGGL(tree_sqnorm_kernel<T>, dim3((unsigned)((nr + threads - 1) / threads)),
@@ -155,7 +176,7 @@ static hipError_t launch_tree3_t(const void *leaves, int H, int M0, int C, int d
     hipLaunchKernelGGL(tree_parents_kernel<T>, dim3((unsigned)((n0 + threads - 1) / threads)), dim3(threads), 0,
                        stream, (const T *)leaves, H, M0, C * C, d, (T *)level0);
     const int64_t nf = (int64_t)H * d;
-    hipLaunchKernelGGL(tree_frame_kernel<T>, dim3((unsigned)((nf + 63) / 64)), dim3(64), 0, stream,
+    hipLaunchKernelGGL(tree_frame_kernel<T>, dim3((unsigned)nf), dim3(kFrameThreads), 0, stream,
                        (const T *)level0, (const T *)level1, (const T *)leaves, H, M0, C, d, frame);
     const int64_t nr = (int64_t)H * M0 * (1 + C + C * C);
     hipLaunchKernelGGL(tree_sqnorm_kernel<T>, dim3((unsigned)((nr + threads - 1) / threads)), dim3(threads), 0,

@@ -20,21 +20,28 @@
 
 namespace avq {
 
-// Stable counting sort of one chunk's keys by group of children.  One wave
-// per (chunk, b*h); keys that stayed at their root are left out.  A list
-// entry is key | (child mod 256) << 24, the form the refinement kernel reads
-// (it needs the child only relative to its group's first child).
-__global__ __launch_bounds__(64) void bucket_children_kernel(const int32_t *__restrict__ leaf, int N, int M0,
-                                                             int C, int group, int ngroups, int nbits, int nchunks,
-                                                             int32_t *__restrict__ sorted, int2 *__restrict__ seg,
-                                                             int32_t *__restrict__ cmax)
+// Stable counting sort of one chunk's keys by group of children.  Four
+// waves per (chunk, b*h), each over a quarter of the chunk's keys in key
+// order; keys that stayed at their root are left out.  A list entry is
+// key | (child mod 256) << 24, the form the refinement kernel reads (it
+// needs the child only relative to its group's first child).  A key's
+// position: its group's start, plus that group's keys in earlier waves,
+// plus those earlier in its own wave (same-group lanes matched with one
+// ballot per bit of the group index).
+constexpr int kBucketWaves = 4;
+__global__ __launch_bounds__(64 * kBucketWaves) void bucket_children_kernel(
+    const int32_t *__restrict__ leaf, int N, int M0, int C, int group, int ngroups, int nbits, int nchunks,
+    int32_t *__restrict__ sorted, int2 *__restrict__ seg, int32_t *__restrict__ cmax)
 {
-    extern __shared__ int cnt[];   // [ngroups]: counts, then running positions
-    const int chunk = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+    extern __shared__ int wcnt[];   // [kBucketWaves][ngroups] counts, then running positions; [ngroups] starts
+    int *start = wcnt + kBucketWaves * ngroups;
+    const int chunk = blockIdx.x, bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t head = (int64_t)bh * N;
     const int key0 = chunk * kAssignChunk, nk = min(kAssignChunk, N - key0);
     const int n1 = M0 * C;
-    for (int g = lane; g < ngroups; g += 64) cnt[g] = 0;
+    constexpr int KPW = kAssignChunk / kBucketWaves;   // keys per wave
+    for (int g = tid; g < kBucketWaves * ngroups; g += 64 * kBucketWaves) wcnt[g] = 0;
     __syncthreads();
 
     // child reached by key x of the chunk, -1 for a key that stayed at its root
@@ -53,47 +60,68 @@ __global__ __launch_bounds__(64) void bucket_children_kernel(const int32_t *__re
         }
         return m;
     };
-    const int rounds = (nk + 63) / 64;
-    for (int r = 0; r < rounds; ++r) {   // counts per group
-        const int c = child_of(64 * r + lane);
+    int *mine = wcnt + wave * ngroups;
+    for (int r = 0; r < KPW / 64; ++r) {   // this wave's counts per group
+        const int c = child_of(wave * KPW + 64 * r + lane);
         const bool v = c >= 0;
         const int gi = v ? c / group : 0;
         const unsigned long long m = same_group(v, gi);
-        if (v && mbcnt(m) == 0) cnt[gi] += __popcll(m);   // one lane per group
-        __syncthreads();
+        if (v && mbcnt(m) == 0) mine[gi] += __popcll(m);   // one lane per group
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    int carry = 0, most = 0;   // exclusive scan -> the chunk's segment table
-    for (int base = 0; base < ngroups; base += 64) {
-        const int g = base + lane;
-        const int v = g < ngroups ? cnt[g] : 0;
-        most = max(most, v);
-        int inc = v;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(inc, off);
-            if (lane >= off) inc += t;
-        }
-        if (g < ngroups) {
-            const int start = carry + inc - v;
-            seg[((int64_t)bh * ngroups + g) * nchunks + chunk] = make_int2(start, v);
-            cnt[g] = start;
-        }
-        carry += __shfl(inc, 63);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) most = max(most, __shfl_xor(most, off));
-    if (lane < 2) cmax[((int64_t)bh * nchunks + chunk) * 2 + lane] = lane == 0 ? most : 0;
     __syncthreads();
-    for (int r = 0; r < rounds; ++r) {   // stable scatter in key order
-        const int x = 64 * r + lane;
+    for (int g = tid; g < ngroups; g += 64 * kBucketWaves) {   // earlier waves' counts, and totals
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kBucketWaves; ++w) {
+            const int c = wcnt[w * ngroups + g];
+            wcnt[w * ngroups + g] = run;
+            run += c;
+        }
+        start[g] = run;
+    }
+    __syncthreads();
+    if (wave == 0) {   // exclusive scan over the groups -> the chunk's segment table
+        int carry = 0, most = 0;
+        for (int base = 0; base < ngroups; base += 64) {
+            const int g = base + lane;
+            const int v = g < ngroups ? start[g] : 0;
+            most = max(most, v);
+            int inc = v;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int t = __shfl_up(inc, off);
+                if (lane >= off) inc += t;
+            }
+            if (g < ngroups) {
+                const int st = carry + inc - v;
+                seg[((int64_t)bh * ngroups + g) * nchunks + chunk] = make_int2(st, v);
+                start[g] = st;
+            }
+            carry += __shfl(inc, 63);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) most = max(most, __shfl_xor(most, off));
+        if (lane < 2) cmax[((int64_t)bh * nchunks + chunk) * 2 + lane] = lane == 0 ? most : 0;
+    }
+    __syncthreads();
+    for (int r = 0; r < KPW / 64; ++r) {   // stable scatter, this wave's keys in key order
+        const int x = wave * KPW + 64 * r + lane;
         const int c = child_of(x);
         const bool v = c >= 0;
         const int gi = v ? c / group : 0;
         const unsigned long long m = same_group(v, gi);
-        if (v) sorted[head + key0 + cnt[gi] + mbcnt(m)] = (key0 + x) | (int)(((unsigned)c & 0xFFu) << 24);
-        __syncthreads();
-        if (v && mbcnt(m) == 0) cnt[gi] += __popcll(m);
-        __syncthreads();
+        const int before = mbcnt(m);
+        if (v) sorted[head + key0 + start[gi] + mine[gi] + before] = (key0 + x) | (int)(((unsigned)c & 0xFFu) << 24);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (v && before == 0) mine[gi] += __popcll(m);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -125,7 +153,8 @@ hipError_t launch_assign_aggregate3(const void *K, const void *V, const void *le
     int nbits = 1;
     while ((1 << nbits) < ngroups) ++nbits;
     const int nchunks = (N + kAssignChunk - 1) / kAssignChunk;
-    hipLaunchKernelGGL(bucket_children_kernel, dim3(nchunks, B * H), dim3(64), (size_t)ngroups * sizeof(int), stream,
+    hipLaunchKernelGGL(bucket_children_kernel, dim3(nchunks, B * H), dim3(64 * kBucketWaves),
+                       (size_t)(kBucketWaves + 1) * ngroups * sizeof(int), stream,
                        (const int32_t *)lf, N, M0, C, group, ngroups, nbits, nchunks, ws.sorted, ws.seg, ws.cmax);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
