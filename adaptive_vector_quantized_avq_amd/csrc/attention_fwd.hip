@@ -25,7 +25,8 @@
 // contraction index permuted to match, see perm32).
 //
 // Per step:
-//   parent pass  s = C_j . q over the M0 parents, shift m = max_j scale*s,
+//   parent pass  s = C_j . q over the M0 parents, shift m = max_j scale*s
+//                over the parents that hold keys (n_j > 0),
 //                E = exp2(scale*log2(e)*s - m'), Z = sum_j E n_j,
 //                X^T = Vbar^T E^T ("Tiled VQ-attention");
 //   importance   w_j = n_j sum_i E_ij / Z_i: reduced over the 16 queries of
@@ -64,22 +65,25 @@ struct AttnLds {
 // roots), rounded up to whole chunks of 32
 __host__ __device__ inline int attn_cands(int P, int C) { return (P * C + 31) & ~31; }
 
+// (nwave waves of kQPW queries per work-group step cover nwave * kQPW / tile
+// tiles; each tile keeps one selection)
 template <typename T, int D, bool VT_LDS>
-__host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave, int C = 0, bool three_level = false)
+__host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave, int tile, int C = 0, bool three_level = false)
 {
     const int M0p = padded_parents(M0);
+    const int ntile = nwave * kQPW > tile ? nwave * kQPW / tile : 1;
     AttnLds L;
     size_t o = 0;
     L.ps = o;  o += (size_t)M0p * (D + 8) * sizeof(T);
     L.vt = o;  if (VT_LDS) o += (size_t)D * (M0p + 8) * sizeof(T);
     L.np = o;  o += (size_t)M0p * 4;
     L.wp = o;  o += (size_t)2 * nwave * M0p * 4;
-    L.sel = o; o += (size_t)nwave * ((P + 3) & ~3) * 4;
+    L.sel = o; o += (size_t)ntile * ((P + 3) & ~3) * 4;
     L.wp2 = L.wp;
     L.sel2 = o;
     L.wp2_shared = true;
     if (three_level) {
-        o += (size_t)nwave * ((P + 3) & ~3) * 4;
+        o += (size_t)ntile * ((P + 3) & ~3) * 4;
         L.wp2_shared = attn_cands(P, C) <= M0p;
         if (!L.wp2_shared) {
             L.wp2 = o;
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     constexpr int LC = CC == 2 ? 1 : CC == 4 ? 2 : CC == 8 ? 3 : 4;
     constexpr int SCH = attn_super_chunks<T, D>();
     const int selStride = (P + 3) & ~3;
-    const AttnLds L = attn_lds<T, D, VT_LDS>(M0, P, NWV, CC, L3);
+    const AttnLds L = attn_lds<T, D, VT_LDS>(M0, P, NWV, 1 << ltile, CC, L3);
     T *Ps = reinterpret_cast<T *>(smem + L.ps);
     T *Vt = reinterpret_cast<T *>(smem + L.vt);
     float *nP = reinterpret_cast<float *>(smem + L.np);
@@ -275,12 +279,26 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const float *gnp = reinterpret_cast<const float *>(pk + PL.gn);
 
     // ---- stage the head's parents, parent value sums and counts once.
-    // Padding rows (M0 <= j < M0p) repeat parent 0: their logit is one of the
-    // real ones (the shift is unchanged), and their count and value sum are
-    // zero, so they add nothing to Z, X or the importance.
+    // A row whose parent holds no key -- an empty parent, or a padding row
+    // (M0 <= j < M0p) -- is staged as a copy of the first parent that does,
+    // with its own count and value sum, which are zero: its logit is one of
+    // the real ones, so the shift is the largest logit over the parents that
+    // hold keys (an empty codeword far above them cannot push every weight
+    // to zero), and it adds nothing to Z, X or the importance.
+    int j0 = 0;   // first parent with keys (N >= 1: there is one)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        const unsigned long long m = __ballot(j < M0 && pnp[j < M0 ? j : 0] > 0.f);
+        if (m) {
+            j0 = 64 * i + __ffsll((long long)m) - 1;
+            break;
+        }
+    }
     for (int e = tid * 8; e < M0p * D; e += 64 * NWV * 8) {
         const int r = e / D, c = e % D;
-        store_frag(Ps + r * LDP + c, load_frag(parents + ((size_t)h * M0 + (r < M0 ? r : 0)) * D + c));
+        const int src = r < M0 && pnp[r] > 0.f ? r : j0;
+        store_frag(Ps + r * LDP + c, load_frag(parents + ((size_t)h * M0 + src) * D + c));
     }
     if (VT_LDS) {
         for (int e = tid * 8; e < D * M0p; e += 64 * NWV * 8)
@@ -296,19 +314,41 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const int PC = P * CC;
     const int PCr = attn_cands(P, CC);
 
+    // query fragments of a step (queries past N read the last query; never
+    // stored).  For bf16 two-level trees at d = 64 the next step's are
+    // requested at the start of the current one, so that their latency is
+    // hidden behind a whole step (the other instances have no registers to
+    // spare for them).
+    constexpr bool kPrefetchQ = D == 64 && sizeof(T) == 2 && CC > 0 && !L3;
+    auto load_q_at = [&](int st_, Frag<T> (&fa)[KS], Frag<T> (&fb)[KS]) {
+        const int a0 = st_ * STEP + kQPW * w + i16, a1 = a0 + 16;
+        const T *qra = Qh + (size_t)min(a0, N - 1) * D + 8 * g, *qrb = Qh + (size_t)min(a1, N - 1) * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            fa[ks] = load_frag(qra + 32 * ks);
+            fb[ks] = load_frag(qrb + 32 * ks);
+        }
+    };
+    Frag<T> qa[KS], qb[KS], qna[KS], qnb[KS];
+    if (kPrefetchQ && slice < nsteps) load_q_at(slice, qna, qnb);
     int buf = 0;
     for (int st = slice; st < nsteps; st += per_bh, buf ^= 1) {
         const int q0 = st * STEP + kQPW * w + i16, q1 = q0 + 16;
         const bool v0 = q0 < N, v1 = q1 < N;
-        // query fragments (queries past N read the last query; never stored)
-        Frag<T> qa[KS], qb[KS];
         auto load_q = [&]() {
-            const T *qra = Qh + (size_t)min(q0, N - 1) * D + 8 * g, *qrb = Qh + (size_t)min(q1, N - 1) * D + 8 * g;
+            if constexpr (kPrefetchQ) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                qa[ks] = load_frag(qra + 32 * ks);
-                qb[ks] = load_frag(qrb + 32 * ks);
-                if (neg) {
+                for (int ks = 0; ks < KS; ++ks) {
+                    qa[ks] = qna[ks];
+                    qb[ks] = qnb[ks];
+                }
+                if (st + per_bh < nsteps) load_q_at(st + per_bh, qna, qnb);
+            } else {
+                load_q_at(st, qa, qb);
+            }
+            if (neg) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
                     qa[ks] = negate(qa[ks]);
                     qb[ks] = negate(qb[ks]);
                 }
@@ -755,11 +795,11 @@ int attention_child_chunk(int d, int M0, int C, int P, int tile, int dtype, bool
     if (tile != 32 && tile != 64 && tile != 128 && tile != 256) return 0;
     size_t lds;
     if (dtype == 1)
-        lds = d == 64 ? attn_lds<bf16, 64, true>(M0, P, attn_waves<64, true>(tile), C, three_level).total
-                      : attn_lds<bf16, 128, true>(M0, P, attn_waves<128, true>(tile), C, three_level).total;
+        lds = d == 64 ? attn_lds<bf16, 64, true>(M0, P, attn_waves<64, true>(tile), tile, C, three_level).total
+                      : attn_lds<bf16, 128, true>(M0, P, attn_waves<128, true>(tile), tile, C, three_level).total;
     else
-        lds = d == 64 ? attn_lds<float, 64, true>(M0, P, attn_waves<64, true>(tile), C, three_level).total
-                      : attn_lds<float, 128, false>(M0, P, attn_waves<128, false>(tile), C, three_level).total;
+        lds = d == 64 ? attn_lds<float, 64, true>(M0, P, attn_waves<64, true>(tile), tile, C, three_level).total
+                      : attn_lds<float, 128, false>(M0, P, attn_waves<128, false>(tile), tile, C, three_level).total;
     return lds <= 160 * 1024 ? 32 : 0;
 }
 
@@ -797,7 +837,7 @@ template <typename T, int D, bool VT, int NRB, int CC, int NWV, bool L3>
 static hipError_t launch_attn_k(const AttnArgs &a, hipStream_t stream)
 {
     allow_full_lds<attention_kernel<T, D, VT, NRB, CC, NWV, L3>>();
-    const size_t lds = attn_lds<T, D, VT>(a.M0, a.P, NWV, CC, L3).total;
+    const size_t lds = attn_lds<T, D, VT>(a.M0, a.P, NWV, a.tile, CC, L3).total;
     const int ntiles = (a.N + a.tile - 1) / a.tile;
     const int nsteps = (a.N + NWV * kQPW - 1) / (NWV * kQPW);
     const int BH = a.B * a.H;
@@ -847,7 +887,7 @@ static hipError_t launch_attn_nrb(const AttnArgs &a, hipStream_t stream)
 template <typename T, int D, bool VT>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t stream)
 {
-    if (attn_lds<T, D, VT>(a.M0, a.P, attn_waves<D, VT>(a.tile), a.C, a.leaves != nullptr).total > 160 * 1024)
+    if (attn_lds<T, D, VT>(a.M0, a.P, attn_waves<D, VT>(a.tile), a.tile, a.C, a.leaves != nullptr).total > 160 * 1024)
         return hipErrorInvalidConfiguration;
     switch (padded_parents(a.M0)) {
     case 32: return launch_attn_nrb<T, D, VT, 2>(a, stream);

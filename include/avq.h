@@ -225,9 +225,8 @@ size_t avq_attention_workspace_size(int B, int H, int M0, int C, int d, int dtyp
  *   workspace  device buffer of at least avq_attention_workspace_size(...)
  *              bytes, 256-byte aligned, used only during this call's
  *              kernels (not shared with a concurrent call); caller-owned.
- *   Returns AVQ_ERR_UNSUPPORTED if the codebook and tile do not fit the
- *   kernel's 160 KB of LDS: only fp32 with M0 near 256, 256-query tiles and
- *   P above ~160 (d = 64) or ~224 (d = 128).
+ *   Every supported shape fits the kernel's 160 KB of LDS (a shape that did
+ *   not would return AVQ_ERR_UNSUPPORTED).
  */
 int avq_attention_fwd(const void *Q, const void *parents, const void *children,
                       const float *vsum, const int32_t *count, int B, int H, int N,

@@ -198,6 +198,10 @@ EDGE = [
     ("bf16", 128, 129, 16, 20, 64, 777, True),
     # fp32 at d = 128 with 256-query tiles (8 waves, value sums from L2)
     ("f32", 128, 200, 4, 8, 256, 1100, False),
+    # fp32, 256 parents, 256-query tiles and a large P: the largest LDS
+    # footprints of the two-level kernel (one selection per tile)
+    ("f32", 64, 256, 8, 200, 256, 1100, False),
+    ("f32", 128, 256, 4, 240, 256, 900, False),
     # fewer non-empty parents than P (5 keys, 40 parents, P = 12): the top-P
     # threshold is 0 and the empty parents tie there, lowest indices first
     ("bf16", 64, 40, 4, 12, 64, 5, False),
@@ -250,6 +254,40 @@ def test_negative_and_unit_scale(avq, scale):
     inp = synth.generate("vit-b", B=1, H=2, N=1500, M0=40, C=8, P=6, T=64, seed=31)
     inp.scale = scale
     check_all(avq, inp)
+
+
+def test_empty_parent_far_above_the_others(avq):
+    """A parent that holds no key, whose logits lie over 300 (log2 units) above
+    every other parent's: past fp32's exponent range, so a shift taken over
+    all parents would send every weight, and Z, to zero.  The shift is the
+    largest logit over the parents that hold keys; the empty parent adds
+    nothing to Z, X or the importance (the oracle's fp64 shift is the plain
+    maximum, which changes nothing mathematically)."""
+    inp = synth.generate("vit-b", B=1, H=1, N=1000, M0=16, C=4, P=3, T=64, seed=77)
+    M0, C = inp.M0, inp.C
+    ch = inp.f64("children")
+    old = ch.copy()
+    ch[:, 0] = ch[:, 0] - ch[:, 0].mean(axis=1, keepdims=True)
+    ch[:, 0, :, 0] += 60.0                              # parent 0 at 60 e_0
+    inp.children = synth.to_storage(ch, inp.dtype)
+    # keys drawn from parent 0's leaves move to parent 1's first child
+    K = inp.f64("K")
+    leaf = inp.true_leaf
+    mv = (leaf >= M0) & ((leaf - M0) // C == 0)
+    src = old[0].reshape(M0 * C, -1)[np.where(mv, leaf - M0, 0)]
+    K = np.where(mv[..., None], K - src + old[0, 1, 0], K)
+    inp.K = synth.to_storage(K, inp.dtype)
+    inp.true_leaf = np.where(mv, M0 + C, leaf).astype(np.int32)
+    Q = inp.f64("Q")
+    Q[..., 0] += 8.0
+    inp.Q = synth.to_storage(Q, inp.dtype)
+    inp.scale = 1.0
+    Q64, ch64 = inp.f64("Q"), inp.f64("children")
+    par64, _ = oracle.build_tree(ch64, inp.dtype)
+    sp = np.einsum("bhnd,hmd->bhnm", Q64, par64) / np.log(2.0)
+    assert (sp[..., 0] - sp[..., 1:].max(axis=-1)).min() > 130.0
+    r = check_all(avq, inp)
+    assert r["count"][..., 0].sum() == 0 and np.isfinite(r["g"]["Y"]).all()
 
 
 def test_child_logits_far_above_the_shift(avq):
