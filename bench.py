@@ -211,7 +211,9 @@ def measure_peaks(torch, dev):
     for name, kind, iters, per in (("mfma_bf16_TFLOPs", 0, 4000, 16 * 16 * 32 * 2 * 8 / 64),
                                    ("fma_f32_TFLOPs", 1, 20000, 2 * 8),
                                    ("exp_f32_per_s", 2, 20000, 8)):
-        for rep in range(2):   # the first launch warms up
+        # the launches before the timed one bring the clocks up to their
+        # sustained level (~50 ms of load)
+        for rep in range(16):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             rc = lib.avq_probe_launch(kind, blocks, iters, ctypes.c_void_p(outb.data_ptr()), stream)
@@ -229,8 +231,12 @@ def measure_peaks(torch, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # the GPU's clocks ramp up over tens of milliseconds of sustained load
+    # (a probe's MFMA rate climbs from ~1.8 to ~2.2 PFLOP/s over ~20 ms of
+    # back-to-back launches): 300 untimed steps (~55 ms at long-64k) reach
+    # the steady state the timed steps then measure
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="long-64k")
     ap.add_argument("--P", type=int, default=None)
     ap.add_argument("--sets", type=int, default=4)
