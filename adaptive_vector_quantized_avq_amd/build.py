@@ -79,7 +79,10 @@ def build(verbose: bool = True) -> str:
     # AVQ library does not contain them
     psrc = os.path.join(PROBES, "peaks.hip")
     ptmp = PROBE_LIB + f".tmp{os.getpid()}"
-    cmd = [_hipcc(), *COMMON, "-shared", psrc, "-o", ptmp]
+    # (MFMA results in VGPRs: with accumulator registers the compiler copies
+    # the eight accumulators through VGPRs every iteration, and the MFMA
+    # probe then measures those copies)
+    cmd = [_hipcc(), *COMMON, "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-shared", psrc, "-o", ptmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("probe library build failed:\n" + r.stdout + r.stderr)

@@ -200,10 +200,11 @@ def copy_probe(torch, dev, nbytes=256 << 20, launches=5):
 def measure_peaks(torch, dev):
     """Rates measured on this GPU: bf16 MFMA (TFLOP/s), fp32 FMA (TFLOP/s),
     v_exp_f32 (exponentials/s), and a 1 GiB device copy (GB/s, read + write).
-    4096 blocks of 256 threads: 16 waves per CU, 4 per SIMD."""
+    Sixteen 256-thread blocks per CU (more waves than a SIMD holds at once),
+    eight independent chains per lane."""
     import ctypes
     lib = _probe_lib()
-    blocks = 4096
+    blocks = 16 * torch.cuda.get_device_properties(dev).multi_processor_count
     outb = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     res = {}
