@@ -186,8 +186,8 @@ template <> __device__ __forceinline__ Frag<float> frag_from8<float>(const float
 
 // y[16*db + r] = x[db][r] * s for r < 4, as one 8-byte (bf16) or 16-byte
 // (fp32) store per db
-template <typename T, int DB> __device__ __forceinline__ void store_row4(T *y, const f32x4 (&x)[DB], float s);
-template <> __device__ __forceinline__ void store_row4<bf16, 4>(bf16 *y, const f32x4 (&x)[4], float s)
+template <typename T, int DB> __device__ __forceinline__ void store_row4(T *y, const f32x4 *x, float s);
+template <> __device__ __forceinline__ void store_row4<bf16, 4>(bf16 *y, const f32x4 *x, float s)
 {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -197,7 +197,7 @@ template <> __device__ __forceinline__ void store_row4<bf16, 4>(bf16 *y, const f
         *reinterpret_cast<bf16x4 *>(y + 16 * db) = v;
     }
 }
-template <> __device__ __forceinline__ void store_row4<bf16, 8>(bf16 *y, const f32x4 (&x)[8], float s)
+template <> __device__ __forceinline__ void store_row4<bf16, 8>(bf16 *y, const f32x4 *x, float s)
 {
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
@@ -207,12 +207,12 @@ template <> __device__ __forceinline__ void store_row4<bf16, 8>(bf16 *y, const f
         *reinterpret_cast<bf16x4 *>(y + 16 * db) = v;
     }
 }
-template <> __device__ __forceinline__ void store_row4<float, 4>(float *y, const f32x4 (&x)[4], float s)
+template <> __device__ __forceinline__ void store_row4<float, 4>(float *y, const f32x4 *x, float s)
 {
 #pragma unroll
     for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4 *>(y + 16 * db) = x[db] * s;
 }
-template <> __device__ __forceinline__ void store_row4<float, 8>(float *y, const f32x4 (&x)[8], float s)
+template <> __device__ __forceinline__ void store_row4<float, 8>(float *y, const f32x4 *x, float s)
 {
 #pragma unroll
     for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4 *>(y + 16 * db) = x[db] * s;
@@ -277,6 +277,17 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const T *Lh = L3 ? leaves + (size_t)h * M0 * CC * CC * D : nullptr;
     const T *gvt = reinterpret_cast<const T *>(pk + PL.gvt);
     const float *gnp = reinterpret_cast<const float *>(pk + PL.gn);
+    // Two-level trees with 16-bit operands form the output's denominators on
+    // the matrix cores, from the counts split into three exact bf16 parts
+    // (pack rows hi, mid, lo) and the same bf16 weights as the value sums, so
+    // that the weights' rounding cancels in Y = X / Z; X gains a block whose
+    // rows 0-2 collect them.  (The parent-level Z of the importance stays the
+    // fp32 sum.)
+    constexpr bool ZB = sizeof(T) == 2 && !L3;
+    constexpr int DX = DB + (ZB ? 1 : 0);
+    const T *pzp = reinterpret_cast<const T *>(pk + PL.pz);
+    const T *czp = reinterpret_cast<const T *>(pk + PL.cz);
+    const int zrow = i16 < 3 ? i16 : 3;   // count operand row of this lane (row 3: zero)
 
     // ---- stage the head's parents, parent value sums and counts once.
     // A row whose parent holds no key -- an empty parent, or a padding row
@@ -314,41 +325,19 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const int PC = P * CC;
     const int PCr = attn_cands(P, CC);
 
-    // query fragments of a step (queries past N read the last query; never
-    // stored).  For bf16 two-level trees at d = 64 the next step's are
-    // requested at the start of the current one, so that their latency is
-    // hidden behind a whole step (the other instances have no registers to
-    // spare for them).
-    constexpr bool kPrefetchQ = D == 64 && sizeof(T) == 2 && CC > 0 && !L3;
-    auto load_q_at = [&](int st_, Frag<T> (&fa)[KS], Frag<T> (&fb)[KS]) {
-        const int a0 = st_ * STEP + kQPW * w + i16, a1 = a0 + 16;
-        const T *qra = Qh + (size_t)min(a0, N - 1) * D + 8 * g, *qrb = Qh + (size_t)min(a1, N - 1) * D + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            fa[ks] = load_frag(qra + 32 * ks);
-            fb[ks] = load_frag(qrb + 32 * ks);
-        }
-    };
-    Frag<T> qa[KS], qb[KS], qna[KS], qnb[KS];
-    if (kPrefetchQ && slice < nsteps) load_q_at(slice, qna, qnb);
     int buf = 0;
     for (int st = slice; st < nsteps; st += per_bh, buf ^= 1) {
         const int q0 = st * STEP + kQPW * w + i16, q1 = q0 + 16;
         const bool v0 = q0 < N, v1 = q1 < N;
+        // query fragments (queries past N read the last query; never stored)
+        Frag<T> qa[KS], qb[KS];
         auto load_q = [&]() {
-            if constexpr (kPrefetchQ) {
+            const T *qra = Qh + (size_t)min(q0, N - 1) * D + 8 * g, *qrb = Qh + (size_t)min(q1, N - 1) * D + 8 * g;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    qa[ks] = qna[ks];
-                    qb[ks] = qnb[ks];
-                }
-                if (st + per_bh < nsteps) load_q_at(st + per_bh, qna, qnb);
-            } else {
-                load_q_at(st, qa, qb);
-            }
-            if (neg) {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
+            for (int ks = 0; ks < KS; ++ks) {
+                qa[ks] = load_frag(qra + 32 * ks);
+                qb[ks] = load_frag(qrb + 32 * ks);
+                if (neg) {
                     qa[ks] = negate(qa[ks]);
                     qb[ks] = negate(qb[ks]);
                 }
@@ -443,12 +432,13 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
             *reinterpret_cast<f32x4 *>(Wp + (buf * NWV + w) * M0p + 16 * (i16 >> (4 - LG)) + 4 * g) = part;
         }
         // X^T = Vbar^T E^T over the parents
-        f32x4 X0[DB], X1[DB];
+        f32x4 X0[DX], X1[DX];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < DX; ++db) {
             X0[db] = f32x4{0.f, 0.f, 0.f, 0.f};
             X1[db] = X0[db];
         }
+        auto pz_frag = [&](int s_) -> Frag<T> { return load_frag(pzp + zrow * M0p + 32 * s_ + 8 * g); };
         // (value-sum fragments of the next 32 parents are read while the
         // current ones' MFMAs run)
         // From global memory the fragments are the same in every step; the
@@ -470,6 +460,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
 #pragma unroll
                     for (int db = 0; db < DB; ++db) va[(s + 1) & 1][db] = vt_frag(s + 1, db);
                 }
+                if constexpr (ZB) {
+                    const Frag<T> z = pz_frag(s);
+                    X0[DB] = mma(z, E0[s], X0[DB]);
+                    X1[DB] = mma(z, E1[s], X1[DB]);
+                }
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     X0[db] = mma(va[s & 1][db], E0[s], X0[db]);
@@ -484,6 +479,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                     const Frag<T> a = vt_frag(s, db);
                     X0[db] = mma(a, E0[s], X0[db]);
                     X1[db] = mma(a, E1[s], X1[db]);
+                }
+                if constexpr (ZB) {
+                    const Frag<T> a = pz_frag(s);
+                    X0[DB] = mma(a, E0[s], X0[DB]);
+                    X1[DB] = mma(a, E1[s], X1[DB]);
                 }
             }
         }
@@ -588,7 +588,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
         // `nxt` while this one computes
         auto super_chunk = [&](const Level &lv, int c0, const CwBuf &cw, CwBuf &nxt, bool more) {
             f32x4 nA[SCH], nB[SCH];
-            Frag<T> vc[SCH][DB];
+            Frag<T> vc[SCH][DX];
 #pragma unroll
             for (int q = 0; q < SCH; ++q) {
                 const int ph0 = c0 + 32 * q + 8 * g;
@@ -601,6 +601,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                     const T *vp = lv.vt + ((size_t)pp * D + i16) * CC + (ph0 & (CC - 1));
 #pragma unroll
                     for (int db = 0; db < DB; ++db) vc[q][db] = load_frag(vp + (size_t)16 * db * CC);
+                    if constexpr (ZB)   // count parts of the 8 children (lanes past row 2: the zero entry)
+                        vc[q][DB] = load_frag(czp + ((size_t)(i16 < 3 ? pp : lv.zero) * 3 + (i16 < 3 ? i16 : 0)) * CC +
+                                              (ph0 & (CC - 1)));
                 } else {
                     int pk8[8];   // slot (parent index, or the zero entry) of children ph0..ph0+7
 #pragma unroll
@@ -621,6 +624,14 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                         for (int k = 0; k < 8; ++k)
                             v[k] = to_float(lv.vt[((size_t)pk8[k] * D + 16 * db + i16) * CC + ((ph0 + k) & (CC - 1))]);
                         vc[q][db] = frag_from8<T>(v);
+                    }
+                    if constexpr (ZB) {
+                        float v[8];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            v[k] = to_float(czp[((size_t)(i16 < 3 ? pk8[k] : lv.zero) * 3 + (i16 < 3 ? i16 : 0)) * CC +
+                                                ((ph0 + k) & (CC - 1))]);
+                        vc[q][DB] = frag_from8<T>(v);
                     }
                 }
             }
@@ -654,7 +665,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                     m0 = n0; m1 = n1;
                     Zf0 *= a0; dz0 *= a0; Zf1 *= a1; dz1 *= a1;
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) { X0[db] *= a0; X1[db] *= a1; }
+                    for (int db = 0; db < DX; ++db) { X0[db] *= a0; X1[db] *= a1; }
                 }
             }
 #pragma unroll
@@ -695,12 +706,14 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                     dB0[r] = __builtin_amdgcn_exp2f(fmaf(SB0[q][r], sl2, -m0)) - eB0[r >> 1];
                     dA1[r] = __builtin_amdgcn_exp2f(fmaf(SA1[q][r], sl2, -m1)) - eA1[r >> 1];
                     dB1[r] = __builtin_amdgcn_exp2f(fmaf(SB1[q][r], sl2, -m1)) - eB1[r >> 1];
-                    dz0 = fmaf(dA0[r], nA[q][r], fmaf(dB0[r], nB[q][r], dz0));
-                    dz1 = fmaf(dA1[r], nA[q][r], fmaf(dB1[r], nB[q][r], dz1));
+                    if constexpr (!ZB) {
+                        dz0 = fmaf(dA0[r], nA[q][r], fmaf(dB0[r], nB[q][r], dz0));
+                        dz1 = fmaf(dA1[r], nA[q][r], fmaf(dB1[r], nB[q][r], dz1));
+                    }
                 }
                 const Frag<T> b0 = pack_frag<T>(dA0, dB0), b1 = pack_frag<T>(dA1, dB1);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
+                for (int db = 0; db < DX; ++db) {
                     X0[db] = mma(vc[q][db], b0, X0[db]);
                     X1[db] = mma(vc[q][db], b1, X1[db]);
                 }
@@ -777,7 +790,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
         }   // CC > 0
 
         // ---- Y = X / Z: lane (g, i) holds dims 16*db + 4g .. +3 of its query
-        const float Z0 = Zf0 + xgroup_sum(dz0), Z1 = Zf1 + xgroup_sum(dz1);
+        // (with ZB the rows hi, mid and lo of the count block are in lane
+        // group 0, and the other lane groups' rows of it are zero)
+        const float Z0 = ZB ? xgroup_sum((X0[DX - 1][0] + X0[DX - 1][1]) + X0[DX - 1][2]) : Zf0 + xgroup_sum(dz0);
+        const float Z1 = ZB ? xgroup_sum((X1[DX - 1][0] + X1[DX - 1][1]) + X1[DX - 1][2]) : Zf1 + xgroup_sum(dz1);
         if (v0) store_row4<T, DB>(Yh + (size_t)q0 * D + 4 * g, X0, __builtin_amdgcn_rcpf(Z0));
         if (v1) store_row4<T, DB>(Yh + (size_t)q1 * D + 4 * g, X1, __builtin_amdgcn_rcpf(Z1));
     }

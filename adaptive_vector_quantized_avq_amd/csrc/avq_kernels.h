@@ -95,12 +95,20 @@ struct AssignWorkspace {
 //                        all zero (read for the padding children of a
 //                        partly filled chunk)
 //   cn  [M0+1][C] float  child counts; entry M0 is all zero
-// and, for a three-level tree, the same two sections one level down (the
-// M0*C children as parents of their C leaves):
+// and, for a two-level tree with 16-bit operands, the counts as matrix-core
+// operands (each count n split exactly into three bf16 parts n = hi + mid +
+// lo, so that a product with a bf16 weight is exact), from which the kernel
+// forms the softmax denominators with the same rounded weights as the value
+// sums:
+//   pz  [4][M0p] bf16    rows hi, mid, lo of the parent counts, columns
+//                        permuted like pvt; row 3 all zero
+//   cz  [M0+1][3][C] bf16  hi, mid, lo of the child counts; entry M0 zero
+// and, for a three-level tree, the same two value/count sections one level
+// down (the M0*C children as parents of their C leaves):
 //   gvt [M0*C+1][D][C] T, gn [M0*C+1][C] float (entry M0*C all zero)
 // with M0p = padded_parents(M0).
 struct PackLayout {
-    size_t pvt, pn, cvt, cn, gvt, gn, bytes;
+    size_t pvt, pn, cvt, cn, pz, cz, gvt, gn, bytes;
 };
 // parents padded to a power of two >= 32, so that the stage-2 kernel can be
 // specialised on the number of 16-row MFMA blocks
@@ -118,6 +126,9 @@ __host__ __device__ inline PackLayout pack_layout(int M0, int C, int D, int esiz
     L.pn = o;  o = align256(o + (size_t)M0p * 4);
     L.cvt = o; o = align256(o + (size_t)(M0 + 1) * D * C * esize);
     L.cn = o;  o = align256(o + (size_t)(M0 + 1) * C * 4);
+    const bool zb = esize == 2 && !three_level;
+    L.pz = o;  o = align256(o + (zb ? (size_t)4 * M0p * 2 : 0));
+    L.cz = o;  o = align256(o + (zb ? (size_t)(M0 + 1) * 3 * C * 2 : 0));
     L.gvt = o; L.gn = o;
     if (three_level) {
         const size_t n1 = (size_t)M0 * C;

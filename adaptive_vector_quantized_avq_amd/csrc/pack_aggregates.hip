@@ -16,6 +16,9 @@
 //        t, children innermost; entry M0 is all zero;
 //   pn   parent counts as fp32 (zero past M0);
 //   cn   child counts as fp32; entry M0 is all zero;
+//   pz, cz  (16-bit operands, two-level trees) the parent and child counts
+//        split into three bf16 parts each (count_part), laid out like pvt
+//        and cvt, for the kernel's denominators on the matrix cores;
 //   and for a three-level tree the same two sections for the children as
 //   parents of the leaves (gvt, gn).
 // The grid is 1-D, with the (b, h) units spread over the XCDs in contiguous
@@ -41,12 +44,23 @@ template <> __device__ __forceinline__ void store8<float>(float *dst, const floa
     *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
-template <int D, int CC, bool L3> __host__ __device__ inline int pack_items(int M0)
+template <int D, int CC, bool L3, bool ZB> __host__ __device__ inline int pack_items(int M0)
 {
     const int NG = CC >= 8 ? CC / 8 : 1;
     const int n1 = M0 * CC;
     return D * (padded_parents(M0) / 8) + (CC > 0 ? (M0 + 1) * D * NG : 0) + padded_parents(M0) +
-           (M0 + 1) * CC + (L3 ? (n1 + 1) * D * NG + (n1 + 1) * CC : 0);
+           (M0 + 1) * CC + (ZB ? 4 * (padded_parents(M0) / 8) + (M0 + 1) * 3 * CC : 0) +
+           (L3 ? (n1 + 1) * D * NG + (n1 + 1) * CC : 0);
+}
+
+// part r (0, 1, 2) of the split of a count n (an integer below 2^21) into
+// three bf16 values that sum to it exactly: hi = n rounded to bf16, mid = the
+// rest rounded, lo = what is left (a small integer, exact in bf16)
+__device__ __forceinline__ float count_part(float n, int r)
+{
+    const float hi = (float)(bf16)n;
+    const float mid = (float)(bf16)(n - hi);
+    return r == 0 ? hi : r == 1 ? mid : n - hi - mid;
 }
 
 // child sums of one level: item (p, t, group of 8 children) of `np1` parents
@@ -69,7 +83,7 @@ __device__ __forceinline__ void pack_child_item(int a, const float *vs, int c0, 
     }
 }
 
-template <typename T, int D, int CC, bool L3>
+template <typename T, int D, int CC, bool L3, bool ZB>
 __global__ __launch_bounds__(kPackThreads) void pack_aggregates_kernel(
     const float *__restrict__ vsum, const int32_t *__restrict__ count, int M0, int nbh, int parts,
     unsigned char *__restrict__ pack)
@@ -121,6 +135,28 @@ __global__ __launch_bounds__(kPackThreads) void pack_aggregates_kernel(
         return;
     }
     a -= (M0 + 1) * CC;
+    if constexpr (ZB) {   // the counts as exact sums of three bf16 parts
+        const int n_pz = 4 * (M0p / 8);
+        if (a < n_pz) {   // parents: rows hi, mid, lo, zero; columns as in pvt
+            const int r = a / (M0p / 8), q8 = a % (M0p / 8);
+            const int base = 32 * (q8 >> 2), q = q8 & 3;
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int j = base + (k < 4 ? 4 * q + k : 16 + 4 * q + (k - 4));
+                v[k] = r < 3 && j < M0 ? count_part((float)cs[j], r) : 0.f;
+            }
+            store8<bf16>(reinterpret_cast<bf16 *>(pk + PL.pz) + (size_t)r * M0p + 8 * q8, v);
+            return;
+        }
+        a -= n_pz;
+        if (a < (M0 + 1) * 3 * CC) {   // children [M0+1][3][CC], entry M0 zero
+            const int p = a / (3 * CC), r = (a / CC) % 3, c = a % CC;
+            reinterpret_cast<bf16 *>(pk + PL.cz)[a] = (bf16)(p < M0 ? count_part((float)cs[M0 + p * CC + c], r) : 0.f);
+            return;
+        }
+        a -= (M0 + 1) * 3 * CC;
+    }
     if constexpr (L3) {   // the leaves' sums and counts, the children as parents
         const int n_gvt = (n1 + 1) * D * NG;
         if (a < n_gvt) {
@@ -137,9 +173,10 @@ template <typename T, int D, int CC, bool L3>
 static hipError_t launch_pack_k(const float *vsum, const int32_t *count, int BH, int M0, void *pack,
                                 hipStream_t stream)
 {
-    const int parts = (pack_items<D, CC, L3>(M0) + kPackThreads - 1) / kPackThreads;
+    constexpr bool ZB = sizeof(T) == 2 && !L3;
+    const int parts = (pack_items<D, CC, L3, ZB>(M0) + kPackThreads - 1) / kPackThreads;
     const int grid = (BH * parts + 7) & ~7;
-    hipLaunchKernelGGL((pack_aggregates_kernel<T, D, CC, L3>), dim3(grid), dim3(kPackThreads), 0, stream, vsum,
+    hipLaunchKernelGGL((pack_aggregates_kernel<T, D, CC, L3, ZB>), dim3(grid), dim3(kPackThreads), 0, stream, vsum,
                        count, M0, BH, parts, (unsigned char *)pack);
     return hipGetLastError();
 }

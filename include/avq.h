@@ -182,7 +182,8 @@ int avq_assign_aggregate_noalloc(const void *K, const void *V, const void *paren
  * avq_attention_fwd needs for this shape (0 if the shape is invalid or
  * unsupported).  The workspace receives the aggregates rearranged as the
  * attention kernel's matrix-core operands (value sums rounded to dtype,
- * counts as fp32); its layout is private to the library.
+ * counts as fp32 and, for bf16, as exact sums of three bf16 parts); its
+ * layout is private to the library.
  */
 size_t avq_attention_workspace_size(int B, int H, int M0, int C, int d, int dtype);
 
@@ -214,7 +215,11 @@ size_t avq_attention_workspace_size(int B, int H, int M0, int C, int d, int dtyp
  *                                     must include its children's)
  *   The aggregates may come from avq_assign_aggregate or from anywhere else
  *   (e.g. the sum of several partial runs); they are read, never written.
- *   The value sums enter the matrix-core products rounded to dtype.
+ *   The value sums enter the matrix-core products rounded to dtype.  For
+ *   bf16 the weights enter them rounded to bf16 as well, and Z in the output
+ *   step is summed from those same rounded weights (the counts split exactly
+ *   into three bf16 parts), so that their rounding cancels in Y; the Z of
+ *   the importance is the fp32 sum.
  *   P          0 <= P <= M0 parents refined per tile
  *   tile       queries per tile
  *   scale      finite softmax scale applied to every logit

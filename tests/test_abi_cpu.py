@@ -49,10 +49,13 @@ def test_abi_version_and_status_strings(lib):
 def test_attention_workspace_size(lib):
     f = lib.avq_attention_workspace_size
     # per (b,h): parent sums [d][256] + counts [256] + child sums [257][d][8] +
-    # counts [257][8] (one all-zero entry), each section 256-byte aligned
+    # counts [257][8] (one all-zero entry), then, for bf16, the counts as
+    # three bf16 parts: parents [4][256], children [257][3][8]; each section
+    # 256-byte aligned
     al = lambda x: (x + 255) // 256 * 256
     per = al(64 * 256 * 2) + al(256 * 4) + al(257 * 64 * 8 * 2) + al(257 * 8 * 4)
-    assert f(1, 8, 256, 8, 64, 1) == 8 * per
+    assert f(1, 8, 256, 8, 64, 1) == 8 * (per + al(4 * 256 * 2) + al(257 * 3 * 8 * 2))
+    assert f(1, 8, 256, 8, 64, 0) == 8 * (al(64 * 256 * 4) + al(256 * 4) + al(257 * 64 * 8 * 4) + al(257 * 8 * 4))
     assert f(1, 1, 300, 8, 64, 1) == 0
     assert f(0, 1, 16, 8, 64, 1) == 0
 
