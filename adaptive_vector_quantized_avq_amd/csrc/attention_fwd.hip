@@ -5,8 +5,10 @@
 // 256-query tiles and for bf16 at d = 128); each wave owns 32 queries as two
 // 16-query MFMA column blocks (each codeword fragment read feeds two MFMAs;
 // one block per wave, at twice the operand traffic per MFMA, measured ~1.6x
-// slower), a work-group step covers NWV*32 queries (whole tiles).  Barriers
-// per step: one after the importance partials, one after the selection.  A
+// slower), a work-group step covers NWV*32 queries (whole tiles).  One
+// barrier per step, after the importance partials: every wave then selects
+// its tile's parents itself (a three-level tree: the tile's first wave, and
+// a second barrier after the selection).  A
 // work-group stages its head's parents, their value sums (transposed) and
 // counts in LDS once; LDS holds nothing else but the per-wave importance
 // partials, so two work-groups share a CU and hide each other's barrier and
@@ -33,8 +35,8 @@
 //                each block with DPP, written per wave to LDS (alternating
 //                between two buffers from step to step), summed over the
 //                tile's waves ("Codeword importance");
-//   top-P        the first wave of each tile selects the tile's P parents
-//                into LDS: exact bisection on the fp32 bit patterns of w
+//   top-P        every wave selects its tile's P parents into its own LDS
+//                slots: exact bisection on the fp32 bit patterns of w
 //                (w >= 0), ties to the lower index ("Child spawning");
 //   correction   the selected parents' children are read straight from
 //                global memory into MFMA operands, 32 children at a time
@@ -68,7 +70,8 @@ __host__ __device__ inline int attn_cands(int P, int C) { return (P * C + 31) & 
 // (nwave waves of kQPW queries per work-group step cover nwave * kQPW / tile
 // tiles; each tile keeps one selection)
 template <typename T, int D, bool VT_LDS>
-__host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave, int tile, int C = 0, bool three_level = false)
+__host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave, int tile, int C = 0, bool three_level = false,
+                                            bool wave_sel = false)
 {
     const int M0p = padded_parents(M0);
     const int ntile = nwave * kQPW > tile ? nwave * kQPW / tile : 1;
@@ -78,7 +81,9 @@ __host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave, int tile, 
     L.vt = o;  if (VT_LDS) o += (size_t)D * (M0p + 8) * sizeof(T);
     L.np = o;  o += (size_t)M0p * 4;
     L.wp = o;  o += (size_t)2 * nwave * M0p * 4;
-    L.sel = o; o += (size_t)ntile * ((P + 3) & ~3) * 4;
+    // (one selection per wave when every wave of a tile selects for itself,
+    // else one per tile)
+    L.sel = o; o += (size_t)(wave_sel ? nwave : ntile) * ((P + 3) & ~3) * 4;
     L.wp2 = L.wp;
     L.sel2 = o;
     L.wp2_shared = true;
@@ -235,7 +240,7 @@ template <typename T, int D, bool VT_LDS, int NRB, int CC, int NWV, bool L3>
 __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const T *__restrict__ Q, const T *__restrict__ parents, const T *__restrict__ children,
     const unsigned char *__restrict__ pack, int H, int N, int M0, int P, int ltile, float sl2,
-    int neg, int ntiles, int nsteps, int per_bh, int nbh, T *__restrict__ Y,
+    int neg, int wsel, int ntiles, int nsteps, int per_bh, int nbh, T *__restrict__ Y,
     int32_t *__restrict__ sel_out, float *__restrict__ imp_out, const T *__restrict__ leaves,
     int32_t *__restrict__ sel1_out)
 {
@@ -249,7 +254,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     constexpr int LC = CC == 2 ? 1 : CC == 4 ? 2 : CC == 8 ? 3 : 4;
     constexpr int SCH = attn_super_chunks<T, D>();
     const int selStride = (P + 3) & ~3;
-    const AttnLds L = attn_lds<T, D, VT_LDS>(M0, P, NWV, 1 << ltile, CC, L3);
+    // wsel: every wave selects its tile's parents itself (two-level trees,
+    // when the per-wave selections fit in LDS)
+    const bool rsel = !L3 && wsel;
+    const AttnLds L = attn_lds<T, D, VT_LDS>(M0, P, NWV, 1 << ltile, CC, L3, rsel);
     T *Ps = reinterpret_cast<T *>(smem + L.ps);
     T *Vt = reinterpret_cast<T *>(smem + L.vt);
     float *nP = reinterpret_cast<float *>(smem + L.np);
@@ -320,7 +328,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
 
     const int wpt = (1 << ltile) / kQPW;         // waves per tile
     const int tw0 = (w / wpt) * wpt;             // first wave of this wave's tile
-    int *mysel = selS + (w / wpt) * selStride;   // the tile's selection
+    // With rsel every wave sums its tile's importance partials and selects
+    // the tile's parents itself (the same values in the same order give every
+    // wave of the tile the same selection), so no wave waits for another's
+    // selection.  Otherwise the tile's first wave selects for the tile.
+    int *mysel = selS + (rsel ? w : w / wpt) * selStride;   // this wave's copy of the tile's selection
     int *mysel2 = reinterpret_cast<int *>(smem + L.sel2) + (w / wpt) * selStride;   // its children's (L3)
     const int PC = P * CC;
     const int PCr = attn_cands(P, CC);
@@ -350,22 +362,31 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
         // the current block's MFMAs run)
         f32x4 S0[NRB], S1[NRB];
         if constexpr (KS == 2) {
-            Frag<T> pa[2][KS];
+            // fragments two row blocks ahead (ring of three).  The scheduling
+            // barriers pin the LDS reads of block rb+2 before the MFMAs of
+            // block rb: left to itself the compiler reuses one pair of
+            // fragment registers, and every block then waits for its own
+            // LDS reads.
+            Frag<T> pa[3][KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) pa[0][ks] = load_frag(Ps + i16 * LDP + 32 * ks + 8 * g);
+            for (int b = 0; b < 2 && b < NRB; ++b)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) pa[b][ks] = load_frag(Ps + (16 * b + i16) * LDP + 32 * ks + 8 * g);
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
-                if (rb + 1 < NRB) {
+                if (rb + 2 < NRB) {
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
-                        pa[(rb + 1) & 1][ks] = load_frag(Ps + (16 * (rb + 1) + i16) * LDP + 32 * ks + 8 * g);
+                        pa[(rb + 2) % 3][ks] = load_frag(Ps + (16 * (rb + 2) + i16) * LDP + 32 * ks + 8 * g);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    a0 = mma(pa[rb & 1][ks], qa[ks], a0);
-                    a1 = mma(pa[rb & 1][ks], qb[ks], a1);
+                    a0 = mma(pa[rb % 3][ks], qa[ks], a0);
+                    a1 = mma(pa[rb % 3][ks], qb[ks], a1);
                 }
+                __builtin_amdgcn_sched_barrier(0);
                 S0[rb] = a0;
                 S1[rb] = a1;
             }
@@ -431,7 +452,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
             const f32x4 part = row16_reduce_scatter<NRB>(S0, i16);
             *reinterpret_cast<f32x4 *>(Wp + (buf * NWV + w) * M0p + 16 * (i16 >> (4 - LG)) + 4 * g) = part;
         }
-        // X^T = Vbar^T E^T over the parents
+        __syncthreads();       // every wave's importance partials are in Wp[buf]
+        // X^T = Vbar^T E^T over the parents (issued after the barrier, so
+        // that these MFMAs run beside the selection's chain of dependent
+        // compare-and-count rounds below)
         f32x4 X0[DX], X1[DX];
 #pragma unroll
         for (int db = 0; db < DX; ++db) {
@@ -487,12 +511,14 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                 }
             }
         }
-        __syncthreads();       // every wave's importance partials are in Wp[buf]
 
-        // ---- tile importance and top-P, by the first wave of each tile (the
-        // tile's other waves wait at the barrier below)
+        // ---- tile importance and top-P: by every wave (rsel), or by the
+        // first wave of each tile while the tile's other waves wait at the
+        // barrier below
+        // (Wp[buf] is rewritten two steps later, after the next step's
+        // barrier, which every wave reaches only once it has read Wp[buf])
         const int tg = ((st * STEP) >> ltile) + (w / wpt);   // global tile index
-        if ((P > 0 || imp_out) && w == tw0) {
+        if ((P > 0 || imp_out) && (rsel || w == tw0)) {
             // sum of the tile's wave partials (all NWV slots are read, those of
             // other tiles are masked out, so the loop has no branches)
             const float *wb = Wp + buf * NWV * M0p;
@@ -508,7 +534,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
                 }
                 wv[i] = j < M0 ? a * nP[jc] : 0.f;
             }
-            if (imp_out && tg < ntiles) {
+            if (imp_out && tg < ntiles && w == tw0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int j = lane + 64 * i;
@@ -517,9 +543,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
             }
             if (P > 0)
                 select_top_p_regs(wv, M0, P, mysel,
-                                  (sel_out && tg < ntiles) ? sel_out + ((size_t)bh * ntiles + tg) * P : nullptr);
+                                  (sel_out && tg < ntiles && w == tw0) ? sel_out + ((size_t)bh * ntiles + tg) * P
+                                                                       : nullptr);
         }
-        if (P > 0 && wpt > 1) __syncthreads();   // the selection is in LDS
+        if (!rsel && P > 0 && wpt > 1) __syncthreads();   // the tile's selection is in LDS
 
         // ---- child correction, SCH chunks of 32 children at a time.
         // A position ph >= P*C (padding of the last chunks) takes the
@@ -853,7 +880,13 @@ template <typename T, int D, bool VT, int NRB, int CC, int NWV, bool L3>
 static hipError_t launch_attn_k(const AttnArgs &a, hipStream_t stream)
 {
     allow_full_lds<attention_kernel<T, D, VT, NRB, CC, NWV, L3>>();
-    const size_t lds = attn_lds<T, D, VT>(a.M0, a.P, NWV, a.tile, CC, L3).total;
+    // per-wave selections (two-level trees) when they fit in LDS without
+    // costing a CU its second work-group
+    const size_t lds_t = attn_lds<T, D, VT>(a.M0, a.P, NWV, a.tile, CC, L3, false).total;
+    const size_t lds_w = attn_lds<T, D, VT>(a.M0, a.P, NWV, a.tile, CC, L3, true).total;
+    auto cu_share = [](size_t b) { return NWV == 4 && b * 2 <= 160 * 1024 ? 2 : 1; };
+    const bool wsel = !L3 && lds_w <= 160 * 1024 && cu_share(lds_w) == cu_share(lds_t);
+    const size_t lds = wsel ? lds_w : lds_t;
     const int ntiles = (a.N + a.tile - 1) / a.tile;
     const int nsteps = (a.N + NWV * kQPW - 1) / (NWV * kQPW);
     const int BH = a.B * a.H;
@@ -862,12 +895,13 @@ static hipError_t launch_attn_k(const AttnArgs &a, hipStream_t stream)
     // head's steps; rounded down, so that every work-group is resident from
     // the start (one more slice per head would leave work-groups waiting for
     // a second round)
-    const int per_cu = NWV == 4 && lds * 2 <= 160 * 1024 ? 2 : 1;
+    const int per_cu = cu_share(lds);
     const int per_bh = max(1, min(nsteps, per_cu * device_cus() / BH));
     const int grid = (BH * per_bh + 7) & ~7;
     hipLaunchKernelGGL((attention_kernel<T, D, VT, NRB, CC, NWV, L3>), dim3(grid), dim3(64 * NWV), lds, stream,
                        (const T *)a.Q, (const T *)a.parents, (const T *)a.children, (const unsigned char *)a.pack,
-                       a.H, a.N, a.M0, a.P, ilog2(a.tile), fabsf(a.scale) * kLog2e, a.scale < 0.f ? 1 : 0, ntiles,
+                       a.H, a.N, a.M0, a.P, ilog2(a.tile), fabsf(a.scale) * kLog2e, a.scale < 0.f ? 1 : 0,
+                       wsel ? 1 : 0, ntiles,
                        nsteps, per_bh, BH, (T *)a.Y, a.sel, a.imp, (const T *)a.leaves, a.sel1);
     return hipGetLastError();
 }
