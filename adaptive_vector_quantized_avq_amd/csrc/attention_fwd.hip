@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const unsigned char *__restrict__ pack, int H, int N, int M0, int P, int ltile, float sl2,
     int neg, int wsel, int ntiles, int nsteps, int per_bh, int nbh, T *__restrict__ Y,
     int32_t *__restrict__ sel_out, float *__restrict__ imp_out, const T *__restrict__ leaves,
-    int32_t *__restrict__ sel1_out)
+    int32_t *__restrict__ sel1_out, int wsplit)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int KS = D / 32;
@@ -337,8 +337,23 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const int PC = P * CC;
     const int PCr = attn_cands(P, CC);
 
+    // Rounds of per_bh steps: every slice takes one step per round.  With
+    // two work-groups on every CU (wsplit), the last round goes to the
+    // head's slices whose work-group was dispatched first to its CU (the
+    // first half of the grid): the SIMDs favour the older waves, and the
+    // first work-group runs ~1.2x faster than the second, which otherwise
+    // ends ~15 us later, alone on its CU at a fraction of the CU's rate.
+    const int G2 = G8 >> 1;
+    auto early_before = [&](int p) { return (p / G8) * G2 + min(p % G8, G2); };
+    const int p0 = bh * per_bh;
+    const int nF = early_before(p0 + per_bh) - early_before(p0);   // early slices of the head
+    const bool early = (pair % G8) < G2;
+    const int eRank = early_before(pair) - early_before(p0);
+    const int R = (nsteps + per_bh - 1) / per_bh;
+    const bool split = wsplit && R >= 2 && nF > 0;
+    const int lastR = (R - 1) * per_bh;   // first step of the last round
     int buf = 0;
-    for (int st = slice; st < nsteps; st += per_bh, buf ^= 1) {
+    for (int st = slice; st < nsteps; buf ^= 1) {
         const int q0 = st * STEP + kQPW * w + i16, q1 = q0 + 16;
         const bool v0 = q0 < N, v1 = q1 < N;
         // query fragments (queries past N read the last query; never stored)
@@ -823,6 +838,15 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
         const float Z1 = ZB ? xgroup_sum((X1[DX - 1][0] + X1[DX - 1][1]) + X1[DX - 1][2]) : Zf1 + xgroup_sum(dz1);
         if (v0) store_row4<T, DB>(Yh + (size_t)q0 * D + 4 * g, X0, __builtin_amdgcn_rcpf(Z0));
         if (v1) store_row4<T, DB>(Yh + (size_t)q1 * D + 4 * g, X1, __builtin_amdgcn_rcpf(Z1));
+        // the next step
+        if (!split) {
+            st += per_bh;
+        } else if (st < lastR) {
+            st += per_bh;
+            if (st >= lastR) st = early ? lastR + eRank : nsteps;   // entering the last round
+        } else {
+            st += nF;
+        }
     }
 }
 
@@ -902,7 +926,8 @@ static hipError_t launch_attn_k(const AttnArgs &a, hipStream_t stream)
                        (const T *)a.Q, (const T *)a.parents, (const T *)a.children, (const unsigned char *)a.pack,
                        a.H, a.N, a.M0, a.P, ilog2(a.tile), fabsf(a.scale) * kLog2e, a.scale < 0.f ? 1 : 0,
                        wsel ? 1 : 0, ntiles,
-                       nsteps, per_bh, BH, (T *)a.Y, a.sel, a.imp, (const T *)a.leaves, a.sel1);
+                       nsteps, per_bh, BH, (T *)a.Y, a.sel, a.imp, (const T *)a.leaves, a.sel1,
+                       per_cu == 2 && grid == 2 * device_cus() ? 1 : 0);   // wsplit
     return hipGetLastError();
 }
 
