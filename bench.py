@@ -417,7 +417,7 @@ def main():
         "data": "synthetic (seeded PCG64; shapes of the pages' long-sequence timing sweep)",
         "config": {"workload": inp.name, "B": B, "H": H, "N": N, "d": d, "M0": inp.M0,
                    "C": inp.C, "P": P, "tile": inp.T, "input_sets": args.sets, "levels": inp.levels,
-                   "stage1": "unfused" if args.unfused else "fused"},
+                   "stage1": "unfused" if args.unfused else "fused", "seed": inp.seed},
         "roofline": roof,
         "stages": {
             "assign_aggregate": {"ms": round(s1_ms, 5), "alg_bytes": alg["s1_bytes"],
