@@ -170,8 +170,9 @@ void refine_aggregate_kernel(
     // slices per group scanned, and the item's group and slice looked up.
     // (The plan arrays live in the union region, before its use.)
     int *gsz = reinterpret_cast<int *>(un);      // [ngroups]
-    int *ist = gsz + ngroups;                    // [ngroups + 1] first item of each group
+    int *ist = gsz + ngroups;                    // [ngroups + 1] first item of each group (in `ord` order)
     int *pst = ist + ngroups + 1;                // [ngroups + 1] first partial slot of each group
+    int *ord = pst + ngroups + 1;                // [ngroups] groups by decreasing length
     int bound = 0;
     for (int c = lane; c < nchunks; c += 64) {
         const int2 m = *reinterpret_cast<const int2 *>(cmax + ((int64_t)bh * nchunks + c) * 2);
@@ -192,11 +193,24 @@ void refine_aggregate_kernel(
         for (int e = tid; e < ngroups * nchunks; e += NT)
             atomicAdd(gsz + e / nchunks, seg[(int64_t)bh * ngroups * nchunks + e].y);
         __syncthreads();
-        if (wave == 0) {   // exclusive scans of the slice and partial-slot counts
+        // Items go to the groups longest first (ties to the lower index): the
+        // grid dispatches item-major over the heads, so every head's longest
+        // work is dispatched first and the short items fill in at the end.
+        for (int gi = tid; gi < ngroups; gi += NT) {
+            const int sz = gsz[gi];
+            int rank = 0;
+            for (int o = 0; o < ngroups; ++o) {
+                const int so = gsz[o];
+                rank += (so > sz) | ((so == sz) & (o < gi));
+            }
+            ord[rank] = gi;
+        }
+        __syncthreads();
+        if (wave == 0) {   // exclusive scans of the slice and partial-slot counts, in `ord` order
             int c1 = 0, c2 = 0;
             for (int base = 0; base < ngroups; base += 64) {
-                const int gi = base + lane;
-                const int ns = gi < ngroups ? max(1, (gsz[gi] + target - 1) / target) : 0;
+                const int gi = base + lane < ngroups ? ord[base + lane] : 0;
+                const int ns = base + lane < ngroups ? max(1, (gsz[gi] + target - 1) / target) : 0;
                 const int np = ns > 1 ? ns - 1 : 0;
                 int i1 = ns, i2 = np;
 #pragma unroll
@@ -207,9 +221,9 @@ void refine_aggregate_kernel(
                         i2 += t2;
                     }
                 }
-                if (gi < ngroups) {
-                    ist[gi] = c1 + i1 - ns;
-                    pst[gi] = c2 + i2 - np;
+                if (base + lane < ngroups) {
+                    ist[base + lane] = c1 + i1 - ns;
+                    pst[base + lane] = c2 + i2 - np;
                 }
                 c1 += __shfl(i1, 63);
                 c2 += __shfl(i2, 63);
@@ -221,18 +235,18 @@ void refine_aggregate_kernel(
         }
         __syncthreads();
         if (item >= ist[ngroups]) return;    // past this (b, h)'s items (the same for the whole group)
-        int lo = 0, hi = ngroups;            // the group: last one whose first item is <= item
+        int lo = 0, hi = ngroups;            // the group's place: last one whose first item is <= item
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             const bool right = ist[mid] <= item;
             lo = right ? mid : lo;
             hi = right ? hi : mid;
         }
-        gq = lo;
-        slice = item - ist[gq];
-        nslices = ist[gq + 1] - ist[gq];
+        gq = ord[lo];
+        slice = item - ist[lo];
+        nslices = ist[lo + 1] - ist[lo];
         gsize = gsz[gq];
-        pslot = pst[gq];
+        pslot = pst[lo];
         __syncthreads();                     // the plan arrays are dead from here
     }
 
@@ -597,7 +611,7 @@ static hipError_t launch_refine(const void *K, const void *V, const void *parent
     const int ngroups = (M0 + Cfg::G - 1) / Cfg::G;
     const RefinePlan pl = refine_plan(N, M0, CC, D);
     // the plan arrays share the union region when they fit in it
-    const size_t plan_bytes = (size_t)(3 * ngroups + 2) * 4;
+    const size_t plan_bytes = (size_t)(4 * ngroups + 2) * 4;
     const size_t lds = Cfg::lds(nchunks) + (plan_bytes > Cfg::union_bytes ? plan_bytes - Cfg::union_bytes + 16 : 0);
     allow_full_lds<refine_aggregate_kernel<T, D, CC>>();
     // grid (b*h, items): consecutive work-groups take the same item of
