@@ -145,6 +145,15 @@ def test_maximum_sequence_length(avq):
     check_all(avq, synth.generate("long-64k", H=1, N=1 << 20))
 
 
+def test_ragged_last_round_of_steps(avq):
+    """long-64k's launch shape (two work-groups per CU, 64 slices per head)
+    with 1000 more queries per head: 520 steps of 128 queries, so the last
+    round of each head's steps -- the one the first-dispatched half of the
+    grid takes -- holds 8 steps, and the last tile is partial.  Every key
+    and every query tile."""
+    check_all(avq, synth.generate("long-64k", N=65536 + 1000))
+
+
 def test_stage2_on_summed_partial_aggregates(avq):
     """Stage 2 on aggregates the caller formed: stage 1 runs on two disjoint
     halves of every head's keys, the test adds the two value sums and the

@@ -63,6 +63,13 @@ def test_noalloc_matches_workspace_entry_point_twice(avq):
     _compare(avq, synth.generate("wide-d128", B=1, H=3, N=5000, M0=100), True)
 
 
+def test_noalloc_skewed_keys_split_groups(avq):
+    """Zipf-skewed keys (seg-zipf's generator, 8192 keys per head): a group
+    holds more keys than the refinement's split target, so its slices store
+    partial sums in the scratch and the last one adds them."""
+    _compare(avq, synth.generate("seg-zipf", B=1, H=4, N=8192), False)
+
+
 def test_noalloc_refuses_shapes_past_the_scratch(avq):
     _say("noalloc scratch limit")
     B, H, N, d, M0, C = 1, 64, 65536, 64, 16, 4   # 16 MiB of keys + segments > 16 MiB
