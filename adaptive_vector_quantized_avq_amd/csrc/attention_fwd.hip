@@ -68,7 +68,8 @@ struct AttnLds {
 __host__ __device__ inline int attn_cands(int P, int C) { return (P * C + 31) & ~31; }
 
 // (nwave waves of kQPW queries per work-group step cover nwave * kQPW / tile
-// tiles; each tile keeps one selection)
+// tiles; each tile keeps one selection, or each wave its own copy of its
+// tile's with wave_sel)
 template <typename T, int D, bool VT_LDS>
 __host__ __device__ inline AttnLds attn_lds(int M0, int P, int nwave, int tile, int C = 0, bool three_level = false,
                                             bool wave_sel = false)
