@@ -237,7 +237,7 @@ template <typename T, int D> constexpr int attn_super_chunks()
 // L3: three-level tree -- `children` is the middle level and `leaves` the
 // C leaves of every child; after the children's correction the tile's
 // level-1 importance picks P children, whose leaves correct them in turn.
-template <typename T, int D, bool VT_LDS, int NRB, int CC, int NWV, bool L3>
+template <typename T, int D, bool VT_LDS, int NRB, int CC, int NWV, bool L3, bool RANGES>
 __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const T *__restrict__ Q, const T *__restrict__ parents, const T *__restrict__ children,
     const unsigned char *__restrict__ pack, int H, int N, int M0, int P, int ltile, float sl2,
@@ -265,27 +265,27 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     float *Wp = reinterpret_cast<float *>(smem + L.wp);
     int *selS = reinterpret_cast<int *>(smem + L.sel);
 
-    // (head, slice) of this work-group: XCD x = blockIdx.x % 8 gets pairs
-    // [x * G/8, (x+1) * G/8) of the G = gridDim.x pairs
+    // The work-group's share of the (head, step) list, in one of two ways:
+    //  - (head, slice) pairs (!RANGES): slice s of a head takes its steps
+    //    s, s + per_bh, ... (see the step schedule below);
+    //  - contiguous ranges of the list (RANGES), one per work-group,
+    //    when the heads do not divide the CU slots evenly (e.g. 20 heads on
+    //    256 one-work-group CUs): a range that crosses into the next head
+    //    stages that head's codebook in LDS and goes on.
+    // XCD x = blockIdx.x % 8 gets pairs (ranges) [x * G/8, (x+1) * G/8) of
+    // the G = gridDim.x, so that every XCD holds a contiguous run of heads.
     const int G8 = gridDim.x >> 3;
     const int pair = (blockIdx.x & 7) * G8 + (blockIdx.x >> 3);
-    const int bh = pair / per_bh, slice = pair - bh * per_bh;
-    if (bh >= nbh) return;
-    const int h = bh % H;
+    const int TS = nbh * nsteps;
+    const int gs0 = RANGES ? (int)((long long)pair * TS / gridDim.x) : 0;
+    const int gs1 = RANGES ? (int)((long long)(pair + 1) * TS / gridDim.x) : 0;
+    int bh = RANGES ? gs0 / nsteps : pair / per_bh;
+    const int slice = RANGES ? 0 : pair - bh * per_bh;
+    if (RANGES ? gs0 >= gs1 : bh >= nbh) return;
+    int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, i16 = lane & 15;
     const PackLayout PL = pack_layout(M0, CC, D, (int)sizeof(T), L3);
-    const unsigned char *pk = pack + (size_t)bh * PL.bytes;
-    const T *pvt = reinterpret_cast<const T *>(pk + PL.pvt);
-    const float *pnp = reinterpret_cast<const float *>(pk + PL.pn);
-    const T *cvt = reinterpret_cast<const T *>(pk + PL.cvt);
-    const float *cnp = reinterpret_cast<const float *>(pk + PL.cn);
-    const T *Qh = Q + (size_t)bh * N * D;
-    T *Yh = Y + (size_t)bh * N * D;
-    const T *Ch = children + (size_t)h * M0 * CC * D;
-    const T *Lh = L3 ? leaves + (size_t)h * M0 * CC * CC * D : nullptr;
-    const T *gvt = reinterpret_cast<const T *>(pk + PL.gvt);
-    const float *gnp = reinterpret_cast<const float *>(pk + PL.gn);
     // Two-level trees with 16-bit operands form the output's denominators on
     // the matrix cores, from the counts split into three exact bf16 parts
     // (pack rows hi, mid, lo) and the same bf16 weights as the value sums, so
@@ -294,38 +294,63 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     // fp32 sum.)
     constexpr bool ZB = sizeof(T) == 2 && !L3;
     constexpr int DX = DB + (ZB ? 1 : 0);
-    const T *pzp = reinterpret_cast<const T *>(pk + PL.pz);
-    const T *czp = reinterpret_cast<const T *>(pk + PL.cz);
+    // the head's operands
+    const unsigned char *pk;
+    const T *pvt, *cvt, *Qh, *Ch, *Lh, *gvt, *pzp, *czp;
+    const float *pnp, *cnp, *gnp;
+    T *Yh;
+    auto set_head = [&](int nb) {
+        bh = nb;
+        h = bh % H;
+        pk = pack + (size_t)bh * PL.bytes;
+        pvt = reinterpret_cast<const T *>(pk + PL.pvt);
+        pnp = reinterpret_cast<const float *>(pk + PL.pn);
+        cvt = reinterpret_cast<const T *>(pk + PL.cvt);
+        cnp = reinterpret_cast<const float *>(pk + PL.cn);
+        Qh = Q + (size_t)bh * N * D;
+        Yh = Y + (size_t)bh * N * D;
+        Ch = children + (size_t)h * M0 * CC * D;
+        Lh = L3 ? leaves + (size_t)h * M0 * CC * CC * D : nullptr;
+        gvt = reinterpret_cast<const T *>(pk + PL.gvt);
+        gnp = reinterpret_cast<const float *>(pk + PL.gn);
+        pzp = reinterpret_cast<const T *>(pk + PL.pz);
+        czp = reinterpret_cast<const T *>(pk + PL.cz);
+    };
+    set_head(bh);
     const int zrow = i16 < 3 ? i16 : 3;   // count operand row of this lane (row 3: zero)
 
-    // ---- stage the head's parents, parent value sums and counts once.
+    // ---- stage the head's parents, parent value sums and counts (once per
+    // head the work-group visits).
     // A row whose parent holds no key -- an empty parent, or a padding row
     // (M0 <= j < M0p) -- is staged as a copy of the first parent that does,
     // with its own count and value sum, which are zero: its logit is one of
     // the real ones, so the shift is the largest logit over the parents that
     // hold keys (an empty codeword far above them cannot push every weight
     // to zero), and it adds nothing to Z, X or the importance.
-    int j0 = 0;   // first parent with keys (N >= 1: there is one)
+    auto stage_head = [&]() {
+        int j0 = 0;   // first parent with keys (N >= 1: there is one)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = lane + 64 * i;
-        const unsigned long long m = __ballot(j < M0 && pnp[j < M0 ? j : 0] > 0.f);
-        if (m) {
-            j0 = 64 * i + __ffsll((long long)m) - 1;
-            break;
+        for (int i = 0; i < 4; ++i) {
+            const int j = lane + 64 * i;
+            const unsigned long long m = __ballot(j < M0 && pnp[j < M0 ? j : 0] > 0.f);
+            if (m) {
+                j0 = 64 * i + __ffsll((long long)m) - 1;
+                break;
+            }
         }
-    }
-    for (int e = tid * 8; e < M0p * D; e += 64 * NWV * 8) {
-        const int r = e / D, c = e % D;
-        const int src = r < M0 && pnp[r] > 0.f ? r : j0;
-        store_frag(Ps + r * LDP + c, load_frag(parents + ((size_t)h * M0 + src) * D + c));
-    }
-    if (VT_LDS) {
-        for (int e = tid * 8; e < D * M0p; e += 64 * NWV * 8)
-            store_frag(Vt + (e / M0p) * LDV + (e % M0p), load_frag(pvt + e));
-    }
-    for (int j = tid; j < M0p; j += 64 * NWV) nP[j] = pnp[j];
-    __syncthreads();
+        for (int e = tid * 8; e < M0p * D; e += 64 * NWV * 8) {
+            const int r = e / D, c = e % D;
+            const int src = r < M0 && pnp[r] > 0.f ? r : j0;
+            store_frag(Ps + r * LDP + c, load_frag(parents + ((size_t)h * M0 + src) * D + c));
+        }
+        if (VT_LDS) {
+            for (int e = tid * 8; e < D * M0p; e += 64 * NWV * 8)
+                store_frag(Vt + (e / M0p) * LDV + (e % M0p), load_frag(pvt + e));
+        }
+        for (int j = tid; j < M0p; j += 64 * NWV) nP[j] = pnp[j];
+        __syncthreads();
+    };
+    stage_head();
 
     const int wpt = (1 << ltile) / kQPW;         // waves per tile
     const int tw0 = (w / wpt) * wpt;             // first wave of this wave's tile
@@ -354,7 +379,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
     const bool split = wsplit && R >= 2 && nF > 0;
     const int lastR = (R - 1) * per_bh;   // first step of the last round
     int buf = 0;
-    for (int st = slice; st < nsteps; buf ^= 1) {
+    int st = RANGES ? gs0 - bh * nsteps : slice;
+    for (int gs = gs0; RANGES ? gs < gs1 : st < nsteps; buf ^= 1) {
         const int q0 = st * STEP + kQPW * w + i16, q1 = q0 + 16;
         const bool v0 = q0 < N, v1 = q1 < N;
         // query fragments (queries past N read the last query; never stored)
@@ -840,7 +866,16 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_kernel(
         if (v0) store_row4<T, DB>(Yh + (size_t)q0 * D + 4 * g, X0, __builtin_amdgcn_rcpf(Z0));
         if (v1) store_row4<T, DB>(Yh + (size_t)q1 * D + 4 * g, X1, __builtin_amdgcn_rcpf(Z1));
         // the next step
-        if (!split) {
+        if constexpr (RANGES) {
+            ++gs;
+            ++st;
+            if (gs < gs1 && st == nsteps) {   // the range goes on in the next head
+                __syncthreads();              // every wave is done with this head's LDS
+                set_head(bh + 1);
+                stage_head();
+                st = 0;
+            }
+        } else if (!split) {
             st += per_bh;
         } else if (st < lastR) {
             st += per_bh;
@@ -904,7 +939,7 @@ struct AttnArgs {
 template <typename T, int D, bool VT, int NRB, int CC, int NWV, bool L3>
 static hipError_t launch_attn_k(const AttnArgs &a, hipStream_t stream)
 {
-    allow_full_lds<attention_kernel<T, D, VT, NRB, CC, NWV, L3>>();
+    allow_full_lds<attention_kernel<T, D, VT, NRB, CC, NWV, L3, false>>();
     // per-wave selections (two-level trees) when they fit in LDS without
     // costing a CU its second work-group
     const size_t lds_t = attn_lds<T, D, VT>(a.M0, a.P, NWV, a.tile, CC, L3, false).total;
@@ -921,9 +956,28 @@ static hipError_t launch_attn_k(const AttnArgs &a, hipStream_t stream)
     // the start (one more slice per head would leave work-groups waiting for
     // a second round)
     const int per_cu = cu_share(lds);
-    const int per_bh = max(1, min(nsteps, per_cu * device_cus() / BH));
-    const int grid = (BH * per_bh + 7) & ~7;
-    hipLaunchKernelGGL((attention_kernel<T, D, VT, NRB, CC, NWV, L3>), dim3(grid), dim3(64 * NWV), lds, stream,
+    const int slots = per_cu * device_cus();
+    const int per_bh = max(1, min(nsteps, slots / BH));
+    // contiguous ranges of the (head, step) list when they take fewer steps
+    // per work-group than whole slices of a head (heads that do not divide
+    // the slots), one work-group per slot
+    const long long TS = (long long)BH * nsteps;
+    const bool ranges = NWV == 8 && slots % 8 == 0 && TS < (1ll << 31) &&
+                        (TS + slots - 1) / slots < (nsteps + per_bh - 1) / per_bh;
+    const int grid = ranges ? slots : (BH * per_bh + 7) & ~7;
+    // (the range form is built for the one-work-group-per-CU shapes only)
+    if constexpr (NWV == 8) {
+        if (ranges) {
+            allow_full_lds<attention_kernel<T, D, VT, NRB, CC, NWV, L3, true>>();
+            hipLaunchKernelGGL((attention_kernel<T, D, VT, NRB, CC, NWV, L3, true>), dim3(grid), dim3(64 * NWV), lds,
+                               stream, (const T *)a.Q, (const T *)a.parents, (const T *)a.children,
+                               (const unsigned char *)a.pack, a.H, a.N, a.M0, a.P, ilog2(a.tile),
+                               fabsf(a.scale) * kLog2e, a.scale < 0.f ? 1 : 0, wsel ? 1 : 0, ntiles, nsteps, per_bh,
+                               BH, (T *)a.Y, a.sel, a.imp, (const T *)a.leaves, a.sel1, 0);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((attention_kernel<T, D, VT, NRB, CC, NWV, L3, false>), dim3(grid), dim3(64 * NWV), lds, stream,
                        (const T *)a.Q, (const T *)a.parents, (const T *)a.children, (const unsigned char *)a.pack,
                        a.H, a.N, a.M0, a.P, ilog2(a.tile), fabsf(a.scale) * kLog2e, a.scale < 0.f ? 1 : 0,
                        wsel ? 1 : 0, ntiles,

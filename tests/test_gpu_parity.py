@@ -154,6 +154,14 @@ def test_ragged_last_round_of_steps(avq):
     check_all(avq, synth.generate("long-64k", N=65536 + 1000))
 
 
+def test_step_ranges_across_heads(avq):
+    """wide-d128's kind of launch (bf16, d = 128: one 8-wave work-group per
+    CU) with 20 heads of 25 256-query steps: contiguous ranges of the
+    (head, step) list, most crossing from one head into the next, and 64-query
+    tiles.  Every key and every tile."""
+    check_all(avq, synth.generate("wide-d128", B=2, H=10, N=6400))
+
+
 def test_stage2_on_summed_partial_aggregates(avq):
     """Stage 2 on aggregates the caller formed: stage 1 runs on two disjoint
     halves of every head's keys, the test adds the two value sums and the

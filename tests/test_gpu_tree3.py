@@ -154,6 +154,14 @@ def test_deep_workload_full_size(avq):
     check_all3(avq, synth.generate("deep-64k"))
 
 
+def test_step_ranges_across_heads(avq):
+    """bf16 at d = 128 runs one 8-wave work-group per CU; 20 heads of 25
+    256-query steps do not divide the CUs, so each work-group takes a
+    contiguous range of the (head, step) list and stages the next head's
+    codebook where its range crosses into it.  Every key and every tile."""
+    check_all3(avq, synth.generate("deep-64k", B=2, H=10, N=6400, d=128))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M0,C,P,T,d", [(6, 4, 2, 64, 64), (32, 8, 8, 128, 64), (100, 2, 40, 32, 64),
                                         (16, 16, 16, 256, 64), (24, 8, 5, 128, 128), (64, 4, 64, 64, 128)])
