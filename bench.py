@@ -42,9 +42,12 @@ def log(*a):
 
 
 def algorithmic(inp, P):
-    """Algorithmic bytes and flops per launch ('Roofline').
-    A three-level tree refines once more: C more distances per key in stage
-    1, P*C more codes per query in stage 2."""
+    """Algorithmic bytes and flops per launch.  Bytes: each stage's inputs
+    read once and outputs written once (stage 1: K and V in, the sums and
+    counts out; stage 2: Q, every codeword, sum and count in, Y out).  Flops: two per multiply-add of the per-query and
+    per-key interaction counts in the complexity table of "AVQ-Attention"
+    (Sec. 4.3, Table 1).  A three-level tree refines once more: C more
+    distances per key in stage 1, P*C more codes per query in stage 2."""
     e = 2 if inp.dtype == "bf16" else 4
     BH, N, d, M0, C = inp.B * inp.H, inp.N, inp.d, inp.M0, inp.C
     deep = inp.levels == 3
@@ -259,7 +262,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the method's "
-              "multi-GPU split is described in DESIGN.md but not built", file=sys.stderr)
+              "split over several GPUs is not built", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -11,7 +11,7 @@
  * head) unit at a time, single-threaded.  Inputs are float64 arrays holding
  * the exact values of the stored bf16/fp32 tensors.
  *
- * Readings taken where the pages are silent (each also listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - argmin ties go to the lowest index; a child replaces the parent only if
  *    it is strictly closer;
  *  - top-P orders parents by importance descending, then index ascending;
@@ -425,7 +425,7 @@ void avqo_gilbert_order(int W, int H, int32_t *order /*[W*H]*/)
 /* ------------------------------------------------------------------ */
 /* Three-level tree (Sec. 6 "Discussion and Conclusion": a deeper       */
 /* hierarchy adds P*C codes per extra level).  The pages propose it and */
-/* give no algorithm; the readings taken here (each in the design doc):      */
+/* give no algorithm; the readings taken here:                       */
 /*  - leaves L[p][a][b] are given; level 1 c[p][a] is the mean of its C  */
 /*    leaves and the root r[p] the mean of its C*C leaves (the mean      */
 /*    constraint at every level), each rounded once to the storage type; */
